@@ -1,0 +1,173 @@
+/* w4.h - C ABI of the MI355X (gfx950) ConvRot INT4 weight-quantized linear layer.
+ *
+ * The layer (ComfyUI-INT-Crush README, "Inference / INT4" and "Forward Pass";
+ * stable-diffusion.cpp PR #2010 "feat: packed int4 convrot model loading and
+ * dispatch", "Summary"):
+ *
+ *   X' = X . blockdiag(H_g / sqrt(g))            block Hadamard rotation along K
+ *   q  = rint(X' / s_x),  s_x = fp32(max|X'| / qmax) per token      (qmax 127 or 7)
+ *   W' = W . blockdiag(H_g / sqrt(g)),  c = packed int4 codes per output row
+ *   acc[m, n] = sum_k q[m, k] * (c[n, k] - z[n])                     int32, exact
+ *   Y  = bf16( acc * s_x[m] * s_w[n] + (X . L1) . L2 + bias[n] )
+ *
+ * H_g is the Sylvester-ordered Hadamard matrix, g in {64, 256}, groups are
+ * contiguous blocks of g along K.  rint is round-half-to-even.  Two 4-bit codes
+ * per byte along K, low nibble = even k.  Symmetric weights: signed codes in
+ * [-8, 7] (two's complement nibbles), z = 0, s_w = fp32(max|W'| / 7).
+ * Asymmetric weights: unsigned codes in [0, 15] with a zero point z[n] in [0, 15],
+ * s_w = fp32((max(W', 0) - min(W', 0)) / 15), z = clamp(-rint(min(W', 0) / s_w)).
+ * Codes are rounded first and the zero point added after.
+ *
+ * Conventions for every call:
+ *  - Every pointer is a DEVICE pointer unless stated otherwise; the caller owns
+ *    and allocates every buffer.  The library never allocates, never frees and
+ *    never synchronizes; work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and is complete when that stream is.
+ *  - Matrices are row-major and dense (row stride = number of columns).
+ *  - Device pointers must be 16-byte aligned.
+ *  - Return value: W4_OK (0) or a positive W4_ERR_* code.  Arguments are checked
+ *    before anything is launched, so an error leaves every output untouched
+ *    (except W4_ERR_HIP, a launch failure).  w4_last_error() gives a message
+ *    for the calling thread's last error.  Faults during execution surface at
+ *    the caller's next synchronization, as for any HIP work.
+ *  - M == 0 is a valid no-op.  N >= 1 and K >= g are required.
+ *  - Thread-safe: no global state besides the per-thread error message.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define W4_OK 0
+#define W4_ERR_INVALID_ARG 1 /* null pointer, unknown enum value */
+#define W4_ERR_SHAPE 2       /* negative or zero size, K % g != 0, K out of range */
+#define W4_ERR_UNSUPPORTED 3 /* g not in {64, 256}, act_bits not in {4, 8}, K not tileable */
+#define W4_ERR_ALIGN 4       /* a device pointer is not 16-byte aligned */
+#define W4_ERR_HIP 5         /* a HIP launch failed (message from hipGetErrorString) */
+#define W4_ERR_WORKSPACE 6   /* workspace missing or smaller than w4_workspace_bytes() */
+
+/* element types of floating-point inputs */
+#define W4_F32 0
+#define W4_BF16 1
+
+/* weight quantization modes */
+#define W4_SYM 0  /* signed codes, no zero point */
+#define W4_ASYM 1 /* unsigned codes with a per-row zero point */
+
+/* output kinds of the linear calls */
+#define W4_OUT_BF16 0 /* Y bf16 [M, N]: the dequantized layer output */
+#define W4_OUT_I32 1  /* Y int32 [M, N]: the raw exact accumulator acc[m, n] (no epilogue) */
+
+/* Largest K the library accepts.  The int32 accumulation of 16 * q * c would stay exact up to
+ * K = 65536; the activation kernel keeps a whole token row in registers and stops at 32768. */
+#define W4_MAX_K 32768
+
+/* Low-rank side branch added before the bias: lr = (X . L1) . L2 with the UNROTATED
+ * activations (ComfyUI-INT-Crush README, "Forward Pass" step 6 and "LoRA").
+ *  x  : bf16 [M, K] unrotated layer input; read only when t == NULL
+ *  l1 : bf16 [K, r]; read only when t == NULL
+ *  t  : optional f32 [M, r] = x . l1 computed earlier (e.g. by w4_lowrank_down, and
+ *       shared by linears that read the same input); NULL -> computed into the workspace
+ *  l2 : bf16 [r, N]
+ *  r  : rank, 1 <= r <= 64 */
+typedef struct w4_lowrank {
+    const void *x;
+    const void *l1;
+    const float *t;
+    const void *l2;
+    int r;
+} w4_lowrank;
+
+/* w4_pack_weights - offline weight step: rotate every row of W along K in groups of g,
+ * quantize it per row to int4 and pack two codes per byte.
+ * (ComfyUI-INT-Crush README, "Weight Format" and "Workflow" step 1 (converter);
+ *  stable-diffusion.cpp PR #2010, "Summary": packed nibbles + row scales, and the
+ *  discussion's shape report: the packed input dimension is K / 2.)
+ *  W        : [N, K] of w_dtype (W4_F32 or W4_BF16)
+ *  wmode    : W4_SYM or W4_ASYM
+ *  packed   : out uint8 [N, K/2]
+ *  row_scale: out f32 [N]
+ *  zp       : out uint8 [N] zero points; required for W4_ASYM, must be NULL for W4_SYM
+ * Requires K % g == 0, g in {64, 256}, K <= W4_MAX_K.  Rotation, scales and quotients are
+ * computed in fp64 with IEEE division, exactly as in the definition above. */
+int w4_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int g, int wmode,
+                    uint8_t *packed, float *row_scale, uint8_t *zp, void *stream);
+
+/* w4_rotate_quant_act - activation step: rotate each token (row of X) along K in groups
+ * of g and quantize it per token to act_bits.
+ * (ComfyUI-INT-Crush README, "Inference / INT4": Hadamard rotation + dynamic activation
+ *  quantization; "Inference / INT8": dynamic per-token quantization;
+ *  stable-diffusion.cpp PR #2010, "Summary": this result is what gets shared and cached
+ *  per (input, group size).)
+ *  X         : [M, K] of x_dtype
+ *  q         : out, act_bits == 8: int8 [M, K]; act_bits == 4: uint8 [M, K/2] packed like
+ *              the weights (low nibble = even k, two's complement)
+ *  tok_scale : out f32 [M]
+ *  tok_rowsum: out int32 [M] = sum_k q[m, k] (used by the asymmetric-weight correction)
+ * The rotation runs in fp64 (exact for bf16 inputs); codes equal rint(X'/s_x) up to the
+ * last fp64 bit of the quotient.  Requires K % g == 0 and K/16 = C * T for some
+ * C in 1..4 and T a multiple of g/16 with T <= 512 (every K used by DiT / text-encoder
+ * linears qualifies); else W4_ERR_UNSUPPORTED. */
+int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
+                        void *q, float *tok_scale, int32_t *tok_rowsum, void *stream);
+
+/* w4_linear_cached_rot - integer GEMM + fused dequant epilogue on already rotated and
+ * quantized activations (the cached half of the layer).
+ * (ComfyUI-INT-Crush README, "Inference / INT4" (INT8 GEMM with fused dequant; W4A8 and
+ *  fused ConvRot paths) and "Forward Pass" steps 5-6; stable-diffusion.cpp PR #2010,
+ *  "Summary": packed weights stream to the kernel unconverted.)
+ *  q, tok_scale, tok_rowsum, act_bits : as produced by w4_rotate_quant_act
+ *  packed, row_scale, zp              : as produced by w4_pack_weights (zp NULL = symmetric)
+ *  bias      : NULL or [N] of bias_dtype (W4_F32 or W4_BF16)
+ *  lr        : NULL or the low-rank branch (host pointer to the struct; its fields are
+ *              device pointers)
+ *  Y         : out [M, N], bf16 for W4_OUT_BF16, int32 for W4_OUT_I32 (bias and lr unused)
+ *  ws        : workspace of at least w4_workspace_bytes(M, N, K, act_bits, r_needed)
+ *              where r_needed = lr->r when lr && !lr->t, else 0; may be NULL if that is 0
+ * M <= 64 runs a split-K streaming kernel, larger M the MFMA GEMM. */
+int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *tok_rowsum,
+                         int act_bits, const uint8_t *packed, const float *row_scale,
+                         const uint8_t *zp, const void *bias, int bias_dtype,
+                         const w4_lowrank *lr, int64_t M, int64_t N, int64_t K, void *Y,
+                         int y_kind, void *ws, size_t ws_bytes, void *stream);
+
+/* w4_linear - the whole layer: w4_rotate_quant_act into the workspace, then
+ * w4_linear_cached_rot.  Arguments as above; ws must hold at least
+ * w4_workspace_bytes(M, N, K, act_bits, r) + room for the activation codes, i.e.
+ * w4_linear_workspace_bytes(M, N, K, act_bits, r_needed). */
+int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
+              const uint8_t *packed, const float *row_scale, const uint8_t *zp, const void *bias,
+              int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *ws,
+              size_t ws_bytes, void *stream);
+
+/* w4_lowrank_down - t = x . l1, f32 [M, r], from bf16 x [M, K] and bf16 l1 [K, r]
+ * (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of the low-rank
+ *  residual).  Lets linears that read the same input share t.  1 <= r <= 64. */
+int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t,
+                    void *stream);
+
+/* Workspace sizes in bytes (0 when nothing is needed).
+ * w4_workspace_bytes: for w4_linear_cached_rot (the low-rank t when not supplied).
+ * w4_linear_workspace_bytes: for w4_linear (activation codes, token scales and row sums,
+ * plus the above).  Each piece is 256-byte aligned inside the workspace. */
+size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);
+size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);
+
+/* Human-readable name of a status code (static string). */
+const char *w4_status_string(int status);
+/* Message describing the calling thread's last error ("" if none). */
+const char *w4_last_error(void);
+/* Library version string (static). */
+const char *w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,42 @@
+// Internal launchers of the gfx950 kernels (C++ linkage, not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Activation rotate + per-token quantize.  Returns hipSuccess or the launch error;
+// returns hipErrorInvalidValue when K has no supported (C, T) split.
+bool rotquant_supported(int64_t K, int g);
+hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
+                           void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st);
+
+// Offline weight rotate + per-row quantize + nibble pack.
+hipError_t launch_pack(const void *W, bool f32in, int64_t N, int64_t K, int g, bool asym,
+                       uint8_t *packed, float *row_scale, uint8_t *zp, hipStream_t st);
+
+struct LinearArgs {
+    const uint8_t *A;      // activation codes: int8 [M, K] or packed int4 [M, K/2]
+    const float *sx;       // [M]
+    const int32_t *rowsum; // [M]
+    const uint8_t *B;      // packed weights [N, K/2]
+    const float *sw;       // [N]
+    const uint8_t *zp;     // [N] or null (symmetric)
+    const void *bias;      // [N] or null
+    int bias_bf16;
+    const float *lr_t;        // [M, lr_r] or null
+    const uint16_t *lr_l2;    // bf16 [lr_r, N]
+    int lr_r;
+    void *Y;               // bf16 or int32 [M, N]
+    int y_i32;
+    int64_t M, N, K;
+};
+
+hipError_t launch_gemm(const LinearArgs &a, int act_bits, hipStream_t st);
+hipError_t launch_gemv(const LinearArgs &a, int act_bits, hipStream_t st);
+
+hipError_t launch_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r,
+                               float *t, hipStream_t st);
+
+}  // namespace w4

@@ -1,0 +1,276 @@
+// Activation rotate + per-token quantize for gfx950.
+//
+// Block Hadamard rotation of each token along K in groups of g (ComfyUI-INT-Crush README,
+// "Inference / INT4": Hadamard rotation fused with activation quantization), then dynamic
+// per-token symmetric quantization to int8 or int4 ("Inference / INT8": dynamic per-token
+// INT8 quantization; stable-diffusion.cpp PR #2010 "Summary": the W4A4 format).
+//
+// Work split.  A "team" of T lanes owns one token row.  Each lane holds C chunks of 16
+// consecutive elements; chunk c of lane t starts at element 16 * (c * T + t), so the lanes
+// of a wave read consecutive 32-byte pieces (coalesced).  A group of g elements is 16
+// consecutive chunks (g = 256: an aligned 16-lane row of the wave) or 4 (g = 64: a quad).
+//
+// The whole row stays in registers as fp64 (C * 16 doubles per lane), so X is read from
+// HBM once and the absmax needs no second pass.  fp64 makes the transform exact for bf16
+// inputs (8-bit significands, 8 stages of growth fit in 53 bits), so the codes match
+// rint(X' / s) of the plain definition except within ~1e-13 of a rounding tie.
+//
+// FWHT: 4 butterfly stages inside each 16-element chunk (bits 0-3 of the in-group index),
+// then the remaining bits across lanes.  g = 64: 2 stages over the quad with DPP lane moves.
+// g = 256: a 16 x 16 fp64 transpose through LDS within each 16-lane row, 4 more in-register
+// stages; lane r then holds group elements r + 16 j, and the int8 codes go back to
+// natural order through a 256-byte LDS transpose before the coalesced store.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int kTrStride = 18;                 // doubles per transpose row (16 + 2 pad)
+constexpr int kTrRow = 16 * kTrStride + 16;   // doubles per 16-lane row (2432 bytes)
+constexpr int kMaxBlock = 512;
+
+template <int G, int C, int BITS, bool F32IN>
+__global__ void __launch_bounds__(kMaxBlock)
+k_rotquant(const void *__restrict__ Xv, int64_t M, int K, int T, int R, void *__restrict__ qv,
+           float *__restrict__ tok_scale, int32_t *__restrict__ tok_rowsum) {
+    extern __shared__ double lds[];
+    constexpr int SEG = G / 16;
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
+
+    const int tid = threadIdx.x;
+    const int team = tid / T;
+    const int t = tid - team * T;
+    const int64_t row = (int64_t)blockIdx.x * R + team;
+    const bool valid = row < M;
+
+    double *tr = lds;                                                   // g = 256 only
+    double *slot_d = lds + (G == 256 ? (int)(blockDim.x >> 4) * kTrRow : 0);
+    int *slot_i = reinterpret_cast<int *>(slot_d + blockDim.x / SEG);
+
+    double v[C][16];
+
+    // ---- load and widen to fp64
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int64_t e0 = ((int64_t)c * T + t) * 16;
+        if (F32IN) {
+            uint4 w[4] = {};
+            if (valid) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(
+                    reinterpret_cast<const float *>(Xv) + row * K + e0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = p[j];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[c][4 * j + 0] = (double)__uint_as_float(w[j].x);
+                v[c][4 * j + 1] = (double)__uint_as_float(w[j].y);
+                v[c][4 * j + 2] = (double)__uint_as_float(w[j].z);
+                v[c][4 * j + 3] = (double)__uint_as_float(w[j].w);
+            }
+        } else {
+            uint4 w[2] = {};
+            if (valid) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(
+                    reinterpret_cast<const uint16_t *>(Xv) + row * K + e0);
+                w[0] = p[0];
+                w[1] = p[1];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v[c][8 * j + 0] = (double)bf16_lo(w[j].x);
+                v[c][8 * j + 1] = (double)bf16_hi(w[j].x);
+                v[c][8 * j + 2] = (double)bf16_lo(w[j].y);
+                v[c][8 * j + 3] = (double)bf16_hi(w[j].y);
+                v[c][8 * j + 4] = (double)bf16_lo(w[j].z);
+                v[c][8 * j + 5] = (double)bf16_hi(w[j].z);
+                v[c][8 * j + 6] = (double)bf16_lo(w[j].w);
+                v[c][8 * j + 7] = (double)bf16_hi(w[j].w);
+            }
+        }
+    }
+
+    // ---- Walsh-Hadamard transform of every group (unnormalised)
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        fwht16(v[c]);
+        if constexpr (G == 64) {
+            const double s1 = (tid & 1) ? -1.0 : 1.0;
+            const double s2 = (tid & 2) ? -1.0 : 1.0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s1, dpp_f64<kQuadXor1>(v[c][i]));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s2, dpp_f64<kQuadXor2>(v[c][i]));
+        } else {
+            double *buf = tr + (tid >> 4) * kTrRow;
+            const int r = tid & 15;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) buf[r * kTrStride + i] = v[c][i];
+            __syncthreads();
+            double u[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) u[j] = buf[j * kTrStride + r];
+            __syncthreads();
+            fwht16(u);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[c][j] = u[j];  // group element r + 16 j
+        }
+    }
+
+    // ---- per-token absmax
+    double am = 0.0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmax(am, fabs(v[c][i]));
+#pragma unroll
+    for (int off = 1; off < SEG; off <<= 1) am = fmax(am, __shfl_xor(am, off));
+    if ((tid & (SEG - 1)) == 0) slot_d[tid / SEG] = am;
+    __syncthreads();
+    const int nseg = T / SEG;
+    double amax = 0.0;
+    for (int s = 0; s < nseg; ++s) amax = fmax(amax, slot_d[team * nseg + s]);
+
+    // s = fp32(amax' / qmax) with amax' = amax / sqrt(g) (exact power-of-two scaling)
+    const float scale = (float)((amax * INV_SQRT_G) / (double)QMAX);
+    const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
+    if (valid && t == 0) tok_scale[row] = scale;
+
+    // ---- quantize, restore natural order, pack, store
+    int rowsum = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        int code[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int qi = __double2loint(fma(v[c][i], rr, kRoundMagic));
+            code[i] = min(max(qi, -QMAX - 1), QMAX);
+        }
+        uint32_t d[4];
+        if constexpr (G == 256) {
+            uint8_t *b = reinterpret_cast<uint8_t *>(tr + (tid >> 4) * kTrRow);
+            const int r = tid & 15;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) b[r + 16 * j] = (uint8_t)code[j];
+            __syncthreads();
+            const uint4 w = *reinterpret_cast<const uint4 *>(b + 16 * r);
+            __syncthreads();
+            d[0] = w.x; d[1] = w.y; d[2] = w.z; d[3] = w.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                d[j] = (uint32_t)(code[4 * j] & 0xff) | ((uint32_t)(code[4 * j + 1] & 0xff) << 8) |
+                       ((uint32_t)(code[4 * j + 2] & 0xff) << 16) |
+                       ((uint32_t)(code[4 * j + 3] & 0xff) << 24);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rowsum = __builtin_amdgcn_sdot4((int)d[j], 0x01010101, rowsum, false);
+        if (valid) {
+            const int64_t e0 = ((int64_t)c * T + t) * 16;
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<uint4 *>(reinterpret_cast<int8_t *>(qv) + row * K + e0) =
+                    make_uint4(d[0], d[1], d[2], d[3]);
+            } else {
+                uint32_t x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = d[j] & 0x0F0F0F0Fu;
+                    x[j] = lo | (lo >> 4);  // bytes 0 and 2 = (k, k+1) and (k+2, k+3) nibble pairs
+                }
+                const uint32_t p0 = __builtin_amdgcn_perm(x[1], x[0], 0x06040200u);
+                const uint32_t p1 = __builtin_amdgcn_perm(x[3], x[2], 0x06040200u);
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(qv) + row * (K / 2) + e0 / 2) =
+                    make_uint2(p0, p1);
+            }
+        }
+    }
+
+    // ---- per-token code sum
+#pragma unroll
+    for (int off = 1; off < SEG; off <<= 1) rowsum += __shfl_xor(rowsum, off);
+    if ((tid & (SEG - 1)) == 0) slot_i[tid / SEG] = rowsum;
+    __syncthreads();
+    if (valid && t == 0) {
+        int total = 0;
+        for (int s = 0; s < nseg; ++s) total += slot_i[team * nseg + s];
+        tok_rowsum[row] = total;
+    }
+}
+
+struct Split {
+    int C, T, R;
+};
+
+bool choose_split(int64_t K, int g, Split &sp) {
+    if (K <= 0 || K % g) return false;
+    const int64_t chunks = K / 16;
+    const int seg = g / 16;
+    for (int C = 4; C >= 1; --C) {
+        if (chunks % C) continue;
+        const int64_t T = chunks / C;
+        if (T % seg || T > kMaxBlock) continue;
+        int R = 1;
+        while (R * T < 256 && 2 * R * T <= kMaxBlock) R *= 2;
+        while ((R * T) % 64 && (R + 1) * T <= kMaxBlock) ++R;
+        sp = {C, (int)T, R};
+        return true;
+    }
+    return false;
+}
+
+template <int G, int C, int BITS, bool F32IN>
+hipError_t launch_t(const void *X, int64_t M, int64_t K, const Split &sp, void *q, float *s,
+                    int32_t *rs, hipStream_t st) {
+    const int block = sp.R * sp.T;
+    const size_t lds = (G == 256 ? (size_t)(block / 16) * kTrRow * sizeof(double) : 0) +
+                       (size_t)(block / (G / 16)) * (sizeof(double) + sizeof(int));
+    if (lds > 65536) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_rotquant<G, C, BITS, F32IN>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (attr != hipSuccess) return attr;
+    }
+    const int64_t grid = (M + sp.R - 1) / sp.R;
+    hipLaunchKernelGGL((k_rotquant<G, C, BITS, F32IN>), dim3((unsigned)grid), dim3(block), lds, st,
+                       X, M, (int)K, sp.T, sp.R, q, s, rs);
+    return hipGetLastError();
+}
+
+template <int G, int BITS, bool F32IN>
+hipError_t dispatch_c(const void *X, int64_t M, int64_t K, const Split &sp, void *q, float *s,
+                      int32_t *rs, hipStream_t st) {
+    switch (sp.C) {
+        case 1: return launch_t<G, 1, BITS, F32IN>(X, M, K, sp, q, s, rs, st);
+        case 2: return launch_t<G, 2, BITS, F32IN>(X, M, K, sp, q, s, rs, st);
+        case 3: return launch_t<G, 3, BITS, F32IN>(X, M, K, sp, q, s, rs, st);
+        default: return launch_t<G, 4, BITS, F32IN>(X, M, K, sp, q, s, rs, st);
+    }
+}
+
+}  // namespace
+
+bool rotquant_supported(int64_t K, int g) {
+    Split sp;
+    return choose_split(K, g, sp);
+}
+
+hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
+                           void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st) {
+    Split sp;
+    if (!choose_split(K, g, sp)) return hipErrorInvalidValue;
+    if (M == 0) return hipSuccess;
+#define W4_RQ(G, B, F) return dispatch_c<G, B, F>(X, M, K, sp, q, tok_scale, tok_rowsum, st)
+    if (g == 64) {
+        if (bits == 8) { if (f32in) W4_RQ(64, 8, true); else W4_RQ(64, 8, false); }
+        else { if (f32in) W4_RQ(64, 4, true); else W4_RQ(64, 4, false); }
+    } else {
+        if (bits == 8) { if (f32in) W4_RQ(256, 8, true); else W4_RQ(256, 8, false); }
+        else { if (f32in) W4_RQ(256, 4, true); else W4_RQ(256, 4, false); }
+    }
+#undef W4_RQ
+}
+
+}  // namespace w4

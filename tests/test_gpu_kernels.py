@@ -1,0 +1,195 @@
+"""Kernel-level parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Each test prints what it runs before touching the GPU, so a failing case is named
+even if the process dies.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import int4_weight_quantized_block_amd as w4
+from parity import check_codes, check_scales, np_, rel_frob, FROB_TOL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def act_input(M, K, seed, dtype=torch.bfloat16, n_out=None, scale=30.0):
+    r = rng(seed)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    n_out = max(1, K // 100) if n_out is None else n_out
+    x[:, r.choice(K, n_out, replace=False)] *= scale
+    return torch.from_numpy(x).to(dtype)
+
+
+# --------------------------------------------------------------------------- integer GEMM
+@pytest.mark.parametrize("M,N,K,bits,asym", [
+    (16, 128, 256, 8, False), (1, 64, 256, 8, True), (5, 48, 320, 8, False), (64, 256, 512, 4, False),
+    (33, 272, 1024, 4, True), (128, 128, 256, 8, False), (200, 136, 448, 8, True), (300, 520, 3072, 4, False),
+    (257, 256, 4096, 8, False), (130, 1000, 192, 4, True), (65, 17, 64, 8, False),
+])
+def test_accumulators_bit_exact_on_oracle_codes(M, N, K, bits, asym):
+    """acc[m, n] = sum_k q (c - z) from the oracle's own codes, through W4_OUT_I32."""
+    say("acc exact M=%d N=%d K=%d bits=%d asym=%s" % (M, N, K, bits, asym))
+    r = rng(M * 7 + N * 3 + K + bits + asym)
+    qmax = oracle.QMAX[bits]
+    q = r.integers(-qmax - 1, qmax + 1, size=(M, K)).astype(np.int8)
+    if asym:
+        codes = r.integers(0, 16, size=(N, K))
+        zp = r.integers(0, 16, size=N).astype(np.uint8)
+    else:
+        codes = r.integers(-8, 8, size=(N, K))
+        zp = None
+    packed = oracle.pack_nibbles(codes)
+    acc = oracle.gemm_i64(q, oracle.weight_operand(packed, zp, asym))
+    qa = q if bits == 8 else oracle.pack_nibbles(q)
+    y = w4.w4_linear_cached_rot(
+        to_dev(qa), to_dev(np.ones(M, np.float32)), to_dev(q.astype(np.int64).sum(1).astype(np.int32)), bits,
+        to_dev(packed), to_dev(np.ones(N, np.float32)), to_dev(zp) if asym else None, out_i32=True)
+    got = np_(y).astype(np.int64)
+    bad = np.argwhere(got != acc)
+    assert bad.size == 0, "first mismatches %s: gpu %s oracle %s" % (
+        bad[:4].tolist(), got[tuple(bad[:4].T)].tolist(), acc[tuple(bad[:4].T)].tolist())
+
+
+def test_accumulators_extreme_codes():
+    """All activation codes -128 against weight codes -8 (and 127 against 7) at K = 4096."""
+    say("acc extremes")
+    M, N, K = 80, 64, 4096
+    q = np.full((M, K), -128, np.int8)
+    q[1::2] = 127
+    codes = np.full((N, K), -8)
+    codes[1::2] = 7
+    packed = oracle.pack_nibbles(codes)
+    acc = oracle.gemm_i64(q, oracle.weight_operand(packed, None, False))
+    for m in (M, 16):
+        y = w4.w4_linear_cached_rot(to_dev(q[:m]), to_dev(np.ones(m, np.float32)),
+                                    to_dev(q[:m].astype(np.int64).sum(1).astype(np.int32)), 8,
+                                    to_dev(packed), to_dev(np.ones(N, np.float32)), out_i32=True)
+        assert np.array_equal(np_(y).astype(np.int64), acc[:m])
+
+
+# --------------------------------------------------------------------------- activations
+@pytest.mark.parametrize("M,K,g,bits,dtype", [
+    (16, 256, 64, 8, torch.float32), (16, 256, 256, 8, torch.bfloat16), (7, 3072, 256, 8, torch.bfloat16),
+    (33, 3072, 256, 4, torch.bfloat16), (5, 12288, 256, 8, torch.bfloat16), (9, 12288, 256, 4, torch.bfloat16),
+    (3, 4096, 256, 8, torch.bfloat16), (300, 768, 256, 8, torch.bfloat16), (21, 192, 64, 4, torch.float32),
+    (40, 1280, 64, 8, torch.bfloat16), (2, 4608, 256, 8, torch.float32), (1, 64, 64, 4, torch.bfloat16),
+])
+def test_rotate_quant_act_matches_oracle(M, K, g, bits, dtype):
+    say("rotquant M=%d K=%d g=%d bits=%d %s" % (M, K, g, bits, dtype))
+    X = act_input(M, K, seed=M + K + g + bits, dtype=dtype)
+    X[M // 2] = 0  # an all-zero token
+    ref = oracle.rotate_quant_act(X, g, bits)
+    q, s, rs = w4.w4_rotate_quant_act(X.to(DEV), g, bits)
+    amax64 = np.abs(ref["rotated"]).max(axis=1) / oracle.QMAX[bits]
+    eq = check_scales(np_(s), ref["scale"], amax64, "tok_scale")
+    assert eq.all()
+    qg = np_(q)
+    if bits == 4:
+        assert qg.shape == (M, K // 2)
+        codes = oracle.unpack_nibbles(qg, signed=True)
+    else:
+        codes = qg
+    n = check_codes(codes, ref["q"], ref["pre"], "act codes")
+    if n == 0:
+        want = ref["packed"] if bits == 4 else ref["q"].view(np.uint8)
+        assert np.array_equal(qg.view(np.uint8), want)
+    assert np.array_equal(np_(rs).astype(np.int64), codes.astype(np.int64).sum(1))
+    assert np_(s)[M // 2] == 0 and np.all(codes[M // 2] == 0)
+
+
+def test_rotate_quant_rejects_unsupported_k():
+    # 37 groups of 256: K/16 = 592 chunks has no split C * T with C <= 4, T % 16 == 0, T <= 512
+    X = torch.zeros((2, 37 * 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(w4.W4Error) as e:
+        w4.w4_rotate_quant_act(X, 256, 8)
+    assert e.value.status == w4.W4_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- weights
+@pytest.mark.parametrize("N,K,g,asym,dtype", [
+    (256, 256, 64, False, torch.float32), (64, 3072, 256, False, torch.bfloat16),
+    (48, 4096, 256, True, torch.bfloat16), (33, 12288, 256, True, torch.bfloat16),
+    (17, 192, 64, True, torch.float32), (8, 9216, 256, False, torch.bfloat16),
+])
+def test_pack_weights_matches_oracle(N, K, g, asym, dtype):
+    say("pack N=%d K=%d g=%d asym=%s %s" % (N, K, g, asym, dtype))
+    r = rng(N + K)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(dtype)
+    W[1] = 0  # zero row
+    if N > 4:
+        W[2] = W[2].abs() + 0.01  # all-positive row (asym: z = 0)
+        W[3] = -(W[3].abs() + 0.01)
+    ref = oracle.pack_weights(W, g, asym)
+    packed, s, zp = w4.w4_pack_weights(W.to(DEV), g, asym)
+    Wr = ref["rotated"]
+    if asym:
+        unr = (np.maximum(Wr.max(1), 0) - np.minimum(Wr.min(1), 0)) / 15.0
+    else:
+        unr = np.abs(Wr).max(1) / 7.0
+    assert check_scales(np_(s), ref["scale"], unr, "row_scale").all()
+    pg = np_(packed)
+    assert pg.shape == (N, K // 2)
+    codes = oracle.unpack_nibbles(pg, signed=not asym)
+    if asym:
+        zg = np_(zp)
+        zdiff = zg != ref["zp"]
+        if zdiff.any():  # only at a tie of -lo/s
+            f = np.abs(ref["zpre"][zdiff] - np.floor(ref["zpre"][zdiff]) - 0.5)
+            assert np.all(f <= 1e-6)
+        pre = ref["pre"] + ref["zp"].astype(np.float64)[:, None]
+        check_codes(codes[~zdiff], ref["codes"][~zdiff], pre[~zdiff], "weight codes")
+    else:
+        check_codes(codes, ref["codes"], ref["pre"], "weight codes")
+
+
+# --------------------------------------------------------------------------- whole layer
+@pytest.mark.parametrize("M,N,K,g,bits,asym,lr", [
+    (16, 256, 256, 64, 8, False, False), (100, 200, 512, 256, 8, False, True), (40, 96, 768, 256, 4, True, True),
+    (130, 64, 256, 64, 4, False, False), (1, 300, 1024, 256, 8, True, False),
+])
+def test_linear_matches_oracle(M, N, K, g, bits, asym, lr):
+    say("linear M=%d N=%d K=%d g=%d bits=%d asym=%s lr=%s" % (M, N, K, g, bits, asym, lr))
+    r = rng(M + N + K)
+    X = act_input(M, K, seed=M * 3 + K)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    L1 = L2 = None
+    if lr:
+        L1 = torch.from_numpy((r.standard_normal((K, 16)) * 0.01).astype(np.float32)).to(torch.bfloat16)
+        L2 = torch.from_numpy((r.standard_normal((16, N)) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    ref = oracle.linear(X, W, g, bits, asym, bias=bias, L1=L1, L2=L2)
+    pw = ref["w"]
+    Xd = X.to(DEV)
+    args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
+    low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.to(DEV)) if lr else None
+    y = w4.w4_linear(Xd, g, bits, *args, bias=bias.to(DEV), lowrank=low)
+    err = rel_frob(y, ref["y64"])
+    say("  rel frob %.3e" % err)
+    assert err <= FROB_TOL
+    # the same through the cached half, with a precomputed low-rank t
+    q, s, rs = w4.w4_rotate_quant_act(Xd, g, bits)
+    if lr:
+        t = w4.w4_lowrank_down(Xd, L1.to(DEV))
+        tref = oracle.to_f64(X) @ oracle.to_f64(L1)
+        assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
+        low = w4.LowRank(l2=L2.to(DEV), t=t)
+    y2 = w4.w4_linear_cached_rot(q, s, rs, bits, *args, bias=bias.to(DEV), lowrank=low)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
