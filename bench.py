@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Throughput of the ConvRot INT4 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--M M]
+
+One "step" is one pass of the whole layer over one batch: rotate + quantize the
+activations (w4_rotate_quant_act) and the integer GEMM with the fused dequant
+epilogue (w4_linear_cached_rot); for the 20-block workload a step is all 80 linears
+of the 20 blocks with the rotation cache and the low-rank branches.  Weights are packed
+once before timing (an offline step).  Inputs are resident in HBM; the timed loop
+cycles through enough distinct input copies (> 256 MB) that reads come from HBM, not
+from the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``roofline`` describes the dominant kernel, timed live with HIP
+events around its launches on the stream it runs on; ``cpu_baseline`` is the CPU oracle
+timed on this host's cores on a bounded sample of the same workload.
+
+Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
+  attn_proj    (default) W4A8 g=256, X [4096, 3072] -> 3072           metric: TOPS
+  mlp_up       W4A4 g=256, X [4096, 3072] -> 12288                   metric: TOPS
+  mlp_down     W4A4 g=256, X [4096, 12288] -> 3072                   metric: TOPS
+  small_m      asym W4A8 g=256, M in {1,4,16,64}, K/N 4096/12288     metric: weight GB/s
+  double_block 20 blocks x {QKV, out, up, down} at M=4608, cached    metric: TOPS
+  tiny         W4A8 g=64, 16 x 256 -> 256                            metric: TOPS
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A8/W4A4 linear TOPS at M=4096; weight GB/s at M≤16; % of roofline"
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POPS
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="attn_proj",
+                    choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny"])
+    ap.add_argument("--M", type=int, default=None, help="tokens (small_m: 1, 4, 16 or 64)")
+    ap.add_argument("--K", type=int, default=12288, help="small_m: input features (4096 or 12288)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="token rows in the CPU oracle sample")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- workloads
+class Linear:
+    """One quantized linear with its inputs on the GPU (weights packed once, untimed)."""
+
+    def __init__(self, X, W, bias, g, bits, asym, lowrank=None):
+        import int4_weight_quantized_block_amd as w4
+        self.g, self.bits, self.asym = g, bits, asym
+        self.M, self.K = X.shape
+        self.N = W.shape[0]
+        self.X = X
+        self.bias = bias
+        self.packed, self.s_w, self.zp = w4.w4_pack_weights(W, g, asym)
+        self.lowrank = lowrank
+
+    def ops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of one GEMM launch (codes, weights, scales, bias, output)."""
+        M, N, K = self.M, self.N, self.K
+        a = M * K if self.bits == 8 else M * K // 2
+        w = N * K // 2 + 4 * N + (N if self.asym else 0)
+        return a + w + 8 * M + 2 * N + 2 * M * N
+
+    def weight_bytes(self):
+        return self.N * self.K // 2 + 4 * self.N + (self.N if self.asym else 0)
+
+    def rotquant_bytes(self):
+        M, K = self.M, self.K
+        return 2 * M * K + (M * K if self.bits == 8 else M * K // 2) + 8 * M
+
+
+def build_workload(args, dev):
+    import torch
+    import synth
+    name = args.workload
+    if name == "attn_proj":
+        M = args.M or 4096
+        d = synth.attn_proj(M=M)
+        return [[("attn_proj", d["X"], d["W"], d["bias"], 256, 8, False)]], {
+            "workload": "attn_proj", "M": M, "K": 3072, "N": 3072, "g": 256, "act_bits": 8,
+            "weights": "sym int4 per-row"}
+    if name in ("mlp_up", "mlp_down"):
+        M = args.M or 4096
+        up = synth.mlp_up(M=M)
+        if name == "mlp_up":
+            return [[("mlp_up", up["X"], up["W"], up["bias"], 256, 4, False)]], {
+                "workload": "mlp_up", "M": M, "K": 3072, "N": 12288, "g": 256, "act_bits": 4,
+                "weights": "sym int4 per-row"}
+        dn = synth.mlp_down_weights()
+        # the down-projection input has the shape of GELU(up); drawn as GELU of a scaled normal
+        h = torch.nn.functional.gelu(torch.randn((M, 12288), generator=torch.Generator().manual_seed(2010)) * 0.6)
+        return [[("mlp_down", h.to(torch.bfloat16), dn["W"], dn["bias"], 256, 4, False)]], {
+            "workload": "mlp_down", "M": M, "K": 12288, "N": 3072, "g": 256, "act_bits": 4,
+            "weights": "sym int4 per-row"}
+    if name == "small_m":
+        M = args.M or 16
+        K = args.K
+        N = 12288 if K == 4096 else 4096
+        d = synth.small_m(M, K, N)
+        return [[("small_m", d["X"], d["W"], d["bias"], 256, 8, True)]], {
+            "workload": "small_m", "M": M, "K": K, "N": N, "g": 256, "act_bits": 8,
+            "weights": "asym int4 per-row + zero point"}
+    if name == "tiny":
+        d = synth.tiny()
+        return [[("tiny", d["X"], d["W"], d["bias"], 64, 8, False)]], {
+            "workload": "tiny", "M": 16, "K": 256, "N": 256, "g": 64, "act_bits": 8,
+            "weights": "sym int4 per-row"}
+    raise SystemExit("unknown workload")
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(layer, rows_wanted):
+    """The oracle as it stands, on this host's cores, over the first ``rows_wanted`` token rows
+    of the layer: rotate + quantize, int64 GEMM, fp64 epilogue (weight packing not counted).
+    Returns (dict, seconds, rows)."""
+    import oracle
+    name, X, W, bias, g, bits, asym = layer
+    M = X.shape[0]
+    rows = min(M, rows_wanted)
+    Xs = X[:rows].cpu()
+    pw = oracle.pack_weights(W.cpu(), g, asym)
+    t1 = time.perf_counter()
+    qa = oracle.rotate_quant_act(Xs, g, bits)
+    oracle.linear_from_codes(qa["q"], qa["scale"], pw["packed"], pw["scale"], pw["zp"], asym, bias.cpu())
+    sec = time.perf_counter() - t1
+    return {"cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%s: %d of %d token rows, one pass (rotate + quantize + int64 GEMM + epilogue)"
+                      % (name, rows, M), "seconds": round(sec, 3)}, sec, rows
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import int4_weight_quantized_block_amd as w4
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w4.load_library()
+    log("bench: workload %s on %s" % (args.workload, torch.cuda.get_device_name(0)))
+
+    if args.workload == "double_block":
+        return bench_double_block(args, dev)
+
+    layer_specs, cfg = build_workload(args, dev)
+    name, X, W, bias, g, bits, asym = layer_specs[0][0]
+    lin = Linear(X.to(dev), W.to(dev), bias.to(dev), g, bits, asym)
+    # distinct copies of the inputs so the timed loop streams from HBM
+    per_copy = lin.X.numel() * lin.X.element_size() + lin.packed.numel() + lin.s_w.numel() * 4
+    ncopy = max(1, min(64, math.ceil(2 * MALL_BYTES / per_copy)))
+    Xs = [lin.X] + [lin.X.clone() for _ in range(ncopy - 1)]
+    Ps = [(lin.packed, lin.s_w, lin.zp)] + [(lin.packed.clone(), lin.s_w.clone(),
+                                            lin.zp.clone() if lin.zp is not None else None)
+                                           for _ in range(ncopy - 1)]
+    M, K, N = lin.M, lin.K, lin.N
+    qbuf = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    rs = torch.empty((M,), dtype=torch.int32, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L = w4.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def rotquant(i):
+        x = Xs[i % ncopy]
+        w4._check(L.w4_rotate_quant_act(x.data_ptr(), w4.W4_BF16 if x.dtype == torch.bfloat16 else w4.W4_F32,
+                                        M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr))
+
+    def gemm(i):
+        p, s, z = Ps[i % ncopy]
+        w4._check(L.w4_linear_cached_rot(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(),
+                                         s.data_ptr(), z.data_ptr() if z is not None else None,
+                                         lin.bias.data_ptr(), w4.W4_BF16, None, M, N, K, Y.data_ptr(),
+                                         w4.W4_OUT_BF16, None, 0, sptr))
+
+    for i in range(args.warmup):
+        rotquant(i)
+        gemm(i)
+    torch.cuda.synchronize()
+    log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
+                                                                            args.warmup))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        rotquant(i)
+        ev[i][1].record(stream)
+        gemm(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
+    t_mm = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    ms_step = wall / args.steps * 1e3
+    log("bench: %.3f ms/step wall; rotate+quant %.2f us, GEMM %.2f us per launch" % (ms_step, t_rq * 1e6,
+                                                                                   t_mm * 1e6))
+
+    small = args.workload == "small_m"
+    if small:
+        value = lin.weight_bytes() / (wall / args.steps) / 1e9
+        unit = "GB/s"
+        roof = {"bound": "hbm", "achieved": lin.gemm_bytes() / t_mm / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        value = lin.ops() / (wall / args.steps) / 1e12
+        unit = "TOPS"
+        roof = {"bound": "mfma", "achieved": lin.ops() / t_mm / 1e12, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "k_gemv" if M <= 64 else "k_gemm"
+    roof["traffic"] = measured_traffic(roof["kernel"], cfg)
+    roof["launch_us"] = round(t_mm * 1e6, 3)
+    extra = {
+        "rotquant_us": round(t_rq * 1e6, 3),
+        "rotquant_hbm_gbs": round(lin.rotquant_bytes() / t_rq / 1e9, 1),
+        "rotquant_hbm_frac": round(lin.rotquant_bytes() / t_rq / 1e9 / PEAK_HBM_GBS, 4),
+        "gemm_tops": round(lin.ops() / t_mm / 1e12, 2),
+        "gemm_weight_gbs": round(lin.weight_bytes() / t_mm / 1e9, 1),
+        "gemm_alg_bytes": lin.gemm_bytes(),
+        "input_copies": ncopy,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or M
+        log("bench: timing the CPU oracle on %d rows" % rows)
+        cpu, sec, rows = cpu_baseline(layer_specs[0][0], rows)
+        if small:  # weight bytes streamed per full pass over the M tokens
+            cpu["value"] = round(lin.weight_bytes() / (sec * M / rows) / 1e9, 4)
+            cpu["unit"] = "GB/s"
+        else:
+            cpu["value"] = round(lin.ops() * rows / M / sec / 1e12, 6)
+            cpu["unit"] = "TOPS"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8" if bits == 8 else "int4",
+        "data": "synthetic", "config": dict(cfg, parallelism="single-gpu"),
+        "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def measured_traffic(kernel, cfg):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    key = "%s:%s" % (kernel, cfg["workload"])
+    ent = data.get(key)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "int4_weight_quantized_block_amd", "csrc", ent["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["sha256"]:
+        return None  # the kernel changed since the counters were taken
+    return ent["bytes"]
+
+
+def bench_double_block(args, dev):
+    import torch
+    import synth
+    import int4_weight_quantized_block_amd as w4
+    nb = synth.N_BLOCKS
+    M = args.M or synth.DOUBLE_BLOCK_TOKENS
+    blocks = []
+    for b in range(nb):
+        blk = synth.double_block(b, dev, M=M)
+        lins = {}
+        for name, k, n in synth.DOUBLE_BLOCK_LINEARS:
+            p = blk[name]
+            packed, s_w, _ = w4.w4_pack_weights(p["W"], 256, False)
+            lins[name] = (packed, s_w, p["bias"], p["L1"], p["L2"])
+            del p["W"]
+        blocks.append((blk["x"], blk["attn"], lins))
+        log("bench: block %d packed" % b)
+    torch.cuda.synchronize()
+    K = synth.DIT_HIDDEN
+    ops = sum(2.0 * M * k * n for _, k, n in synth.DOUBLE_BLOCK_LINEARS) * nb
+    h = torch.empty((M, synth.DIT_MLP), dtype=torch.bfloat16, device=dev)
+    outs = {name: torch.empty((M, n), dtype=torch.bfloat16, device=dev) for name, _, n in synth.DOUBLE_BLOCK_LINEARS}
+    t_bufs = {name: torch.empty((M, synth.LOWRANK), dtype=torch.float32, device=dev)
+              for name, _, _ in synth.DOUBLE_BLOCK_LINEARS}
+    stream = torch.cuda.current_stream(dev)
+    gemm_times = []
+
+    def step(record):
+        for x, attn, lins in blocks:
+            cache = w4.RotationCache()
+            for name, inp in (("qkv", x), ("up", x), ("out", attn)):
+                packed, s_w, bias, L1, L2 = lins[name]
+                q, sx, rs = cache.get(inp, 256, 8)
+                t = w4.w4_lowrank_down(inp, L1)
+                e0 = torch.cuda.Event(enable_timing=True) if record else None
+                if record:
+                    e0.record(stream)
+                w4.w4_linear_cached_rot(q, sx, rs, 8, packed, s_w, bias=bias, lowrank=w4.LowRank(l2=L2, t=t),
+                                        out=outs[name])
+                if record:
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e1.record(stream)
+                    gemm_times.append((e0, e1))
+            torch.nn.functional.gelu(outs["up"], out=h)  # host glue between the MLP linears
+            packed, s_w, bias, L1, L2 = lins["down"]
+            q, sx, rs = w4.w4_rotate_quant_act(h, 256, 8)
+            t = w4.w4_lowrank_down(h, L1)
+            w4.w4_linear_cached_rot(q, sx, rs, 8, packed, s_w, bias=bias, lowrank=w4.LowRank(l2=L2, t=t),
+                                    out=outs["down"])
+            cache.clear()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall / args.steps * 1e3
+    value = ops / (wall / args.steps) / 1e12
+    g_ops = 2.0 * M * K * (synth.DIT_QKV + synth.DIT_MLP + synth.DIT_HIDDEN)
+    t_g = sum(a.elapsed_time(b) for a, b in gemm_times) * 1e-3 / (args.steps * nb)
+    roof = {"bound": "mfma", "achieved": g_ops / t_g / 1e12, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "k_gemm"
+    roof["traffic"] = None
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "double_block", "blocks": nb, "M": M, "g": 256, "act_bits": 8,
+                   "lowrank": synth.LOWRANK, "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
