@@ -20,6 +20,8 @@
 // g = 256: a 16 x 16 fp64 transpose through LDS within each 16-lane row, 4 more in-register
 // stages; lane r then holds group elements r + 16 j, and the int8 codes go back to
 // natural order through a 256-byte LDS transpose before the coalesced store.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -200,6 +202,180 @@ k_rotquant(const void *__restrict__ Xv, int64_t M, int K, int T, int R, void *__
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Streaming variant for K % 256 == 0 (every DiT / text-encoder width): no LDS transposes.
+//
+// A quad of lanes owns each 256-element block of a row; lane p of the quad holds the four
+// 16-element chunks p, p+4, p+8, p+12 (slots c = 0..3), so a quad reads and writes 128
+// contiguous bytes per slot.  Within a block, element e = 16 * (p + 4c) + i:
+//   g = 256: bits 0-3 (i) and 6-7 (c) are butterflies in registers, bits 4-5 (p) use DPP quad
+//            exchanges - the whole group never leaves the quad;
+//   g = 64:  slot c is its own group (bits 0-3 in registers, bits 4-5 across the quad).
+// Each lane's 16 codes of a chunk are contiguous in the output, so they are packed and stored
+// directly.  A team of T = K / 64 lanes owns a row; a workgroup owns R rows per iteration and
+// loops over row groups with the next group's input loads in flight while it transforms the
+// current one (one HBM read per element, no second pass).
+template <int G, int BITS, bool F32IN>
+__global__ void __launch_bounds__(512)
+k_rotquant_stream(const void *__restrict__ Xv, int64_t M, int K, int T, int R, int64_t ngroups,
+                  void *__restrict__ qv, float *__restrict__ tok_scale, int32_t *__restrict__ tok_rowsum) {
+    __shared__ double slot_d[2][128];
+    __shared__ int slot_i[2][128];
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
+    constexpr int NW = F32IN ? 4 : 2;  // 16-byte words per 16-element chunk
+
+    const int tid = threadIdx.x;
+    const int team = tid / T;
+    const int t = tid - team * T;
+    const int p = tid & 3;           // position in the quad
+    const int blk = t >> 2;          // 256-element block of the row
+    const int nquads = T / 4;        // quads per row
+
+    auto load = [&](int64_t rg, uint4 (&w)[4][NW]) {
+        const int64_t row = rg * R + team;
+        if (row < M) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t e0 = (int64_t)blk * 256 + 16 * (p + 4 * c);
+                const uint4 *src = F32IN ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(Xv) + row * K + e0)
+                                         : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Xv) + row * K + e0);
+#pragma unroll
+                for (int j = 0; j < NW; ++j) w[c][j] = src[j];
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int j = 0; j < NW; ++j) w[c][j] = make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // bf16 input: the next row group's loads are issued before this one is transformed
+    // (fp32 input, the small fp32 case, loads at the top of each iteration to save registers)
+    uint4 nxt[4][NW];
+    int64_t rg = blockIdx.x;
+    if (!F32IN && rg < ngroups) load(rg, nxt);
+    int par = 0;
+    for (; rg < ngroups; rg += gridDim.x, par ^= 1) {
+        if constexpr (F32IN) load(rg, nxt);
+        double v[4][16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if constexpr (F32IN) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[c][4 * j + 0] = (double)__uint_as_float(nxt[c][j].x);
+                    v[c][4 * j + 1] = (double)__uint_as_float(nxt[c][j].y);
+                    v[c][4 * j + 2] = (double)__uint_as_float(nxt[c][j].z);
+                    v[c][4 * j + 3] = (double)__uint_as_float(nxt[c][j].w);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    v[c][8 * j + 0] = (double)bf16_lo(nxt[c][j].x);
+                    v[c][8 * j + 1] = (double)bf16_hi(nxt[c][j].x);
+                    v[c][8 * j + 2] = (double)bf16_lo(nxt[c][j].y);
+                    v[c][8 * j + 3] = (double)bf16_hi(nxt[c][j].y);
+                    v[c][8 * j + 4] = (double)bf16_lo(nxt[c][j].z);
+                    v[c][8 * j + 5] = (double)bf16_hi(nxt[c][j].z);
+                    v[c][8 * j + 6] = (double)bf16_lo(nxt[c][j].w);
+                    v[c][8 * j + 7] = (double)bf16_hi(nxt[c][j].w);
+                }
+            }
+        }
+        const int64_t row = rg * R + team;
+        if (!F32IN && rg + gridDim.x < ngroups) load(rg + gridDim.x, nxt);  // in flight during the transform
+
+        // ---- Walsh-Hadamard butterflies (unnormalised)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) fwht16(v[c]);
+        if constexpr (G == 256) {
+#pragma unroll
+            for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((c & h) == 0)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const double a = v[c][i], b = v[c + h][i];
+                            v[c][i] = a + b;
+                            v[c + h][i] = a - b;
+                        }
+        }
+        {
+            const double s1 = (p & 1) ? -1.0 : 1.0, s2 = (p & 2) ? -1.0 : 1.0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s1, dpp_f64<kQuadXor1>(v[c][i]));
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s2, dpp_f64<kQuadXor2>(v[c][i]));
+        }
+
+        // ---- per-token absmax: quad, then the row's quads through LDS (double-buffered slots)
+        double am = 0.0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) am = fmax(am, fabs(v[c][i]));
+        am = fmax(am, dpp_f64<kQuadXor1>(am));
+        am = fmax(am, dpp_f64<kQuadXor2>(am));
+        if (p == 0) slot_d[par][tid >> 2] = am;
+        __syncthreads();
+        double amax = 0.0;
+        for (int s = 0; s < nquads; ++s) amax = fmax(amax, slot_d[par][team * nquads + s]);
+        const float scale = (float)((amax * INV_SQRT_G) / (double)QMAX);
+        const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
+        if (row < M && t == 0) tok_scale[row] = scale;
+
+        // ---- quantize, pack, store
+        int rowsum = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int q4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = __double2loint(fma(v[c][4 * j + r], rr, kRoundMagic));
+                    q4[r] = min(max(qi, -QMAX - 1), QMAX);
+                }
+                d[j] = (uint32_t)(q4[0] & 0xff) | ((uint32_t)(q4[1] & 0xff) << 8) | ((uint32_t)(q4[2] & 0xff) << 16) |
+                       ((uint32_t)(q4[3] & 0xff) << 24);
+                rowsum = __builtin_amdgcn_sdot4((int)d[j], 0x01010101, rowsum, false);
+            }
+            if (row < M) {
+                const int64_t e0 = (int64_t)blk * 256 + 16 * (p + 4 * c);
+                if constexpr (BITS == 8) {
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<int8_t *>(qv) + row * K + e0) = make_uint4(d[0], d[1], d[2], d[3]);
+                } else {
+                    uint32_t x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo = d[j] & 0x0F0F0F0Fu;
+                        x[j] = lo | (lo >> 4);
+                    }
+                    *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(qv) + row * (K / 2) + e0 / 2) =
+                        make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u));
+                }
+            }
+        }
+        rowsum += __shfl_xor(rowsum, 1);
+        rowsum += __shfl_xor(rowsum, 2);
+        if (p == 0) slot_i[par][tid >> 2] = rowsum;
+        __syncthreads();
+        if (row < M && t == 0) {
+            int total = 0;
+            for (int s = 0; s < nquads; ++s) total += slot_i[par][team * nquads + s];
+            tok_rowsum[row] = total;
+        }
+    }
+}
+
 struct Split {
     int C, T, R;
 };
@@ -250,18 +426,49 @@ hipError_t dispatch_c(const void *X, int64_t M, int64_t K, const Split &sp, void
     }
 }
 
+template <int G, int BITS, bool F32IN>
+hipError_t launch_stream(const void *X, int64_t M, int64_t K, void *q, float *s, int32_t *rs, hipStream_t st) {
+    const int T = (int)(K / 64);
+    int R = 1;
+    while (R * T < 256 && 2 * R * T <= 512) R *= 2;
+    while ((R * T) % 64 && (R + 1) * T <= 512) ++R;
+    const int block = R * T;
+    const int64_t ngroups = (M + R - 1) / R;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int waves_per_block = (block + 63) / 64;
+    const int64_t resident = (int64_t)ncu * std::max(1, 8 / waves_per_block);
+    const int64_t grid = std::min<int64_t>(ngroups, resident);
+    hipLaunchKernelGGL((k_rotquant_stream<G, BITS, F32IN>), dim3((unsigned)grid), dim3(block), 0, st, X, M, (int)K,
+                       T, R, ngroups, q, s, rs);
+    return hipGetLastError();
+}
+
+bool stream_ok(int64_t K) { return K % 256 == 0 && K / 64 <= 512; }
+
 }  // namespace
 
 bool rotquant_supported(int64_t K, int g) {
     Split sp;
-    return choose_split(K, g, sp);
+    return stream_ok(K) || choose_split(K, g, sp);
 }
 
 hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (stream_ok(K)) {
+#define W4_RS(G, B, F) return launch_stream<G, B, F>(X, M, K, q, tok_scale, tok_rowsum, st)
+        if (g == 64) {
+            if (bits == 8) { if (f32in) W4_RS(64, 8, true); else W4_RS(64, 8, false); }
+            else { if (f32in) W4_RS(64, 4, true); else W4_RS(64, 4, false); }
+        } else {
+            if (bits == 8) { if (f32in) W4_RS(256, 8, true); else W4_RS(256, 8, false); }
+            else { if (f32in) W4_RS(256, 4, true); else W4_RS(256, 4, false); }
+        }
+#undef W4_RS
+    }
     Split sp;
     if (!choose_split(K, g, sp)) return hipErrorInvalidValue;
-    if (M == 0) return hipSuccess;
 #define W4_RQ(G, B, F) return dispatch_c<G, B, F>(X, M, K, sp, q, tok_scale, tok_rowsum, st)
     if (g == 64) {
         if (bits == 8) { if (f32in) W4_RQ(64, 8, true); else W4_RQ(64, 8, false); }

@@ -91,6 +91,8 @@ def test_accumulators_extreme_codes():
     (33, 3072, 256, 4, torch.bfloat16), (5, 12288, 256, 8, torch.bfloat16), (9, 12288, 256, 4, torch.bfloat16),
     (3, 4096, 256, 8, torch.bfloat16), (300, 768, 256, 8, torch.bfloat16), (21, 192, 64, 4, torch.float32),
     (40, 1280, 64, 8, torch.bfloat16), (2, 4608, 256, 8, torch.float32), (1, 64, 64, 4, torch.bfloat16),
+    (37, 9472, 256, 8, torch.bfloat16), (3, 32768, 256, 4, torch.bfloat16), (1000, 256, 64, 8, torch.bfloat16),
+    (129, 1024, 256, 4, torch.float32),
 ])
 def test_rotate_quant_act_matches_oracle(M, K, g, bits, dtype):
     say("rotquant M=%d K=%d g=%d bits=%d %s" % (M, K, g, bits, dtype))
@@ -116,10 +118,11 @@ def test_rotate_quant_act_matches_oracle(M, K, g, bits, dtype):
 
 
 def test_rotate_quant_rejects_unsupported_k():
-    # 37 groups of 256: K/16 = 592 chunks has no split C * T with C <= 4, T % 16 == 0, T <= 512
-    X = torch.zeros((2, 37 * 256), dtype=torch.bfloat16, device=DEV)
+    # g = 64, K = 64 * 131: not a multiple of 256 (no streaming kernel), and K/16 = 524 chunks
+    # have no split C * T with C <= 4, T % 4 == 0, T <= 512
+    X = torch.zeros((2, 64 * 131), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(w4.W4Error) as e:
-        w4.w4_rotate_quant_act(X, 256, 8)
+        w4.w4_rotate_quant_act(X, 64, 8)
     assert e.value.status == w4.W4_ERR_UNSUPPORTED
 
 
