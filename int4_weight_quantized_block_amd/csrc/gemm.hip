@@ -15,23 +15,29 @@
 // two halves are interleaved back to natural k order with two v_perm; against int4
 // activation codes both operands keep the even/odd order (only the pairing of k between A
 // and B matters).  The accumulator holds 16 * acc (int8 codes) or 256 * acc (int4 codes),
-// exact in int32 for K <= 65536, and is shifted back in the epilogue.
+// exact in int32 for K <= 65536.  The epilogue converts it to float as is and folds the
+// power-of-two factor into the row scale (exact: float(2^s * a) = 2^s * float(a)).
 //
-// Tiling.  One workgroup of 8 waves (two per SIMD) computes a BM x BN = 256 x 192 output tile;
-// each wave owns 64 tokens x 96 output features = 2 x 3 blocks of v_mfma_i32_32x32x32_i8 (the
-// int8 MFMA shape that runs at the full rate on gfx950).  The weights are the MFMA "A" operand
-// and the tokens the "B" operand, so a lane ends up holding 4 consecutive output features of
-// one token: the epilogue packs them into one 8-byte bf16 store.  K advances 128 per stage
-// through a 3-deep LDS ring filled by direct global->LDS 16-byte loads (no register staging).
-// Each stage is read in two halves; the barrier sits between them, so the fragment reads of
-// the next stage are issued while the MFMAs of the current one run, and each stage's loads
-// are issued three stages ahead.  Within a row the 16-byte chunks are XOR-swizzled so the
-// fragment reads of 16 consecutive rows hit distinct banks.  256 x 192 tiles give exactly one
-// tile per CU for a 4096 x 3072 output.
+// Tiling.  One workgroup of 4 waves (one per SIMD) computes a BM x BN = 256 x 192 output
+// tile; each wave owns 128 tokens x 96 output features = 4 x 3 blocks of
+// v_mfma_i32_32x32x32_i8 (the int8 MFMA shape that runs at the full rate on gfx950), so each
+// unpacked weight operand feeds 4 MFMAs.  The weights are the MFMA "A" operand and the
+// tokens the "B" operand, so a lane ends up holding 4 consecutive output features of one
+// token.  K advances 128 per stage through a 3-deep LDS ring filled by direct global->LDS
+// 16-byte loads (no register staging), issued three stages ahead.  Within a row the 16-byte
+// chunks are XOR-swizzled so the fragment reads of 16 consecutive rows hit distinct banks.
+//
+// Schedule.  With one wave per SIMD every instruction of the wave takes an issue slot, and
+// the matrix core only stays busy if the wave's other work (LDS fragment reads, weight
+// unpacking, the global->LDS loads of a later stage) sits in the shadow of its own MFMAs.
+// Each half stage (64 k, 24 MFMAs) is therefore emitted in a fixed order: MFMA, then a
+// fragment read of the next half, an unpacking unit of the next half, or one global->LDS
+// load, spread over the 24 MFMA slots (sched_barrier pins the order).
 //
 // The block -> tile map keeps each XCD (blocks are dealt to the 8 XCDs round-robin) on a
 // compact group of tiles so the A row panels and B column panels it streams stay in its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -43,47 +49,76 @@ namespace {
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 192, BK = 128;
-constexpr int WAVES_M = 4, WAVES_N = 2;
-constexpr int kThreads = 64 * WAVES_M * WAVES_N;  // 512
-constexpr int WTM = BM / WAVES_M;                 // 64 tokens per wave
+constexpr int WAVES_M = 2, WAVES_N = 2;
+constexpr int kWaves = WAVES_M * WAVES_N;
+constexpr int kThreads = 64 * kWaves;             // 256: one wave per SIMD
+constexpr int WTM = BM / WAVES_M;                 // 128 tokens per wave
 constexpr int WTN = BN / WAVES_N;                 // 96 output features per wave
-constexpr int FM = WTM / 32, FN = WTN / 32;       // 2 x 3 MFMA blocks per wave
+constexpr int FM = WTM / 32, FN = WTN / 32;       // 4 x 3 MFMA blocks per wave
 constexpr int STAGES = 3;
-constexpr int kOutStride = BN * 2 + 16;        // bytes per staged output row (padded)
+constexpr int kOutStride = BN * 2 + 16;           // bytes per staged output row (padded)
 constexpr int kOutBytes = BM * kOutStride;
-constexpr int kEpiBytes = kOutBytes + 3 * BN * 4;  // plus per-feature scale, bias, zero-point term
 
 template <int ABITS>
 struct Lay {
-    static constexpr int A_ROW = ABITS == 8 ? BK : BK / 2;  // activation bytes per row per stage
-    static constexpr int A_CHUNKS = A_ROW / 16;              // 8 or 4
+    static constexpr int A_ROW = ABITS == 8 ? BK : BK / 2;    // activation bytes per row per stage
+    static constexpr int A_CHUNKS = A_ROW / 16;                // 8 or 4
     static constexpr int A_BYTES = BM * A_ROW;
-    static constexpr int A_INSTR = A_BYTES / (1024 * (kThreads / 64));  // per wave: 4 or 2
-    static constexpr int B_ROW = BK / 2;                     // 64 packed weight bytes per row
-    static constexpr int B_BYTES = BN * B_ROW;               // 12 KB = 16 loads of 48 lanes
-    static constexpr int B_INSTR = 2;                        // per wave, 12 rows each
+    static constexpr int A_INSTR = A_BYTES / (1024 * kWaves);  // per wave: 8 or 4
+    static constexpr int B_ROW = BK / 2;                       // 64 packed weight bytes per row
+    static constexpr int B_BYTES = BN * B_ROW;                 // 12 KB
+    static constexpr int B_INSTR = B_BYTES / (1024 * kWaves);  // per wave: 3 (16 rows each)
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LOADS = A_INSTR + B_INSTR;          // per wave and stage
+    static constexpr int LOADS = A_INSTR + B_INSTR;            // per wave and stage
+    static constexpr int XW = ABITS == 8 ? 2 : 1;              // 16-byte activation chunks per half
+    static constexpr int READS = FN + FM * XW;                 // ds_read_b128 per wave and half
+    // the per-feature constants of the tile (raw row scales, bias, zero points) sit past the
+    // ring and past the staged output tile
+    static constexpr int CONST_OFF = ((std::max(STAGES * STAGE, kOutBytes) + 255) / 256) * 256;
+    // (one dword per feature each: f32 scale, f32 or zero-extended bf16 bias, zero-extended
+    // zero point)
+    static constexpr int C_SW = CONST_OFF, C_BIAS = C_SW + BN * 4, C_ZP = C_BIAS + BN * 4;
+    static constexpr int LDS_BYTES = C_ZP + BN * 4;
 };
 
 // physical chunk of logical chunk c in row r (an involution)
 __device__ __forceinline__ int swz_a8(int r, int c) { return c ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int swz_4(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// One 16-byte global -> LDS load per active lane: lane l's bytes land at lds_base + 16 * l
-// (lds_base is wave-uniform and goes through M0).  Issued through inline asm so that the
-// compiler does not add its own conservative vmcnt(0) waits in front of every LDS read of the
-// other stages: the kernel waits for its own loads explicitly (s_waitcnt vmcnt(n) +
-// s_barrier).  The instruction writes no VGPR, so no register is left pending when the asm
-// returns.  M0 is written inside the asm; no other code in these kernels keeps a value in M0.
+// Global -> LDS loads (16 or 4 bytes per lane), addressed as a wave-uniform 64-bit base
+// (SGPRs) plus a per-lane 32-bit byte offset: lane l's bytes land at lds_base + size * l
+// (lds_base is wave-uniform and goes through M0; one wait state separates the M0 write from
+// the load that reads it).  Issued through inline asm so that the compiler does not add its
+// own conservative vmcnt(0) waits in front of every LDS read of the other stages: the kernel
+// waits for its own loads explicitly (s_waitcnt vmcnt(n) + s_barrier).  The instruction
+// writes no VGPR, so no register is left pending when the asm returns.  M0 is written inside
+// the asm; no other code in these kernels keeps a value in M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void gl_lds16(const void *g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
-}
-// Same, addressed as a wave-uniform 64-bit base (SGPRs) plus a per-lane 32-bit byte offset.
 __device__ __forceinline__ void gl_lds16_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void gl_lds4_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+// 2- and 1-byte forms: each lane's value lands zero-extended in its own dword at
+// lds_base + 4 * l.
+__device__ __forceinline__ void gl_lds2_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void gl_lds1_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_base)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -96,6 +131,7 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void unpack_nat(uint32_t d, uint32_t &lo, uint32_t &hi) {
     const uint32_t e = nib_evens16(d), o = nib_odds16(d);
@@ -111,83 +147,125 @@ __device__ __forceinline__ v4i evod(uint32_t d0, uint32_t d1) {
 // that half, used as two MFMA k-steps of 16.
 template <int ABITS>
 struct Frags {
-    uint4 w[FN];                        // packed weights, one 16-byte chunk per n-block
-    uint4 x[FM][ABITS == 8 ? 2 : 1];    // activation codes per m-block
+    uint4 w[FN];                    // packed weights, one 16-byte chunk per n-block
+    uint4 x[FM][Lay<ABITS>::XW];    // activation codes per m-block
 };
 
+// Fragment read number idx of a half: the FN weight chunks first (their unpacking waits only
+// for them), then the activation chunks.
 template <int ABITS>
-__device__ __forceinline__ void read_half(Frags<ABITS> &f, const uint8_t *stage, int t, int wm, int wn, int lr,
-                                          int kb) {
+__device__ __forceinline__ void read_one(Frags<ABITS> &f, const uint8_t *stage, int t, int wm, int wn, int lr,
+                                         int kb, int idx) {
     using L = Lay<ABITS>;
-    const uint8_t *As = stage;
-    const uint8_t *Bs = stage + L::A_BYTES;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = wn * WTN + j * 32 + lr;
-        f.w[j] = *reinterpret_cast<const uint4 *>(Bs + n * L::B_ROW + 16 * swz_4(n, 2 * t + kb));
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    if (idx < FN) {
+        const int n = wn * WTN + idx * 32 + lr;
+        f.w[idx] = *reinterpret_cast<const uint4 *>(stage + L::A_BYTES + n * L::B_ROW + 16 * swz_4(n, 2 * t + kb));
+    } else if constexpr (ABITS == 8) {
+        const int i = (idx - FN) / 2, c = (idx - FN) % 2;
         const int r = wm * WTM + i * 32 + lr;
-        if constexpr (ABITS == 8) {
-            const uint8_t *row = As + r * L::A_ROW;
-            f.x[i][0] = *reinterpret_cast<const uint4 *>(row + 16 * swz_a8(r, 4 * t + 2 * kb));
-            f.x[i][1] = *reinterpret_cast<const uint4 *>(row + 16 * swz_a8(r, 4 * t + 2 * kb + 1));
-        } else {
-            f.x[i][0] = *reinterpret_cast<const uint4 *>(As + r * L::A_ROW + 16 * swz_4(r, 2 * t + kb));
-        }
+        f.x[i][c] = *reinterpret_cast<const uint4 *>(stage + r * L::A_ROW + 16 * swz_a8(r, 4 * t + 2 * kb + c));
+    } else {
+        const int i = idx - FN;
+        const int r = wm * WTM + i * 32 + lr;
+        f.x[i][0] = *reinterpret_cast<const uint4 *>(stage + r * L::A_ROW + 16 * swz_4(r, 2 * t + kb));
     }
 }
 
-// Unpacked weight operands of one half stage: two MFMA k-steps per n-block.
-struct WOps {
-    v4i w0[FN], w1[FN];
+// Unpacked operands of one half stage (two MFMA k-steps): weights per n-block, and for int4
+// activations the unpacked token codes per m-block (int8 codes are used as read).
+struct Ops {
+    v4i w[2][FN];
+    v4i x[2][FM];
 };
 
-template <int ABITS, bool ASYM>
-__device__ __forceinline__ void unpack_w(const Frags<ABITS> &f, WOps &o) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        uint4 x = f.w[j];
-        if constexpr (ASYM) {
-            x.x ^= 0x88888888u; x.y ^= 0x88888888u; x.z ^= 0x88888888u; x.w ^= 0x88888888u;
-        }
-        if constexpr (ABITS == 8) {
-            uint32_t q[8];
-            unpack_nat(x.x, q[0], q[1]);
-            unpack_nat(x.y, q[2], q[3]);
-            unpack_nat(x.z, q[4], q[5]);
-            unpack_nat(x.w, q[6], q[7]);
-            o.w0[j] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
-            o.w1[j] = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
-        } else {
-            o.w0[j] = evod(x.x, x.y);
-            o.w1[j] = evod(x.z, x.w);
-        }
-    }
-}
-
+// Keeps the unpacked operands computed where they are written: without it the compiler sinks
+// the unpacking into the half that consumes it, out of the half whose MFMAs should hide it.
 template <int ABITS>
-__device__ __forceinline__ void mma_half(const Frags<ABITS> &f, const WOps &o, v16i (&acc)[FN][FM]) {
+__device__ __forceinline__ void pin(Ops &o) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        v4i a0, a1;
-        if constexpr (ABITS == 8) {
-            a0 = __builtin_bit_cast(v4i, f.x[i][0]);
-            a1 = __builtin_bit_cast(v4i, f.x[i][1]);
-        } else {
-            a0 = evod(f.x[i][0].x, f.x[i][0].y);
-            a1 = evod(f.x[i][0].z, f.x[i][0].w);
-        }
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(o.w[0][j]), "+v"(o.w[1][j]));
+    if constexpr (ABITS == 4) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.w0[j], a0, acc[j][i], 0, 0, 0);
-            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.w1[j], a1, acc[j][i], 0, 0, 0);
-        }
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(o.x[0][i]), "+v"(o.x[1][i]));
     }
 }
 
+// Unpacking work of one half, cut into units of a few VALU instructions so that it can be
+// spread between MFMAs.  int8 activations: 12 units (one packed weight dword -> 8 codes in k
+// order, 5 instructions).  int4 activations: 6 weight units + 8 activation units (two packed
+// dwords -> 16 codes in even/odd order, 6 instructions each).
+template <int ABITS>
+constexpr int kUnits = ABITS == 8 ? 4 * FN : 2 * FN + 2 * FM;
+
 template <int ABITS, bool ASYM>
+__device__ __forceinline__ void unit(const Frags<ABITS> &f, Ops &o, int u) {
+    if constexpr (ABITS == 8) {
+        const int j = u / 4, d = u % 4;  // dword d of chunk j: codes 8d .. 8d+7 of the lane's 32
+        uint32_t x = d == 0 ? f.w[j].x : d == 1 ? f.w[j].y : d == 2 ? f.w[j].z : f.w[j].w;
+        if constexpr (ASYM) x ^= 0x88888888u;
+        uint32_t lo, hi;
+        unpack_nat(x, lo, hi);
+        o.w[d / 2][j][2 * (d % 2)] = (int)lo;
+        o.w[d / 2][j][2 * (d % 2) + 1] = (int)hi;
+    } else if (u < 2 * FN) {
+        const int j = u / 2, h = u % 2;
+        uint32_t x0 = h ? f.w[j].z : f.w[j].x, x1 = h ? f.w[j].w : f.w[j].y;
+        if constexpr (ASYM) {
+            x0 ^= 0x88888888u;
+            x1 ^= 0x88888888u;
+        }
+        o.w[h][j] = evod(x0, x1);
+    } else {
+        const int i = (u - 2 * FN) / 2, h = (u - 2 * FN) % 2;
+        const uint4 &x = f.x[i][0];
+        o.x[h][i] = h ? evod(x.z, x.w) : evod(x.x, x.y);
+    }
+}
+
+// MFMA number `step` of a half: k-step s = step / 12, then m-block, then n-block (an
+// accumulator is reused only 12 MFMAs later).
+template <int ABITS>
+__device__ __forceinline__ void mma_step(const Frags<ABITS> &f, const Ops &o, v16i (&acc)[FN][FM], int step) {
+    const int s = step / (FM * FN), i = (step % (FM * FN)) / FN, j = step % FN;
+    v4i a;
+    if constexpr (ABITS == 8) a = __builtin_bit_cast(v4i, f.x[i][s]);
+    else a = o.x[s][i];
+    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.w[s][j], a, acc[j][i], 0, 0, 0);
+}
+
+// Slot positions inside a half: fragment reads of the next half at MFMA slots 0.., its
+// unpacking from slot kUnitAt on (after the weight chunks have had time to arrive), the
+// global->LDS loads of a later stage from slot kLoadAt on.
+constexpr int kUnitAt = 5;
+constexpr int kLoadAt = 12;
+
+// One half stage: the 24 MFMAs of the current half (fragments fc, operands oc), with the next
+// half's reads and unpacking (into fn, on) and, with LOAD, the global->LDS loads of stage
+// lkt into ring slot lslot, spread over them in a fixed order.
+template <int ABITS, bool ASYM, bool NEXT, bool LOAD, class LoadFn>
+__device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc, Frags<ABITS> &fn, Ops &on,
+                                           const uint8_t *nstage, int nt, int wm, int wn, int lr, int kb,
+                                           v16i (&acc)[FN][FM], LoadFn &load, int lkt, int lslot) {
+    using L = Lay<ABITS>;
+    constexpr int NM = 2 * FM * FN;
+    static_assert(kUnitAt + kUnits<ABITS> <= NM && kLoadAt + L::LOADS <= NM, "half-stage slots");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int step = 0; step < NM; ++step) {
+        mma_step<ABITS>(fc, oc, acc, step);
+        if constexpr (NEXT) {
+            if (step < L::READS) read_one<ABITS>(fn, nstage, nt, wm, wn, lr, kb, step);
+            if (step >= kUnitAt && step - kUnitAt < kUnits<ABITS>) unit<ABITS, ASYM>(fn, on, step - kUnitAt);
+        }
+        if constexpr (LOAD) {
+            if (step >= kLoadAt && step - kLoadAt < L::LOADS) load(lkt, lslot, step - kLoadAt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) pin<ABITS>(on);
+}
+
+template <int ABITS, bool ASYM, bool KTAIL>
 __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
@@ -214,12 +292,35 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     }
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t K = p.K;
-    const int nk = (int)((K + BK - 1) / BK);
-    const bool ktail = (K % BK) != 0;  // last stage holds only 64 valid k
+    const int nk = (int)((K + BK - 1) / BK);  // the last stage holds 64 valid k when KTAIL
+
+    // ---- the tile's per-feature constants go to LDS with the same direct loads (ahead of the
+    // pipeline's loads, so the first stage's wait covers them); per-lane token constants go to
+    // registers and are first used in the epilogue.
+    if (wave == 0) {
+        const uint32_t cb = lds_addr(smem);
+#pragma unroll
+        for (int q = 0; q < BN / 64; ++q) {
+            const uint32_t c = (uint32_t)(min<int64_t>(n0 + q * 64 + lane, p.N - 1) - n0);  // clamped column
+            gl_lds4_so((uint64_t)(p.sw + n0), 4 * c, cb + L::C_SW + q * 256);
+            if (p.bias) {
+                if (p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, cb + L::C_BIAS + q * 256);
+                else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, cb + L::C_BIAS + q * 256);
+            }
+            if constexpr (ASYM) gl_lds1_so((uint64_t)(p.zp + n0), c, cb + L::C_ZP + q * 256);
+        }
+    }
+    float sxv[FM];
+    int rsv[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = min<int64_t>(m0 + wm * WTM + i * 32 + lr, p.M - 1);
+        sxv[i] = p.sx[m];
+        rsv[i] = ASYM ? p.rowsum[m] : 0;
+    }
 
     // ---- per-lane DMA byte offsets relative to the tile's row panel (rows clamped: rows >= M
     // or >= N are computed on valid data and never stored), and LDS destinations per stage.
-    // The panel base advances by one stage of k per k-tile in scalar registers.
     uint32_t offA[L::A_INSTR];
     int chA[L::A_INSTR];
     const int64_t rowbA = ABITS == 8 ? K : K / 2;
@@ -237,11 +338,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     }
     uint32_t offB[L::B_INSTR];
     int chB[L::B_INSTR];
-    const bool bact = lane < 48;  // B loads use 48 lanes: 12 rows of 64 bytes
 #pragma unroll
     for (int i = 0; i < L::B_INSTR; ++i) {
-        const int j = wave * L::B_INSTR + i;  // 12 rows per wave-instruction
-        const int r = j * 12 + (bact ? lane / 4 : 0);
+        const int j = wave * L::B_INSTR + i;  // 16 rows per wave-instruction
+        const int r = j * 16 + lane / 4;
         const int c = swz_4(r, lane % 4);
         const int64_t rc = min<int64_t>(n0 + r, p.N - 1) - n0;
         chB[i] = c;
@@ -250,22 +350,21 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     const uint8_t *panelA = p.A + m0 * rowbA;
     const uint8_t *panelB = p.B + n0 * (K / 2);
     const uint32_t smem_base = lds_addr(smem);
-    // A stage's loads; in a 64-wide last stage the chunks past K re-read chunk 0 of the same
-    // row and stage (in bounds; that half is never multiplied).
-    auto issue = [&](int kt) {
-        const uint32_t sb = smem_base + (uint32_t)((kt % STAGES) * L::STAGE);
-        const uint8_t *ba = panelA + (int64_t)kt * L::A_ROW;
-        const uint8_t *bb = panelB + (int64_t)kt * L::B_ROW;
-        const bool tail = ktail && kt == nk - 1;
-#pragma unroll
-        for (int i = 0; i < L::A_INSTR; ++i) {
+    // Load number idx of stage kt (into ring slot `slot`); in a 64-wide last stage the chunks
+    // past K re-read chunk 0 of the same row and stage (in bounds; that half is never
+    // multiplied).
+    auto load_one = [&](int kt, int slot, int idx) __attribute__((always_inline)) {
+        const uint32_t sb = smem_base + (uint32_t)(slot * L::STAGE);
+        const bool tail = KTAIL && kt == nk - 1;
+        if (idx < L::A_INSTR) {
+            const int i = idx;
             const uint32_t o = tail && chA[i] >= L::A_CHUNKS / 2 ? offA[i] - 16 * chA[i] : offA[i];
-            gl_lds16_so((uint64_t)ba, o, sb + (uint32_t)(wave * L::A_INSTR + i) * 1024);
-        }
-#pragma unroll
-        for (int i = 0; i < L::B_INSTR; ++i) {
+            gl_lds16_so((uint64_t)(panelA + (int64_t)kt * L::A_ROW), o, sb + (uint32_t)(wave * L::A_INSTR + i) * 1024);
+        } else {
+            const int i = idx - L::A_INSTR;
             const uint32_t o = tail && chB[i] >= 2 ? offB[i] - 16 * chB[i] : offB[i];
-            if (bact) gl_lds16_so((uint64_t)bb, o, sb + (uint32_t)(L::A_BYTES + (wave * L::B_INSTR + i) * 768));
+            gl_lds16_so((uint64_t)(panelB + (int64_t)kt * L::B_ROW), o,
+                        sb + (uint32_t)(L::A_BYTES + (wave * L::B_INSTR + i) * 1024));
         }
     };
 
@@ -275,41 +374,61 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[j][i] = v16i{};
 
-    // ---- prologue: three stages in flight, wait for the first
-    issue(0);
-    if (nk > 1) issue(1);
-    if (nk > 2) issue(2);
+    // ---- prologue: three stages in flight, wait for the first (and the constants)
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+        if (s < nk)
+#pragma unroll
+            for (int q = 0; q < L::LOADS; ++q) load_one(s, s, q);
     if (nk > 2) wait_vmcnt<2 * L::LOADS>();
     else if (nk > 1) wait_vmcnt<L::LOADS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 
-    // Per stage: the second half's reads go out before the first half's MFMAs; the barrier
-    // sits between the halves; the next stage's first-half reads go out before the second
-    // half's MFMAs.  Operands are unpacked right before the MFMAs that use them.
-    Frags<ABITS> f0, f1;
-    WOps o;
-    read_half<ABITS>(f0, smem, 0, wm, wn, lr, kb);
-    for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t *stage = smem + (kt % STAGES) * L::STAGE;
-        const bool second = !(ktail && kt == nk - 1);
-        unpack_w<ABITS, ASYM>(f0, o);
-        if (second) read_half<ABITS>(f1, stage, 1, wm, wn, lr, kb);
-        mma_half<ABITS>(f0, o, acc);
-        // this wave has read all of stage kt; wait for stage kt+1 and for every wave
-        if (kt + 1 < nk) {
-            if (kt + 2 < nk) wait_vmcnt<L::LOADS>();
-            else wait_vmcnt<0>();
-        }
+    // ---- main loop.  Software pipeline over half stages: while the MFMAs of half h run, the
+    // fragments of half h+1 are read from LDS and unpacked.  Between the halves of stage kt:
+    // wait for stage kt+1's loads, barrier (every wave has read all of stage kt), then the
+    // second half issues stage kt+3's loads into stage kt's slot.
+    Frags<ABITS> fa, fb;  // fa: first half of a stage, fb: second half
+    Ops oa, ob;
+#pragma unroll
+    for (int q = 0; q < L::READS; ++q) read_one<ABITS>(fa, smem, 0, wm, wn, lr, kb, q);
+#pragma unroll
+    for (int u = 0; u < kUnits<ABITS>; ++u) unit<ABITS, ASYM>(fa, oa, u);
+    int slot = 0;  // kt % STAGES
+    int kt = 0;
+    // steady state: stage kt+3 exists, its loads ride in the second half
+    for (; kt < nk - 3; ++kt) {
+        const int nslot = slot == STAGES - 1 ? 0 : slot + 1;
+        half_stage<ABITS, ASYM, true, false>(fa, oa, fb, ob, smem + slot * L::STAGE, 1, wm, wn, lr, kb, acc, load_one,
+                                             0, 0);
+        wait_vmcnt<L::LOADS>();
+        wait_lgkmcnt0();  // this wave's reads of stage kt have completed
         __builtin_amdgcn_s_barrier();
-        if (kt + 3 < nk) issue(kt + 3);
-        if (second) {
-            unpack_w<ABITS, ASYM>(f1, o);
-            if (kt + 1 < nk) read_half<ABITS>(f0, smem + ((kt + 1) % STAGES) * L::STAGE, 0, wm, wn, lr, kb);
-            mma_half<ABITS>(f1, o, acc);
-        } else if (kt + 1 < nk) {
-            read_half<ABITS>(f0, smem + ((kt + 1) % STAGES) * L::STAGE, 0, wm, wn, lr, kb);
-        }
+        half_stage<ABITS, ASYM, true, true>(fb, ob, fa, oa, smem + nslot * L::STAGE, 0, wm, wn, lr, kb, acc, load_one,
+                                            kt + 3, slot);
+        slot = nslot;
+    }
+    // the last two stages before the final one: nothing left to load
+    for (; kt < nk - 1; ++kt) {
+        const int nslot = slot == STAGES - 1 ? 0 : slot + 1;
+        half_stage<ABITS, ASYM, true, false>(fa, oa, fb, ob, smem + slot * L::STAGE, 1, wm, wn, lr, kb, acc, load_one,
+                                             0, 0);
+        if (kt + 2 < nk) wait_vmcnt<L::LOADS>();
+        else wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        half_stage<ABITS, ASYM, true, false>(fb, ob, fa, oa, smem + nslot * L::STAGE, 0, wm, wn, lr, kb, acc, load_one,
+                                             0, 0);
+        slot = nslot;
+    }
+    // last stage (64 k only when K % 128 == 64)
+    if constexpr (!KTAIL) {
+        half_stage<ABITS, ASYM, true, false>(fa, oa, fb, ob, smem + slot * L::STAGE, 1, wm, wn, lr, kb, acc, load_one, 0,
+                                             0);
+        half_stage<ABITS, ASYM, false, false>(fb, ob, fa, oa, nullptr, 0, wm, wn, lr, kb, acc, load_one, 0, 0);
+    } else {
+        half_stage<ABITS, ASYM, false, false>(fa, oa, fb, ob, nullptr, 0, wm, wn, lr, kb, acc, load_one, 0, 0);
     }
 
     // ---- epilogue.  32x32 block layout: lane l, register v holds output feature
@@ -319,53 +438,52 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // full, 16-byte-vector rows; the raw int32 accumulator output (a test path) is stored
     // directly.
     constexpr int SHIFT = ABITS == 8 ? 4 : 8;
-    // staged output tile rows, then the tile's per-feature constants
-    float *c_sw = reinterpret_cast<float *>(smem + kOutBytes);
-    float *c_bias = c_sw + BN;
-    int *c_zc = reinterpret_cast<int *>(c_bias + BN);
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
     __syncthreads();  // every wave is past its last LDS read of the pipeline
-    for (int t = tid; t < BN; t += kThreads) {
-        const int64_t n = min<int64_t>(n0 + t, p.N - 1);
-        c_sw[t] = p.sw[n];
-        c_bias[t] = !p.bias ? 0.0f
-                            : p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
-                                          : reinterpret_cast<const float *>(p.bias)[n];
-        c_zc[t] = ASYM ? 8 - (int)p.zp[n] : 0;
-    }
-    __syncthreads();
+    const float *c_sw = reinterpret_cast<const float *>(smem + L::C_SW);
+    const uint8_t *c_bias = smem + L::C_BIAS;
+    const uint8_t *c_zp = smem + L::C_ZP;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int ml = wm * WTM + i * 32 + lr;  // token within the tile
-        const int64_t m = m0 + ml;
-        const bool mok = m < p.M;
-        const int64_t mc = mok ? m : p.M - 1;
-        const float sxm = p.sx[mc];
-        const int rsm = ASYM ? p.rowsum[mc] : 0;
+    for (int j = 0; j < FN; ++j) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int g = 0; g < 4; ++g) {
+            const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
+            const int64_t n = n0 + nl;
+            const float4 sw4 = *reinterpret_cast<const float4 *>(c_sw + nl);
+            const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
+            float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const uint4 b4 = *reinterpret_cast<const uint4 *>(c_bias + 4 * nl);
+                const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
-                const int64_t n = n0 + nl;
-                const float4 sw = *reinterpret_cast<const float4 *>(c_sw + nl);
-                int a[4] = {acc[j][i][4 * g] >> SHIFT, acc[j][i][4 * g + 1] >> SHIFT, acc[j][i][4 * g + 2] >> SHIFT,
-                            acc[j][i][4 * g + 3] >> SHIFT};
-                if constexpr (ASYM) {
-                    const int4 zc = *reinterpret_cast<const int4 *>(c_zc + nl);
-                    a[0] += zc.x * rsm; a[1] += zc.y * rsm; a[2] += zc.z * rsm; a[3] += zc.w * rsm;
-                }
+                for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+            }
+            int zc[4] = {0, 0, 0, 0};  // (8 - z) * 2^SHIFT
+            if constexpr (ASYM) {
+                const uint4 z4 = *reinterpret_cast<const uint4 *>(c_zp + 4 * nl);
+                zc[0] = (8 - (int)z4.x) << SHIFT; zc[1] = (8 - (int)z4.y) << SHIFT;
+                zc[2] = (8 - (int)z4.z) << SHIFT; zc[3] = (8 - (int)z4.w) << SHIFT;
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int ml = wm * WTM + i * 32 + lr;  // token within the tile
+                const int64_t m = m0 + ml;
+                int a[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0);
                 if (p.y_i32) {
-                    if (!mok) continue;
+                    if (m >= p.M) continue;
                     int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < p.N) Y[n + r] = a[r];
+                        if (n + r < p.N) Y[n + r] = a[r] >> SHIFT;
                     continue;
                 }
-                const float4 bs = *reinterpret_cast<const float4 *>(c_bias + nl);
-                float y[4] = {fmaf((float)a[0], sxm * sw.x, bs.x), fmaf((float)a[1], sxm * sw.y, bs.y),
-                              fmaf((float)a[2], sxm * sw.z, bs.z), fmaf((float)a[3], sxm * sw.w, bs.w)};
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxv[i] * sw[r], bs[r]);
                 if (p.lr_t) {
+                    const int64_t mc = min<int64_t>(m, p.M - 1);
                     const float *tr = p.lr_t + mc * p.lr_r;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -406,24 +524,28 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     }
 }
 
-template <int ABITS, bool ASYM>
+template <int ABITS, bool ASYM, bool KTAIL>
 hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
-    // the pipeline ring, reused at the end to stage the bf16 output tile
-    const size_t lds = std::max((size_t)STAGES * Lay<ABITS>::STAGE, (size_t)kEpiBytes);
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM>),
+    constexpr size_t lds = Lay<ABITS>::LDS_BYTES;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn);
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn);
     return hipGetLastError();
+}
+
+template <int ABITS, bool ASYM>
+hipError_t launch_k(const LinearArgs &a, hipStream_t st) {
+    return a.K % BK ? launch_t<ABITS, ASYM, true>(a, st) : launch_t<ABITS, ASYM, false>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const LinearArgs &a, int act_bits, hipStream_t st) {
     if (a.M == 0) return hipSuccess;
-    if (act_bits == 8) return a.zp ? launch_t<8, true>(a, st) : launch_t<8, false>(a, st);
-    return a.zp ? launch_t<4, true>(a, st) : launch_t<4, false>(a, st);
+    if (act_bits == 8) return a.zp ? launch_k<8, true>(a, st) : launch_k<8, false>(a, st);
+    return a.zp ? launch_k<4, true>(a, st) : launch_k<4, false>(a, st);
 }
 
 }  // namespace w4
