@@ -56,8 +56,6 @@ constexpr int WTM = BM / WAVES_M;                 // 128 tokens per wave
 constexpr int WTN = BN / WAVES_N;                 // 96 output features per wave
 constexpr int FM = WTM / 32, FN = WTN / 32;       // 4 x 3 MFMA blocks per wave
 constexpr int STAGES = 3;
-constexpr int kOutStride = BN * 2 + 16;           // bytes per staged output row (padded)
-constexpr int kOutBytes = BM * kOutStride;
 
 template <int ABITS>
 struct Lay {
@@ -73,8 +71,8 @@ struct Lay {
     static constexpr int XW = ABITS == 8 ? 2 : 1;              // 16-byte activation chunks per half
     static constexpr int READS = FN + FM * XW;                 // ds_read_b128 per wave and half
     // the per-feature constants of the tile (raw row scales, bias, zero points) sit past the
-    // ring and past the staged output tile
-    static constexpr int CONST_OFF = ((std::max(STAGES * STAGE, kOutBytes) + 255) / 256) * 256;
+    // ring
+    static constexpr int CONST_OFF = STAGES * STAGE;
     // (one dword per feature each: f32 scale, f32 or zero-extended bf16 bias, zero-extended
     // zero point)
     static constexpr int C_SW = CONST_OFF, C_BIAS = C_SW + BN * 4, C_ZP = C_BIAS + BN * 4;
@@ -233,11 +231,13 @@ __device__ __forceinline__ void mma_step(const Frags<ABITS> &f, const Ops &o, v1
     acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.w[s][j], a, acc[j][i], 0, 0, 0);
 }
 
-// Slot positions inside a half: fragment reads of the next half at MFMA slots 0.., its
-// unpacking from slot kUnitAt on (after the weight chunks have had time to arrive), the
-// global->LDS loads of a later stage from slot kLoadAt on.
-constexpr int kUnitAt = 5;
-constexpr int kLoadAt = 12;
+// Slot positions inside a half: fragment reads of the next half at MFMA slots 0..; in a half
+// without global->LDS loads the unpacking starts at slot 5 (once the weight chunks have had
+// time to arrive); in a half with loads, the loads take slots 0.. and the unpacking the last
+// slots, so that no slot carries much more than an MFMA's worth of other instructions.
+template <int ABITS, bool LOAD>
+constexpr int kUnitAt = LOAD ? 2 * FM * FN - kUnits<ABITS> - 1 : 5;
+constexpr int kLoadAt = 0;
 
 // One half stage: the 24 MFMAs of the current half (fragments fc, operands oc), with the next
 // half's reads and unpacking (into fn, on) and, with LOAD, the global->LDS loads of stage
@@ -248,14 +248,15 @@ __device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc
                                            v16i (&acc)[FN][FM], LoadFn &load, int lkt, int lslot) {
     using L = Lay<ABITS>;
     constexpr int NM = 2 * FM * FN;
-    static_assert(kUnitAt + kUnits<ABITS> <= NM && kLoadAt + L::LOADS <= NM, "half-stage slots");
+    constexpr int UA = kUnitAt<ABITS, LOAD>;
+    static_assert(UA + kUnits<ABITS> <= NM && kLoadAt + L::LOADS <= NM, "half-stage slots");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int step = 0; step < NM; ++step) {
         mma_step<ABITS>(fc, oc, acc, step);
         if constexpr (NEXT) {
             if (step < L::READS) read_one<ABITS>(fn, nstage, nt, wm, wn, lr, kb, step);
-            if (step >= kUnitAt && step - kUnitAt < kUnits<ABITS>) unit<ABITS, ASYM>(fn, on, step - kUnitAt);
+            if (step >= UA && step - UA < kUnits<ABITS>) unit<ABITS, ASYM>(fn, on, step - UA);
         }
         if constexpr (LOAD) {
             if (step >= kLoadAt && step - kLoadAt < L::LOADS) load(lkt, lslot, step - kLoadAt);
@@ -433,58 +434,78 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 
     // ---- epilogue.  32x32 block layout: lane l, register v holds output feature
     // n = 8 * (v / 4) + 4 * (l / 32) + v % 4 of token m = l % 32, so registers 4g .. 4g+3 are
-    // four consecutive features of one token.  bf16 results go through LDS (the pipeline
-    // buffers are free once every wave is past its last MFMA) so that the tile leaves in
-    // full, 16-byte-vector rows; the raw int32 accumulator output (a test path) is stored
-    // directly.
+    // four consecutive features of one token.  Each wave finishes on its own (no workgroup
+    // barrier): per block of 32 tokens it converts its 32 x 96 outputs, stages them as bf16
+    // rows in its own piece of a ring slot that no wave reads any more (the slot of stage
+    // nk-2, or one never filled), and stores full 16-byte row chunks, so the stores of one
+    // block drain while the next one is converted.  The raw int32 accumulator output (a test
+    // path) is stored directly.
     constexpr int SHIFT = ABITS == 8 ? 4 : 8;
     constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
-    __syncthreads();  // every wave is past its last LDS read of the pipeline
     const float *c_sw = reinterpret_cast<const float *>(smem + L::C_SW);
     const uint8_t *c_bias = smem + L::C_BIAS;
     const uint8_t *c_zp = smem + L::C_ZP;
+    // per-feature constants of this lane's 12 groups of 4 features
+    float swv[FN][4][4], bsv[FN][4][4];
+    int zcv[FN][4][4];  // (8 - z) * 2^SHIFT
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
-            const int64_t n = n0 + nl;
             const float4 sw4 = *reinterpret_cast<const float4 *>(c_sw + nl);
-            const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
-            float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.bias) {
-                const uint4 b4 = *reinterpret_cast<const uint4 *>(c_bias + 4 * nl);
-                const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+            swv[j][g][0] = sw4.x * kUnscale; swv[j][g][1] = sw4.y * kUnscale;
+            swv[j][g][2] = sw4.z * kUnscale; swv[j][g][3] = sw4.w * kUnscale;
+            const uint4 b4 = p.bias ? *reinterpret_cast<const uint4 *>(c_bias + 4 * nl) : make_uint4(0, 0, 0, 0);
+            const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
-            }
-            int zc[4] = {0, 0, 0, 0};  // (8 - z) * 2^SHIFT
+            for (int r = 0; r < 4; ++r) bsv[j][g][r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
             if constexpr (ASYM) {
                 const uint4 z4 = *reinterpret_cast<const uint4 *>(c_zp + 4 * nl);
-                zc[0] = (8 - (int)z4.x) << SHIFT; zc[1] = (8 - (int)z4.y) << SHIFT;
-                zc[2] = (8 - (int)z4.z) << SHIFT; zc[3] = (8 - (int)z4.w) << SHIFT;
+                zcv[j][g][0] = (8 - (int)z4.x) << SHIFT; zcv[j][g][1] = (8 - (int)z4.y) << SHIFT;
+                zcv[j][g][2] = (8 - (int)z4.z) << SHIFT; zcv[j][g][3] = (8 - (int)z4.w) << SHIFT;
             }
+        }
+    }
+    if (p.y_i32) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int ml = wm * WTM + i * 32 + lr;  // token within the tile
-                const int64_t m = m0 + ml;
-                int a[4];
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * WTM + i * 32 + lr;
+            if (m >= p.M) continue;
+            int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0);
-                if (p.y_i32) {
-                    if (m >= p.M) continue;
-                    int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * kb;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < p.N) Y[n + r] = a[r] >> SHIFT;
-                    continue;
+                        if (n + r < p.N) Y[n + r] = (acc[j][i][4 * g + r] + (ASYM ? zcv[j][g][r] * rsv[i] : 0)) >> SHIFT;
                 }
+        }
+        return;
+    }
+    constexpr int SROW = WTN * 2 + 16;  // staged row: 96 bf16 + pad
+    uint8_t *stg = smem + ((nk + 1) % STAGES) * L::STAGE + wave * 32 * SROW;
+    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
+    const bool full_n = (p.N & 7) == 0;  // 16-byte aligned rows
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t mrow0 = m0 + wm * WTM + i * 32;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
                 float y[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxv[i] * sw[r], bs[r]);
+                for (int r = 0; r < 4; ++r) {
+                    const int a = acc[j][i][4 * g + r] + (ASYM ? zcv[j][g][r] * rsv[i] : 0);
+                    y[r] = fmaf((float)a, sxv[i] * swv[j][g][r], bsv[j][g][r]);
+                }
                 if (p.lr_t) {
-                    const int64_t mc = min<int64_t>(m, p.M - 1);
+                    const int64_t mc = min<int64_t>(mrow0 + lr, p.M - 1);
                     const float *tr = p.lr_t + mc * p.lr_r;
+                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * kb;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int64_t nc = min<int64_t>(n + r, p.N - 1);
@@ -498,28 +519,26 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
                 const fl2 f01 = {y[0], y[1]}, f23 = {y[2], y[3]};
                 const bf2 h0 = __builtin_convertvector(f01, bf2);
                 const bf2 h1 = __builtin_convertvector(f23, bf2);
-                *reinterpret_cast<uint2 *>(smem + ml * kOutStride + nl * 2) =
+                *reinterpret_cast<uint2 *>(stg + lr * SROW + (j * 32 + 8 * g + 4 * kb) * 2) =
                     make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
             }
         }
-    }
-    if (p.y_i32) return;
-    __syncthreads();
-    // the whole 256 x 192 tile, 24 chunks of 16 bytes per row
-    constexpr int CPR = BN * 2 / 16;
-    const bool full_n = (p.N & 7) == 0;  // 16-byte aligned rows
-    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
-#pragma unroll 4
-    for (int c = tid; c < BM * CPR; c += kThreads) {
-        const int row = c / CPR, ch = c % CPR;
-        const int64_t m = m0 + row, n = n0 + ch * 8;
-        if (m >= p.M || n >= p.N) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(smem + row * kOutStride + ch * 16);
-        if (full_n && n + 7 < p.N) {
-            *reinterpret_cast<uint4 *>(Y + m * p.N + n) = v;
-        } else {
-            const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
-            for (int r = 0; r < 8 && n + r < p.N; ++r) Y[m * p.N + n + r] = h[r];
+        // 32 rows x 12 chunks of 16 bytes; LDS operations of one wave complete in order, so
+        // the reads see this block's writes and the next block's writes follow these reads
+        constexpr int CPR = WTN * 2 / 16;
+#pragma unroll
+        for (int k = 0; k < 32 * CPR / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int row = c / CPR, ch = c % CPR;
+            const int64_t m = mrow0 + row, n = n0 + wn * WTN + ch * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * SROW + ch * 16);
+            if (m >= p.M || n >= p.N) continue;
+            if (full_n && n + 7 < p.N) {
+                *reinterpret_cast<uint4 *>(Y + m * p.N + n) = v;
+            } else {
+                const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
+                for (int r = 0; r < 8 && n + r < p.N; ++r) Y[m * p.N + n + r] = h[r];
+            }
         }
     }
 }

@@ -164,16 +164,20 @@ def test_pack_weights_matches_oracle(N, K, g, asym, dtype):
 
 
 # --------------------------------------------------------------------------- whole layer
-@pytest.mark.parametrize("M,N,K,g,bits,asym,lr", [
-    (16, 256, 256, 64, 8, False, False), (100, 200, 512, 256, 8, False, True), (40, 96, 768, 256, 4, True, True),
-    (130, 64, 256, 64, 4, False, False), (1, 300, 1024, 256, 8, True, False),
+@pytest.mark.parametrize("M,N,K,g,bits,asym,lr,bias_dtype", [
+    (16, 256, 256, 64, 8, False, False, torch.bfloat16), (100, 200, 512, 256, 8, False, True, torch.bfloat16),
+    (40, 96, 768, 256, 4, True, True, torch.bfloat16), (130, 64, 256, 64, 4, False, False, torch.bfloat16),
+    (1, 300, 1024, 256, 8, True, False, torch.bfloat16), (97, 33, 320, 64, 8, True, False, torch.float32),
+    (300, 401, 1024, 256, 4, False, False, torch.bfloat16), (77, 195, 256, 256, 8, False, False, None),
+    (513, 389, 448, 64, 8, True, False, torch.float32),
 ])
-def test_linear_matches_oracle(M, N, K, g, bits, asym, lr):
-    say("linear M=%d N=%d K=%d g=%d bits=%d asym=%s lr=%s" % (M, N, K, g, bits, asym, lr))
+def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
+    say("linear M=%d N=%d K=%d g=%d bits=%d asym=%s lr=%s bias=%s" % (M, N, K, g, bits, asym, lr, bias_dtype))
     r = rng(M + N + K)
     X = act_input(M, K, seed=M * 3 + K)
     W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
-    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32))
+    bias = bias.to(bias_dtype) if bias_dtype is not None else None
     L1 = L2 = None
     if lr:
         L1 = torch.from_numpy((r.standard_normal((K, 16)) * 0.01).astype(np.float32)).to(torch.bfloat16)
@@ -183,7 +187,8 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr):
     Xd = X.to(DEV)
     args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
     low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.to(DEV)) if lr else None
-    y = w4.w4_linear(Xd, g, bits, *args, bias=bias.to(DEV), lowrank=low)
+    bias_d = bias.to(DEV) if bias is not None else None
+    y = w4.w4_linear(Xd, g, bits, *args, bias=bias_d, lowrank=low)
     err = rel_frob(y, ref["y64"])
     say("  rel frob %.3e" % err)
     assert err <= FROB_TOL
@@ -194,5 +199,5 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr):
         tref = oracle.to_f64(X) @ oracle.to_f64(L1)
         assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
         low = w4.LowRank(l2=L2.to(DEV), t=t)
-    y2 = w4.w4_linear_cached_rot(q, s, rs, bits, *args, bias=bias.to(DEV), lowrank=low)
+    y2 = w4.w4_linear_cached_rot(q, s, rs, bits, *args, bias=bias_d, lowrank=low)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
