@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--K", type=int, default=12288, help="small_m: input features (4096 or 12288)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="token rows in the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed loop, run two plain 512 MiB device copies (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU: read two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script with "
+                         "--copy-calibration and record the dominant kernel's HBM bytes in profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -149,8 +154,75 @@ def cpu_baseline(layer, rows_wanted):
                       % (name, rows, M), "seconds": round(sec, 3)}, sec, rows
 
 
+COPY_BYTES = 512 << 20
+# kernel-name prefix -> (short name, source file)
+KERNEL_SOURCE = {"k_gemm<": ("k_gemm", "gemm.hip"), "k_gemv<": ("k_gemv", "gemv.hip"),
+                 "k_rotquant": ("k_rotquant", "rotquant.hip")}
+
+
+def copy_calibration(dev):
+    """Two plain device-to-device copies of COPY_BYTES: the known-size reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("bench: %d MiB calibration copies done" % (COPY_BYTES >> 20))
+
+
+def ingest_counters(fetch_dir, write_dir, workload):
+    """Per-dispatch FETCH_SIZE and WRITE_SIZE of the dominant kernels, each scaled by the bytes
+    per counter unit that the same counter shows for the calibration copy (which reads and
+    writes COPY_BYTES), recorded with the hash of the kernel's source."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return by
+
+    out_path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def copy_units(by):
+        vals = [v for k, vs in by.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs
+                if v * 1024 >= COPY_BYTES / 4]
+        if not vals:
+            raise SystemExit("no calibration copy found in the counter runs")
+        return sorted(vals)[len(vals) // 2]
+
+    f_fetch = COPY_BYTES / copy_units(fetch)
+    f_write = COPY_BYTES / copy_units(write)
+    for prefix, (short, src) in KERNEL_SOURCE.items():
+        fk = [v for k, vs in fetch.items() if prefix in k for v in vs]
+        wk = [v for k, vs in write.items() if prefix in k for v in vs]
+        if not fk or not wk:
+            continue
+        fm, wm = sorted(fk)[len(fk) // 2], sorted(wk)[len(wk) // 2]
+        path = os.path.join(ROOT, "int4_weight_quantized_block_amd", "csrc", src)
+        data["%s:%s" % (short, workload)] = {
+            "bytes": round(fm * f_fetch + wm * f_write), "read_bytes": round(fm * f_fetch),
+            "write_bytes": round(wm * f_write), "fetch_size": fm, "write_size": wm,
+            "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write, "dispatches": len(fk),
+            "source": src, "sha256": hashlib.sha256(open(path, "rb").read()).hexdigest()}
+        log("traffic %s:%s  read %.1f MB  write %.1f MB" % (short, workload, fm * f_fetch / 1e6, wm * f_write / 1e6))
+    with open(out_path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+
+
 def main():
     args = parse()
+    if args.ingest_counters:
+        return ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.workload)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -186,17 +258,24 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
+    # argument tuples built once, so the timed loop costs little host time per launch and the
+    # GPU never waits for the host
+    xdt = w4.W4_BF16 if lin.X.dtype == torch.bfloat16 else w4.W4_F32
+    rq_args = [(x.data_ptr(), xdt, M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr) for x in Xs]
+    mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
+                z.data_ptr() if z is not None else None, lin.bias.data_ptr(), w4.W4_BF16, None, M, N, K,
+                Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
+    f_rq, f_mm = L.w4_rotate_quant_act, L.w4_linear_cached_rot
+
     def rotquant(i):
-        x = Xs[i % ncopy]
-        w4._check(L.w4_rotate_quant_act(x.data_ptr(), w4.W4_BF16 if x.dtype == torch.bfloat16 else w4.W4_F32,
-                                        M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr))
+        rc = f_rq(*rq_args[i % ncopy])
+        if rc:
+            w4._check(rc)
 
     def gemm(i):
-        p, s, z = Ps[i % ncopy]
-        w4._check(L.w4_linear_cached_rot(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(),
-                                         s.data_ptr(), z.data_ptr() if z is not None else None,
-                                         lin.bias.data_ptr(), w4.W4_BF16, None, M, N, K, Y.data_ptr(),
-                                         w4.W4_OUT_BF16, None, 0, sptr))
+        rc = f_mm(*mm_args[i % ncopy])
+        if rc:
+            w4._check(rc)
 
     for i in range(args.warmup):
         rotquant(i)
@@ -220,6 +299,8 @@ def main():
     ms_step = wall / args.steps * 1e3
     log("bench: %.3f ms/step wall; rotate+quant %.2f us, GEMM %.2f us per launch" % (ms_step, t_rq * 1e6,
                                                                                    t_mm * 1e6))
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     small = args.workload == "small_m"
     if small:
