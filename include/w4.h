@@ -128,9 +128,12 @@ int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g,
  *  lr        : NULL or the low-rank branch (host pointer to the struct; its fields are
  *              device pointers)
  *  Y         : out [M, N], bf16 for W4_OUT_BF16, int32 for W4_OUT_I32 (bias and lr unused)
- *  ws        : workspace of at least w4_workspace_bytes(M, N, K, act_bits, r_needed)
- *              where r_needed = lr->r when lr && !lr->t, else 0; may be NULL if that is 0
- * M <= 64 runs a split-K streaming kernel, larger M the MFMA GEMM. */
+ *  ws        : workspace, w4_workspace_bytes(M, N, K, act_bits, r_needed) bytes where
+ *              r_needed = lr->r when lr && !lr->t, else 0.  It holds the low-rank t (first,
+ *              required when r_needed > 0) and, for M <= 64, the int32 partial sums of the
+ *              K-split small-M kernel (optional: with less room, or ws == NULL, the small-M
+ *              path runs without splitting K).  Contents are scratch; nothing persists.
+ * M <= 64 runs the HBM-streaming small-M kernels, larger M the MFMA GEMM. */
 int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *tok_rowsum,
                          int act_bits, const uint8_t *packed, const float *row_scale,
                          const uint8_t *zp, const void *bias, int bias_dtype,
@@ -153,7 +156,9 @@ int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, 
                     void *stream);
 
 /* Workspace sizes in bytes (0 when nothing is needed).
- * w4_workspace_bytes: for w4_linear_cached_rot (the low-rank t when not supplied).
+ * w4_workspace_bytes: for w4_linear_cached_rot (the low-rank t when not supplied, and for
+ * M <= 64 the K-split partial sums, S * M * N int32 with S in {2, 4, 8}, when the kernel
+ * splits K for this shape).
  * w4_linear_workspace_bytes: for w4_linear (activation codes, token scales and row sums,
  * plus the above).  Each piece is 256-byte aligned inside the workspace. */
 size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);

@@ -83,64 +83,6 @@ struct Lay {
 __device__ __forceinline__ int swz_a8(int r, int c) { return c ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int swz_4(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// Global -> LDS loads (16 or 4 bytes per lane), addressed as a wave-uniform 64-bit base
-// (SGPRs) plus a per-lane 32-bit byte offset: lane l's bytes land at lds_base + size * l
-// (lds_base is wave-uniform and goes through M0; one wait state separates the M0 write from
-// the load that reads it).  Issued through inline asm so that the compiler does not add its
-// own conservative vmcnt(0) waits in front of every LDS read of the other stages: the kernel
-// waits for its own loads explicitly (s_waitcnt vmcnt(n) + s_barrier).  The instruction
-// writes no VGPR, so no register is left pending when the asm returns.  M0 is written inside
-// the asm; no other code in these kernels keeps a value in M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void gl_lds16_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_base)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void gl_lds4_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_base)
-                 : "memory", "m0");
-}
-// 2- and 1-byte forms: each lane's value lands zero-extended in its own dword at
-// lds_base + 4 * l.
-__device__ __forceinline__ void gl_lds2_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_base)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void gl_lds1_so(uint64_t sbase, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);  // keep it in an SGPR
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_base)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-__device__ __forceinline__ void unpack_nat(uint32_t d, uint32_t &lo, uint32_t &hi) {
-    const uint32_t e = nib_evens16(d), o = nib_odds16(d);
-    lo = __builtin_amdgcn_perm(o, e, 0x05010400u);  // codes k, k+1, k+2, k+3
-    hi = __builtin_amdgcn_perm(o, e, 0x07030602u);  // codes k+4 .. k+7
-}
-
-__device__ __forceinline__ v4i evod(uint32_t d0, uint32_t d1) {
-    return v4i{(int)nib_evens16(d0), (int)nib_odds16(d0), (int)nib_evens16(d1), (int)nib_odds16(d1)};
-}
-
 // Fragments of one half stage (64 k): per lane the 32 k values [32 * kb, 32 * kb + 32) of
 // that half, used as two MFMA k-steps of 16.
 template <int ABITS>

@@ -1,21 +1,27 @@
 // Small-M (M <= 64) integer GEMM + dequant epilogue for gfx950: the HBM-bound regime.
 //
 // ComfyUI-INT-Crush README, "Inference / INT4" (INT8 GEMM with fused dequant on unpacked
-// INT4 weights) and "Inference" (the backend is chosen by batch size: a small-M streaming
-// kernel vs the large-M dense GEMM, as in its OrbitQuant notes); stable-diffusion.cpp PR
-// #2010, "Summary": the packed nibbles are read as stored.
+// INT4 weights) and "Inference / OrbitQuant" (the kernel is chosen by batch size: a
+// small-M kernel next to the large-M dense GEMM); stable-diffusion.cpp PR #2010, "Summary":
+// the packed nibbles are read as stored.
 //
-// At M <= 64 the layer reads ~0.5 byte of weight per 2*M ops, far below the MFMA ridge, so
-// the kernel is organised around streaming each packed weight byte from HBM exactly once,
-// with as many bytes in flight as possible:
-//  - a workgroup owns 16 weight rows and 4 waves; wave s owns the contiguous quarter
-//    [s*K/4, (s+1)*K/4) of K, and every lane issues all of its weight loads (16 bytes each)
-//    before the first multiply, so the HBM latency is paid once per workgroup;
-//  - the weights are the MFMA "A" operand (16 rows x 64 k per v_mfma_i32_16x16x64_i8), the
-//    tokens the "B" operand (one MFMA per 16 tokens); token fragments come from L2 with a
-//    software prefetch several k-steps ahead;
-//  - the 4 partial 16 x 16 int32 tiles are summed through LDS in a fixed order (exact and
-//    deterministic, no atomics); wave 0 runs the epilogue (the large-M kernel's arithmetic).
+// At M <= 64 the layer reads ~0.5 byte of weight per 2 * M integer ops, far below the MFMA
+// ridge, so the kernel is organised around streaming the packed weights from HBM once, with
+// many bytes in flight and in long contiguous runs:
+//  - a workgroup (4 waves) owns R = 16 * RB consecutive weight rows; their bytes for one
+//    stage of 512 k (R rows x 256 bytes) and the token codes of that stage (16 * MB tokens x
+//    512 or 256 bytes, from L2) go straight from global memory into an LDS ring with 16-byte
+//    global->LDS loads (every wave-instruction reads 1 KB of consecutive bytes), issued up to
+//    STAGES - 1 stages ahead without holding any register;
+//  - within a stage, wave w takes k in [128 w, 128 w + 128): per 16 weight rows and 16
+//    tokens, two v_mfma_i32_16x16x64_i8 (weights the "A" operand, tokens the "B" operand);
+//  - the 4 per-wave partial tiles are summed through LDS in a fixed order (exact and
+//    deterministic), then the epilogue (the large-M kernel's arithmetic) stores 4 consecutive
+//    features of a token per lane.
+// Unpacking follows the large-M kernel: nibble -> 16 * code bytes, natural k order against
+// int8 token codes, even/odd order on both sides against int4 token codes.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,204 +30,973 @@ namespace w4 {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kMaxChunks = 32;  // 16-byte weight chunks per lane held in registers at once
+constexpr int kThreads = 64 * kWaves;
+constexpr int KC = 512;             // k per stage
+constexpr int KW = KC / kWaves;     // 128 k per wave and stage: one pair of MFMA k-steps
+constexpr int kLdsBudget = 144 * 1024;
 
-__device__ __forceinline__ v4i evod(uint32_t d0, uint32_t d1) {
-    return v4i{(int)nib_evens16(d0), (int)nib_odds16(d0), (int)nib_evens16(d1), (int)nib_odds16(d1)};
+template <int ABITS, int MB, int RB>
+struct GL {
+    static constexpr int R = 16 * RB;                          // weight rows per workgroup
+    static constexpr int T = 16 * MB;                          // token rows staged
+    static constexpr int A_ROW = ABITS == 8 ? KC : KC / 2;     // token bytes per stage: 512 / 256
+    static constexpr int A_CHUNKS = A_ROW / 16;                // 32 / 16
+    static constexpr int A_BYTES = T * A_ROW;
+    static constexpr int B_ROW = KC / 2;                       // 256 packed weight bytes per row
+    static constexpr int B_BYTES = R * B_ROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int STAGES = kLdsBudget / STAGE < 12 ? kLdsBudget / STAGE : 12;
+    static constexpr int DEPTH = STAGES - 1;                   // stages in flight ahead
+    static constexpr int A_INSTR = A_BYTES / 1024;             // 1 KB wave-instructions per stage
+    static constexpr int B_INSTR = B_BYTES / 1024;
+    static constexpr int LW = (A_INSTR + B_INSTR) / kWaves;    // per wave and stage
+    static constexpr int RED = kWaves * RB * MB * 1024;        // reduction buffer
+    static constexpr int RING = STAGES * STAGE > RED ? STAGES * STAGE : RED;
+    static constexpr int C_SW = RING, C_BIAS = C_SW + 256, C_ZP = C_BIAS + 256, C_SX = C_ZP + 256,
+                         C_RS = C_SX + 256;
+    static constexpr int LDS = C_RS + 256;
+    static_assert((A_INSTR + B_INSTR) % kWaves == 0, "whole loads per wave");
+    static_assert(STAGES >= 2 && DEPTH * LW <= 63, "vmcnt range");
+};
+
+// LDS chunk swizzle (an involution inside a row): the 16 rows / tokens read by one MFMA
+// operand land on distinct banks.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 15); }
+
+// Wait until at most s stages of this wave's loads are still in flight (s <= S).
+template <int LW, int S>
+__device__ __forceinline__ void wait_stages(int s) {
+    if constexpr (S == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (s >= S) wait_vmcnt<S * LW>();
+        else wait_stages<LW, S - 1>(s);
+    }
 }
 
-// Loads are unconditional, from clamped (always valid) addresses, and the value is masked
-// afterwards: a guarded load would become a branch with its own wait, serialising the loads.
-__device__ __forceinline__ uint4 mask4(uint4 v, bool ok) {
-    return ok ? v : make_uint4(0, 0, 0, 0);
-}
-
-// Token fragment of one MFMA k-step (64 k; this lane: tokens mb*16 + lr, k in [k16, k16+16)).
-template <int ABITS>
-__device__ __forceinline__ uint4 load_act(const LinearArgs &p, int64_t m, int64_t k16) {
-    const bool ok = m < p.M && k16 < p.K;
-    const int64_t mc = ok ? m : 0, kc = ok ? k16 : 0;
-    if constexpr (ABITS == 8) return mask4(*reinterpret_cast<const uint4 *>(p.A + mc * p.K + kc), ok);
-    const uint2 x = *reinterpret_cast<const uint2 *>(p.A + mc * (p.K / 2) + kc / 2);
-    return mask4(make_uint4(x.x, x.y, 0, 0), ok);
-}
-
-template <int ABITS>
-__device__ __forceinline__ v4i act_operand(const uint4 &x) {
-    if constexpr (ABITS == 8)
-        return v4i{(int)bytes_evens(x.x, x.y), (int)bytes_odds(x.x, x.y), (int)bytes_evens(x.z, x.w),
-                   (int)bytes_odds(x.z, x.w)};
-    return evod(x.x, x.y);
-}
-
-// NCH = 16-byte weight chunks per lane (each covers 32 k = two MFMA k-steps).
-template <int ABITS, int MB, int NCH, bool ASYM>
-__global__ void __launch_bounds__(64 * kWaves) k_gemv(LinearArgs p) {
-    __shared__ v4i red[kWaves][MB][64];
+template <int ABITS, int MB, int RB, bool ASYM>
+__global__ void __launch_bounds__(kThreads) k_gemv_ring(LinearArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using L = GL<ABITS, MB, RB>;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, s = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kb = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t nrow = n0 + lr;
-    const bool nok = nrow < p.N;
+    const int64_t n0 = (int64_t)blockIdx.x * L::R;
     const int64_t K = p.K;
-    // this wave's K range, in units of 128 k (one chunk for each of the 4 lane groups kb)
-    const int64_t kq = ((K + 127) / 128 + kWaves - 1) / kWaves;  // 128-k steps per wave
-    const int64_t kbeg = (int64_t)s * kq * 128;
-    const uint8_t *wrow = p.B + (nok ? nrow : 0) * (K / 2);
+    const int nk = (int)((K + KC - 1) / KC);
+    const int64_t rowA = ABITS == 8 ? K : K / 2;  // bytes per token row of the codes
+    const int64_t rowB = K / 2;
 
-    v4i acc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
-
-    // The wave's range is processed in segments of NCH chunks (one segment up to K = 16384).
-    for (int64_t seg = 0; seg < kq; seg += NCH) {
-        const int64_t nseg = min<int64_t>(NCH, kq - seg);
-        const int64_t kseg = kbeg + 128 * seg;
-        // ---- all weight chunks of this segment, issued at once.  Chunk c covers
-        //      k in [kseg + 128 c + 32 kb, +32): 16 bytes of the packed row.
-        uint4 wv[NCH];
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int64_t k = kseg + 128 * c + 32 * kb;
-            const bool ok = c < nseg && k < K;
-            wv[c] = mask4(*reinterpret_cast<const uint4 *>(wrow + (ok ? k / 2 : 0)), ok && nok);
+    // ---- per-row constants (scale, bias, zero point) and per-token constants (scale,
+    // rowsum) go to LDS past the ring with 4/2/1-byte direct loads issued ahead of the ring's
+    // loads (so every wait of the pipeline also covers them); one dword per entry.
+    constexpr int SHIFT = ABITS == 8 ? 4 : 8;
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    const uint32_t smem_base = lds_addr(smem);
+    if (wave == 0) {
+        const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(lane, L::R - 1), p.N - 1) - n0);
+        const uint32_t t = (uint32_t)min<int64_t>(lane, p.M - 1);
+        gl_lds4_so((uint64_t)(p.sw + n0), 4 * c, smem_base + L::C_SW);
+        if (p.bias) {
+            if (p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + L::C_BIAS);
+            else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + L::C_BIAS);
         }
-        // ---- k-steps: step t = 2 c + h uses k in [kseg + 128 c + 32 kb + 16 h, +16) per lane
-        // token-fragment prefetch distance in k-steps: deep enough that the L2 round trips of the
-        // fragments overlap (fewer registers per step as the token blocks grow)
-        constexpr int PF = MB == 1 ? 16 : MB == 2 ? 8 : MB == 3 ? 5 : 4;
-        uint4 ab[PF][MB];
-        auto kstep = [&](int t) -> int64_t { return t < 2 * nseg ? kseg + 128 * (t >> 1) + 32 * kb + 16 * (t & 1) : K; };
+        if constexpr (ASYM) {
+            gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + L::C_ZP);
+            gl_lds4_so((uint64_t)p.rowsum, 4 * t, smem_base + L::C_RS);
+        }
+        gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + L::C_SX);
+    }
+
+    // ---- global->LDS loads.  Load j of a stage (j = wave + 4 i) is 1 KB: token codes for
+    // j < A_INSTR (1024 / A_ROW tokens), else 4 weight rows.  Lane l writes LDS bytes
+    // [16 l, 16 l + 16) of the load and reads the matching global chunk of the swizzled row.
+    // Rows past M / N are clamped to the last valid one (their outputs are never stored), and
+    // chunks past K to the last valid chunk of the row (those k are masked to zero codes).
+    auto load = [&](int kt, int slot, int i) __attribute__((always_inline)) {
+        const int j = wave + kWaves * i;
+        const uint32_t dst = smem_base + (uint32_t)(slot * L::STAGE + j * 1024);
+        if (j < L::A_INSTR) {
+            constexpr int TPI = 1024 / L::A_ROW;
+            const int t = j * TPI + lane / L::A_CHUNKS;
+            const int c = swz(t, lane % L::A_CHUNKS);
+            const int64_t tc = min<int64_t>(t, p.M - 1);
+            const int64_t off = min<int64_t>((int64_t)kt * L::A_ROW + 16 * c, rowA - 16);
+            gl_lds16_so((uint64_t)p.A, (uint32_t)(tc * rowA + off), dst);
+        } else {
+            const int r = (j - L::A_INSTR) * 4 + lane / 16;
+            const int c = swz(r, lane % 16);
+            const int64_t rc = min<int64_t>(n0 + r, p.N - 1) - n0;
+            const int64_t off = min<int64_t>((int64_t)kt * L::B_ROW + 16 * c, rowB - 16);
+            gl_lds16_so((uint64_t)(p.B + n0 * rowB), (uint32_t)(rc * rowB + off), dst);
+        }
+    };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < PF; ++t)
+        for (int i = 0; i < L::LW; ++i) load(kt, kt % L::STAGES, i);
+    };
+
+    v4i acc[RB][MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) ab[t][mb] = load_act<ABITS>(p, mb * 16 + lr, kstep(t));
-        // keep every load above issued here, before the first multiply (the compiler would
-        // otherwise sink each one to its use and serialise the HBM round trips)
-        asm volatile("" ::: "memory");
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int t = 0; t < 2 * NCH; ++t) {
-            if (t >= 2 * nseg) break;
-            const int c = t >> 1, h = t & 1;
-            uint32_t d0 = h ? wv[c].z : wv[c].x, d1 = h ? wv[c].w : wv[c].y;
-            if constexpr (ASYM) {
-                d0 ^= 0x88888888u;
-                d1 ^= 0x88888888u;
+        for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = v4i{0, 0, 0, 0};
+
+    for (int s = 0; s < L::DEPTH; ++s)
+        if (s < nk) issue(s);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed for every wave; every wave is done with stage kt - 1, whose
+        // slot takes stage kt + DEPTH
+        wait_stages<L::LW, L::DEPTH - 1>(min(L::DEPTH - 1, nk - 1 - kt));
+        __builtin_amdgcn_s_barrier();
+        if (kt + L::DEPTH < nk) issue(kt + L::DEPTH);
+        const uint8_t *st = smem + (kt % L::STAGES) * L::STAGE;
+        // this lane's 32 k: [kt * 512 + 128 * wave + 32 * kb, + 32)
+        const bool kvalid = (int64_t)kt * KC + KW * wave + 32 * kb < K;
+        v4i a0[MB], a1[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int t = 16 * mb + lr;
+            const uint8_t *row = st + t * L::A_ROW;
+            if constexpr (ABITS == 8) {
+                const int c = 8 * wave + 2 * kb;
+                uint4 x0 = *reinterpret_cast<const uint4 *>(row + 16 * swz(t, c));
+                uint4 x1 = *reinterpret_cast<const uint4 *>(row + 16 * swz(t, c + 1));
+                if (!kvalid) x0 = x1 = make_uint4(0, 0, 0, 0);
+                a0[mb] = __builtin_bit_cast(v4i, x0);
+                a1[mb] = __builtin_bit_cast(v4i, x1);
+            } else {
+                uint4 x = *reinterpret_cast<const uint4 *>(row + 16 * swz(t, 4 * wave + kb));
+                if (!kvalid) x = make_uint4(0, 0, 0, 0);
+                a0[mb] = evod(x.x, x.y);
+                a1[mb] = evod(x.z, x.w);
             }
-            const v4i wf = evod(d0, d1);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = 16 * rb + lr;
+            uint4 w = *reinterpret_cast<const uint4 *>(st + L::A_BYTES + r * L::B_ROW + 16 * swz(r, 4 * wave + kb));
+            if constexpr (ASYM) {
+                w.x ^= 0x88888888u; w.y ^= 0x88888888u; w.z ^= 0x88888888u; w.w ^= 0x88888888u;
+            }
+            v4i w0, w1;
+            if constexpr (ABITS == 8) {
+                uint32_t q[8];
+                unpack_nat(w.x, q[0], q[1]);
+                unpack_nat(w.y, q[2], q[3]);
+                unpack_nat(w.z, q[4], q[5]);
+                unpack_nat(w.w, q[6], q[7]);
+                w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+            } else {
+                w0 = evod(w.x, w.y);
+                w1 = evod(w.z, w.w);
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-                const v4i af = act_operand<ABITS>(ab[t % PF][mb]);
-                acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf, af, acc[mb], 0, 0, 0);
+                acc[rb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0[mb], acc[rb][mb], 0, 0, 0);
+                acc[rb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1[mb], acc[rb][mb], 0, 0, 0);
             }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) ab[t % PF][mb] = load_act<ABITS>(p, mb * 16 + lr, kstep(t + PF));
         }
     }
 
+    // ---- reduce the 4 waves' partial tiles (fixed order), then the epilogue: wave w takes
+    // the (row block, token block) pairs p with p % 4 == w.  16x16 layout: lane l, register r
+    // holds weight row 4 (l / 16) + r of token l % 16.
+    __syncthreads();  // every wave is past its last read of the ring
+    v4i *red = reinterpret_cast<v4i *>(smem);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) red[s][mb][lane] = acc[mb];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[((wave * RB + rb) * MB + mb) * 64 + lane] = acc[rb][mb];
     __syncthreads();
-    if (s != 0) return;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        v4i t = red[0][mb][lane];
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q) t += red[q][mb][lane];
-        acc[mb] = t;
+        for (int mb = 0; mb < MB; ++mb) {
+            if ((rb * MB + mb) % kWaves != wave) continue;
+            v4i t = red[((0 * RB + rb) * MB + mb) * 64 + lane];
+#pragma unroll
+            for (int q = 1; q < kWaves; ++q) t += red[((q * RB + rb) * MB + mb) * 64 + lane];
+            const int64_t m = 16 * mb + lr;
+            if (m >= p.M) continue;
+            const int64_t nb = n0 + 16 * rb + 4 * kb;
+            const int rl = 16 * rb + 4 * kb;  // row within the workgroup
+            const float4 sw4 = *reinterpret_cast<const float4 *>(smem + L::C_SW + 4 * rl);
+            const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
+            const float sxm = *reinterpret_cast<const float *>(smem + L::C_SX + 4 * lr + 64 * mb);
+            int a[4];
+            if constexpr (ASYM) {
+                const uint4 z4 = *reinterpret_cast<const uint4 *>(smem + L::C_ZP + 4 * rl);
+                const int rsm = *reinterpret_cast<const int *>(smem + L::C_RS + 4 * lr + 64 * mb);
+                const uint32_t z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] = t[r] + ((8 - (int)z[r]) << SHIFT) * rsm;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] = t[r];
+            }
+            float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + L::C_BIAS + 4 * rl);
+                const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+            }
+            if (p.y_i32) {
+                int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < p.N) Y[nb + r] = a[r] >> SHIFT;
+                continue;
+            }
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
+            if (p.lr_t) {
+                const float *tr = p.lr_t + m * p.lr_r;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t nc = min<int64_t>(nb + r, p.N - 1);
+                    float l = 0.0f;
+                    for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
+                    y[r] += l;
+                }
+            }
+            uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+            const uint32_t b0 = f32_to_bf16(y[0]), b1 = f32_to_bf16(y[1]), b2 = f32_to_bf16(y[2]),
+                           b3 = f32_to_bf16(y[3]);
+            if (nb + 3 < p.N && (p.N & 3) == 0) {
+                *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            } else {
+                const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < p.N) Y[nb + r] = (uint16_t)bb[r];
+            }
+        }
+    }
+}
+
+template <int ABITS, int MB, int RB>
+hipError_t launch_ring_t(const LinearArgs &a, hipStream_t st) {
+    using L = GL<ABITS, MB, RB>;
+    const unsigned grid = (unsigned)((a.N + L::R - 1) / L::R);
+    if (a.zp) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_gemv_ring<ABITS, MB, RB, true>), hipFuncAttributeMaxDynamicSharedMemorySize,
+            L::LDS);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((k_gemv_ring<ABITS, MB, RB, true>), dim3(grid), dim3(kThreads), L::LDS, st, a);
+    } else {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_gemv_ring<ABITS, MB, RB, false>), hipFuncAttributeMaxDynamicSharedMemorySize,
+            L::LDS);
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((k_gemv_ring<ABITS, MB, RB, false>), dim3(grid), dim3(kThreads), L::LDS, st, a);
+    }
+    return hipGetLastError();
+}
+
+// Rows per workgroup: enough 16-row blocks that about 256 workgroups (one per CU) cover N.
+template <int ABITS, int MB>
+hipError_t dispatch_rb(const LinearArgs &a, hipStream_t st) {
+    const int64_t rb = (a.N + 16 * 256 - 1) / (16 * 256);
+    if (rb <= 1) return launch_ring_t<ABITS, MB, 1>(a, st);
+    if (rb <= 2) return launch_ring_t<ABITS, MB, 2>(a, st);
+    if (rb <= 3) return launch_ring_t<ABITS, MB, 3>(a, st);
+    return launch_ring_t<ABITS, MB, 4>(a, st);
+}
+
+template <int ABITS>
+hipError_t dispatch_mb(const LinearArgs &a, hipStream_t st) {
+    switch ((a.M + 15) / 16) {
+        case 1: return dispatch_rb<ABITS, 1>(a, st);
+        case 2: return dispatch_rb<ABITS, 2>(a, st);
+        case 3: return dispatch_rb<ABITS, 3>(a, st);
+        default: return dispatch_rb<ABITS, 4>(a, st);
+    }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Split path (used when the caller's workspace holds the partial sums): a workgroup owns R
+// rows and one of S equal K ranges.  All of its bytes are requested at once, token codes
+// first (at most 48 KB, from L2), then the weights stage by stage (about 96 KB, in 1 KB runs)
+// into LDS; the waves compute each 512-k stage as soon as it has landed (the loads complete
+// in issue order), so the whole HBM stream is in flight from the start.  With S > 1 each
+// workgroup writes its int32 partial tile and k_gemv_reduce sums the S partials in a fixed
+// order and runs the epilogue; with S = 1 the workgroup runs the epilogue itself.
+constexpr int kSplitActMax = 48 * 1024;
+constexpr int kSplitWeightMax = 96 * 1024;
+constexpr int KCS = 2048;           // k per stage of the split kernel: 1 KB of each weight row
+
+struct SplitPlan {
+    int S, KS, RB, MB, nst;
+    int64_t act_bytes;  // LDS bytes of one wave's token codes
+    int cbase;  // LDS offset of the per-row / per-token constants (past everything else)
+    int lds;
+    unsigned grid;
+};
+
+// Choose S (K ranges) and RB (16-row blocks per workgroup) so that about 256 workgroups
+// cover the layer, the token codes of a K range fit kSplitActMax and the weights of a
+// workgroup fit kSplitWeightMax.  Returns S = 0 when no split fits (the ring kernel runs).
+SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int act_bits) {
+    if (M < 1 || M > 64) return SplitPlan{};
+    for (int S = 1; S <= 8; S *= 2) {
+        if (K % (64 * S)) continue;
+        const int64_t KS = K / S;
+        SplitPlan pl{};
+        pl.nst = (int)((KS + KCS - 1) / KCS);
+        // per wave: nst stages x M tokens x 512 (int8) or 256 (int4) bytes, whole 1 KB loads
+        const int64_t actw = ((int64_t)pl.nst * M * (act_bits == 8 ? 512 : 256) + 1023) / 1024 * 1024;
+        if (kWaves * actw > kSplitActMax) continue;
+        int64_t rb = (N * S + 4095) / 4096;
+        const int64_t rbmax = kSplitWeightMax / (16 * (int64_t)pl.nst * (KCS / 2));
+        rb = std::min<int64_t>(std::min<int64_t>(rb, rbmax), 8);
+        if (rb < 1) continue;
+        pl.S = S;
+        pl.KS = (int)KS;
+        pl.RB = (int)rb;
+        pl.MB = (int)((M + 15) / 16);
+        pl.act_bytes = actw;  // per wave
+        const int64_t wbytes = (int64_t)pl.nst * 16 * rb * (KCS / 2);
+        const int64_t red = (int64_t)kWaves * rb * pl.MB * 1024;
+        pl.cbase = (int)std::max<int64_t>(kWaves * actw + wbytes, red);
+        pl.lds = pl.cbase + 3 * 4 * (int)((16 * rb + 63) / 64 * 64) + 512;
+        if (pl.lds > 160 * 1024) continue;
+        // loads a wave keeps in flight (weights, token codes, constants) within vmcnt's range
+        if (4 * rb * pl.nst + actw / 1024 + 7 > 63) continue;
+        pl.grid = (unsigned)(((N + 16 * rb - 1) / (16 * rb)) * S);
+        return pl;
+    }
+    return SplitPlan{};
+}
+
+// Wait until at most r * PER of this wave's loads are in flight (0 <= r <= RMAX).
+template <int PER, int RMAX>
+__device__ __forceinline__ void wait_rem(int r) {
+    if constexpr (RMAX == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (r >= RMAX) wait_vmcnt<(RMAX * PER < 63 ? RMAX * PER : 63)>();
+        else wait_rem<PER, RMAX - 1>(r);
+    }
+}
+
+// Per-wave layout: within each 2048-k stage wave w takes k in [512 w, 512 w + 512) and loads
+// exactly the bytes it multiplies (its token-code slices and its 256-byte piece of every
+// weight row) into its own LDS region, so the waves never wait for each other until the
+// final reduction.  Token codes: [stage][token][512 or 256 bytes]; weights: [stage][row][256
+// bytes]; 16-byte chunks swizzled by row / token inside groups of 16.
+template <int ABITS, int MB, int RB>
+__global__ void __launch_bounds__(kThreads) k_gemv_split(LinearArgs p, int S, int KS, int nst, int actw,
+                                                         int cbase, int32_t *part, int asym) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    constexpr int R = 16 * RB;
+    constexpr int SHIFT = ABITS == 8 ? 4 : 8;
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    constexpr int SLB = ABITS == 8 ? 512 : 256;  // token-code bytes per wave, stage and token
+    constexpr int SLC = SLB / 16;
+    constexpr int NACC = RB * MB <= 4 ? 2 : 1;   // independent accumulator chains
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int blk = blockIdx.x / S, sp = blockIdx.x % S;
+    const int64_t n0 = (int64_t)blk * R, k0 = (int64_t)sp * KS;
+    const int64_t K = p.K, M = p.M;
+    const int Mi = (int)M;
+    const int64_t rowA = ABITS == 8 ? K : K / 2;
+    const int64_t rowB = K / 2;
+    const int abase = wave * actw;                              // this wave's token codes
+    const int wbase = kWaves * actw + wave * nst * R * 256;     // this wave's weights
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t xr = asym ? 0x88888888u : 0u;
+
+    // ---- requests: constants (wave 0), this wave's token codes, its weights stage by stage.
+    // Constants: row scales, biases, zero points (one dword per row, RP rows each), token
+    // scales and rowsums (one dword per token).
+    constexpr int RP = (R + 63) / 64 * 64;
+    const int c_sw = cbase, c_bias = c_sw + 4 * RP, c_zp = c_bias + 4 * RP, c_sx = c_zp + 4 * RP, c_rs = c_sx + 256;
+    if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < RP / 64; ++h) {
+            const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(64 * h + lane, R - 1), p.N - 1) - n0);
+            gl_lds4_so((uint64_t)(p.sw + n0), 4 * c, smem_base + c_sw + 256 * h);
+            if (p.bias) {
+                if (p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + c_bias + 256 * h);
+                else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + c_bias + 256 * h);
+            }
+            if (asym) gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + c_zp + 256 * h);
+        }
+        const uint32_t t = (uint32_t)min<int64_t>(lane, M - 1);
+        if (asym) gl_lds4_so((uint64_t)p.rowsum, 4 * t, smem_base + c_rs);
+        gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + c_sx);
+    }
+    {
+        const int total = nst * Mi * SLC;  // 16-byte chunks of this wave's token codes
+        const int ninstr = (total + 63) / 64;
+        for (int j = 0; j < ninstr; ++j) {
+            const int f = min(j * 64 + lane, total - 1);
+            const int c = f % SLC, it = f / SLC;
+            const int t = it % Mi, i = it / Mi;
+            const int64_t kbyte = (k0 + (int64_t)i * KCS + 512 * wave) * ABITS / 8 + 16 * (c ^ (t & 15));
+            gl_lds16_so((uint64_t)p.A, (uint32_t)(t * rowA + min<int64_t>(kbyte, rowA - 16)),
+                        smem_base + (uint32_t)(abase + 1024 * j));
+        }
+    }
+    for (int i = 0; i < nst; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4 * RB; ++q) {  // 4 rows x 256 bytes per load
+            const int r = 4 * q + lane / 16;
+            const int64_t rc = min<int64_t>(n0 + r, p.N - 1) - n0;
+            const int64_t off = min<int64_t>(k0 / 2 + (int64_t)i * (KCS / 2) + 256 * wave + 16 * swz(r, lane & 15),
+                                             rowB - 16);
+            gl_lds16_so((uint64_t)(p.B + n0 * rowB), (uint32_t)(rc * rowB + off),
+                        smem_base + (uint32_t)(wbase + i * R * 256 + 1024 * q));
+        }
     }
 
-    // ---- epilogue: lane holds weight rows 4 * kb + r (r = 0..3) for token lr of block mb
+    v4i acc[NACC][RB][MB];
+#pragma unroll
+    for (int h = 0; h < NACC; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[h][rb][mb] = v4i{0, 0, 0, 0};
+
+    for (int i = 0; i < nst; ++i) {
+        wait_rem<4 * RB, 7>(nst - 1 - i);  // this wave's data up to stage i has landed
+        // fragments of the stage's 4 steps of 128 k (k within the range: kl + 32 kb)
+        uint4 xa[4][MB][ABITS == 8 ? 2 : 1], wv[4][RB];
+        bool kv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kl = i * KCS + 512 * wave + 128 * u + 32 * kb;
+            kv[u] = kl < KS;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int t = min(16 * mb + lr, Mi - 1);
+                const uint8_t *sl = smem + abase + (i * Mi + t) * SLB;
+                if constexpr (ABITS == 8) {
+                    const int c0 = 8 * u + 2 * kb;
+                    xa[u][mb][0] = *reinterpret_cast<const uint4 *>(sl + 16 * (c0 ^ (t & 15)));
+                    xa[u][mb][1] = *reinterpret_cast<const uint4 *>(sl + 16 * ((c0 + 1) ^ (t & 15)));
+                } else {
+                    xa[u][mb][0] = *reinterpret_cast<const uint4 *>(sl + 16 * ((4 * u + kb) ^ (t & 15)));
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r = 16 * rb + lr;
+                wv[u][rb] = *reinterpret_cast<const uint4 *>(smem + wbase + i * R * 256 + r * 256 +
+                                                             16 * swz(r, 4 * u + kb));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v4i a0[MB], a1[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                if constexpr (ABITS == 8) {
+                    a0[mb] = kv[u] ? __builtin_bit_cast(v4i, xa[u][mb][0]) : v4i{0, 0, 0, 0};
+                    a1[mb] = kv[u] ? __builtin_bit_cast(v4i, xa[u][mb][1]) : v4i{0, 0, 0, 0};
+                } else {
+                    const uint4 x = xa[u][mb][0];
+                    a0[mb] = kv[u] ? evod(x.x, x.y) : v4i{0, 0, 0, 0};
+                    a1[mb] = kv[u] ? evod(x.z, x.w) : v4i{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                uint4 w = wv[u][rb];
+                w.x ^= xr; w.y ^= xr; w.z ^= xr; w.w ^= xr;
+                v4i w0, w1;
+                if constexpr (ABITS == 8) {
+                    uint32_t q[8];
+                    unpack_nat(w.x, q[0], q[1]);
+                    unpack_nat(w.y, q[2], q[3]);
+                    unpack_nat(w.z, q[4], q[5]);
+                    unpack_nat(w.w, q[6], q[7]);
+                    w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                    w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                } else {
+                    w0 = evod(w.x, w.y);
+                    w1 = evod(w.z, w.w);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    v4i &c = acc[u % NACC][rb][mb];
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0[mb], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1[mb], c, 0, 0, 0);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 1; h < NACC; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[0][rb][mb] += acc[h][rb][mb];
+
+    // ---- fixed-order reduction of the 4 waves' tiles, then partials or the epilogue
+    __syncthreads();
+    v4i *red = reinterpret_cast<v4i *>(smem);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) red[((wave * RB + rb) * MB + mb) * 64 + lane] = acc[0][rb][mb];
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if ((rb * MB + mb) % kWaves != wave) continue;
+            v4i t = red[((0 * RB + rb) * MB + mb) * 64 + lane];
+#pragma unroll
+            for (int q = 1; q < kWaves; ++q) t += red[((q * RB + rb) * MB + mb) * 64 + lane];
+            const int64_t m = 16 * mb + lr;
+            if (m >= M) continue;
+            const int64_t nb = n0 + 16 * rb + 4 * kb;
+            if (part) {  // raw partial sums of this K range (2^SHIFT * acc)
+                int32_t *P = part + ((int64_t)sp * M + m) * p.N;
+                if (nb + 3 < p.N && (p.N & 3) == 0) {
+                    *reinterpret_cast<int4 *>(P + nb) = make_int4(t[0], t[1], t[2], t[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (nb + r < p.N) P[nb + r] = t[r];
+                }
+                continue;
+            }
+            const int rl = 16 * rb + 4 * kb;
+            const float4 sw4 = *reinterpret_cast<const float4 *>(smem + c_sw + 4 * rl);
+            const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
+            const float sxm = *reinterpret_cast<const float *>(smem + c_sx + 4 * m);
+            int a[4] = {t[0], t[1], t[2], t[3]};
+            if (asym) {
+                const uint4 z4 = *reinterpret_cast<const uint4 *>(smem + c_zp + 4 * rl);
+                const int rsm = *reinterpret_cast<const int *>(smem + c_rs + 4 * m);
+                const uint32_t z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] += ((8 - (int)z[r]) << SHIFT) * rsm;
+            }
+            if (p.y_i32) {
+                int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < p.N) Y[nb + r] = a[r] >> SHIFT;
+                continue;
+            }
+            float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.bias) {
+                const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + c_bias + 4 * rl);
+                const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+            }
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
+            if (p.lr_t) {
+                const float *tr = p.lr_t + m * p.lr_r;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t nc = min<int64_t>(nb + r, p.N - 1);
+                    float l = 0.0f;
+                    for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
+                    y[r] += l;
+                }
+            }
+            uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+            const uint32_t b0 = f32_to_bf16(y[0]), b1 = f32_to_bf16(y[1]), b2 = f32_to_bf16(y[2]),
+                           b3 = f32_to_bf16(y[3]);
+            if (nb + 3 < p.N && (p.N & 3) == 0) {
+                *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+            } else {
+                const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < p.N) Y[nb + r] = (uint16_t)bb[r];
+            }
+        }
+    }
+}
+
+// Sum of the S partial sums in a fixed order (exact), then the epilogue.  One thread per
+// token and 4 consecutive output features.
+template <int ABITS>
+__global__ void __launch_bounds__(256) k_gemv_reduce(LinearArgs p, int S, const int32_t *part, int asym) {
     constexpr int SHIFT = ABITS == 8 ? 4 : 8;
-    const int64_t nb = n0 + kb * 4;
-    float swv[4], bsv[4];
-    int zcv[4];
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    const int64_t nq = (p.N + 3) / 4;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= p.M * nq) return;
+    const int64_t m = id / nq, nb = (id % nq) * 4;
+    int a[4] = {0, 0, 0, 0};
+    for (int s = 0; s < S; ++s) {
+        const int32_t *P = part + ((int64_t)s * p.M + m) * p.N;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (nb + r < p.N) a[r] += P[nb + r];
+    }
+    const float sxm = p.sx[m];
+    const int rsm = asym ? p.rowsum[m] : 0;
+    float y[4];
+    uint32_t yb[4];
+    int32_t yi[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t n = min<int64_t>(nb + r, p.N - 1);
-        swv[r] = p.sw[n];
-        bsv[r] = !p.bias ? 0.0f
-                         : p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
-                                       : reinterpret_cast<const float *>(p.bias)[n];
-        zcv[r] = ASYM ? 8 - (int)p.zp[n] : 0;
+        int v = a[r] + (asym ? ((8 - (int)p.zp[n]) << SHIFT) * rsm : 0);
+        yi[r] = v >> SHIFT;
+        const float bs = !p.bias ? 0.0f
+                                 : p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
+                                               : reinterpret_cast<const float *>(p.bias)[n];
+        y[r] = fmaf((float)v, sxm * (p.sw[n] * kUnscale), bs);
+        if (p.lr_t) {
+            const float *tr = p.lr_t + m * p.lr_r;
+            float l = 0.0f;
+            for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), l);
+            y[r] += l;
+        }
+        yb[r] = f32_to_bf16(y[r]);
     }
+    if (p.y_i32) {
+        int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int64_t m = mb * 16 + lr;
-        if (m >= p.M) continue;
-        const float sxm = p.sx[m];
-        const int rsm = ASYM ? p.rowsum[m] : 0;
-        uint32_t ybits[4];
-        int32_t yint[4];
+        for (int r = 0; r < 4; ++r)
+            if (nb + r < p.N) Y[nb + r] = yi[r];
+        return;
+    }
+    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+    if (nb + 3 < p.N && (p.N & 3) == 0) {
+        *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int v = acc[mb][r] >> SHIFT;
-            if constexpr (ASYM) v += zcv[r] * rsm;
-            yint[r] = v;
-            float y = fmaf((float)v, sxm * swv[r], bsv[r]);
-            if (p.lr_t) {
-                const int64_t n = min<int64_t>(nb + r, p.N - 1);
-                const float *tr = p.lr_t + m * p.lr_r;
-                float l = 0.0f;
-                for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), l);
-                y += l;
+        for (int r = 0; r < 4; ++r)
+            if (nb + r < p.N) Y[nb + r] = (uint16_t)yb[r];
+    }
+}
+
+template <int ABITS, int MB, int RB>
+hipError_t launch_split_t(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hipStream_t st) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_split<ABITS, MB, RB>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((k_gemv_split<ABITS, MB, RB>), dim3(pl.grid), dim3(kThreads), pl.lds, st, a, pl.S, pl.KS,
+                       pl.nst, (int)pl.act_bytes, pl.cbase, pl.S > 1 ? part : nullptr, a.zp ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || pl.S == 1) return e;
+    const int64_t threads = a.M * ((a.N + 3) / 4);
+    hipLaunchKernelGGL((k_gemv_reduce<ABITS>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a, pl.S,
+                       part, a.zp ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int ABITS, int MB>
+hipError_t split_rb(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hipStream_t st) {
+    switch (pl.RB) {
+        case 1: return launch_split_t<ABITS, MB, 1>(a, pl, part, st);
+        case 2: return launch_split_t<ABITS, MB, 2>(a, pl, part, st);
+        case 3: return launch_split_t<ABITS, MB, 3>(a, pl, part, st);
+        case 4: return launch_split_t<ABITS, MB, 4>(a, pl, part, st);
+        case 5: return launch_split_t<ABITS, MB, 5>(a, pl, part, st);
+        case 6: return launch_split_t<ABITS, MB, 6>(a, pl, part, st);
+        case 7: return launch_split_t<ABITS, MB, 7>(a, pl, part, st);
+        default: return launch_split_t<ABITS, MB, 8>(a, pl, part, st);
+    }
+}
+
+template <int ABITS>
+hipError_t split_mb(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hipStream_t st) {
+    switch (pl.MB) {
+        case 1: return split_rb<ABITS, 1>(a, pl, part, st);
+        case 2: return split_rb<ABITS, 2>(a, pl, part, st);
+        case 3: return split_rb<ABITS, 3>(a, pl, part, st);
+        default: return split_rb<ABITS, 4>(a, pl, part, st);
+    }
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Streaming path for M <= 16 (no workspace, one pass over K): every wave streams its own
+// slices through its own LDS ring.  In each 1024-k stage wave w takes k in [256 w, 256 w +
+// 256): it loads its 256-byte (int8) or 128-byte (int4) slice of each staged token and its
+// 128-byte piece of each of the workgroup's R weight rows (8 rows x 128 bytes per 1 KB
+// load), D stages ahead, and multiplies a stage as soon as its own loads have landed; no
+// workgroup barrier until the final reduction.  The ring keeps D stages per wave in flight
+// instead of the whole stream, so the wave alternates between issuing and multiplying.
+constexpr int KST = 1024;         // k per stage of the streaming kernel (256 per wave)
+constexpr int kStreamLdsPerWave = 36 * 1024;
+
+template <int ABITS, int TM, int RB>
+struct SL {
+    static constexpr int R = 16 * RB;
+    static constexpr int TB = ABITS == 8 ? 256 : 128;                 // token bytes per wave and stage
+    static constexpr int ACT = TM * TB < 1024 ? 1024 : TM * TB;       // whole 1 KB loads
+    static constexpr int WB = R * 128;                                // weight bytes per wave and stage
+    static constexpr int SLOT = ACT + WB;
+    static constexpr int D0 = kStreamLdsPerWave / SLOT;
+    static constexpr int D = D0 > 8 ? 8 : D0;                         // stages in flight per wave
+    static constexpr int LA = ACT / 1024, LB = WB / 1024;             // loads per stage
+    static constexpr int LPS = LA + LB;
+    static constexpr int RED = kWaves * RB * 1024;
+    static constexpr int RING = kWaves * D * SLOT > RED ? kWaves * D * SLOT : RED;
+    static constexpr int RP = (R + 63) / 64 * 64;
+    static constexpr int C_SW = RING, C_BIAS = C_SW + 4 * RP, C_ZP = C_BIAS + 4 * RP, C_SX = C_ZP + 4 * RP,
+                         C_RS = C_SX + 256;
+    static constexpr int LDS = C_RS + 256;
+    static_assert(D >= 2 && (D - 1) * LPS + 8 <= 63 && LDS <= 160 * 1024, "streaming ring");
+};
+
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int ABITS, int TM, int RB>
+__global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using L = SL<ABITS, TM, RB>;
+    constexpr int R = L::R;
+    constexpr int SHIFT = ABITS == 8 ? 4 : 8;
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * R;
+    const int64_t K = p.K, M = p.M;
+    const int nst = (int)((K + KST - 1) / KST);
+    const int64_t rowA = ABITS == 8 ? K : K / 2;
+    const int64_t rowB = K / 2;
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t xr = asym ? 0x88888888u : 0u;
+    const int ring = wave * L::D * L::SLOT;  // this wave's ring
+
+    if (wave == 0) {  // constants: one dword per row (RP rows) and per token
+#pragma unroll
+        for (int h = 0; h < L::RP / 64; ++h) {
+            const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(64 * h + lane, R - 1), p.N - 1) - n0);
+            gl_lds4_so((uint64_t)(p.sw + n0), 4 * c, smem_base + L::C_SW + 256 * h);
+            if (p.bias) {
+                if (p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + L::C_BIAS + 256 * h);
+                else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + L::C_BIAS + 256 * h);
             }
-            ybits[r] = f32_to_bf16(y);
+            if (asym) gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + L::C_ZP + 256 * h);
+        }
+        const uint32_t t = (uint32_t)min<int64_t>(lane, M - 1);
+        if (asym) gl_lds4_so((uint64_t)p.rowsum, 4 * t, smem_base + L::C_RS);
+        gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + L::C_SX);
+    }
+
+    // stage i of this wave into ring slot i % D.  Token slice chunk c of token t sits at
+    // position c ^ (t & (chunks per slice - 1)); weight chunk c of row r at position swz8(r, c).  Bytes past K
+    // come from the last valid chunk of the row (those k are multiplied by zero codes).
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const uint32_t slot = smem_base + (uint32_t)(ring + (i % L::D) * L::SLOT);
+        const int64_t kw = (int64_t)i * KST + 256 * wave;  // first k of this wave's slice
+#pragma unroll
+        for (int j = 0; j < L::LA; ++j) {
+            constexpr int CPT = L::TB / 16;  // chunks per token slice
+            const int f = min(j * 64 + lane, TM * CPT - 1);
+            const int t = f / CPT, c = f % CPT;
+            const int64_t tc = min<int64_t>(t, M - 1);
+            const int64_t off = min<int64_t>(kw * ABITS / 8 + 16 * (c ^ (t & (CPT - 1))), rowA - 16);
+            gl_lds16_so((uint64_t)p.A, (uint32_t)(tc * rowA + off), slot + 1024 * j);
+        }
+#pragma unroll
+        for (int j = 0; j < L::LB; ++j) {
+            const int r = 8 * j + lane / 8;
+            const int64_t rc = min<int64_t>(n0 + r, p.N - 1) - n0;
+            const int64_t off = min<int64_t>(kw / 2 + 16 * swz8(r, lane & 7), rowB - 16);
+            gl_lds16_so((uint64_t)(p.B + n0 * rowB), (uint32_t)(rc * rowB + off), slot + L::ACT + 1024 * j);
+        }
+    };
+
+    v4i acc[2][RB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[h][rb] = v4i{0, 0, 0, 0};
+
+    for (int i = 0; i < L::D; ++i)
+        if (i < nst) issue(i);
+    for (int i = 0; i < nst; ++i) {
+        wait_rem<L::LPS, L::D - 1>(min(L::D - 1, nst - 1 - i));
+        const uint8_t *sl = smem + ring + (i % L::D) * L::SLOT;
+        const int t = min(lr, (int)M - 1);
+        uint4 xa[2][ABITS == 8 ? 2 : 1], wv[2][RB];
+        bool kv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            kv[u] = (int64_t)i * KST + 256 * wave + 128 * u + 32 * kb < K;
+            if constexpr (ABITS == 8) {  // 16 chunks per token slice
+                const int c0 = 8 * u + 2 * kb;
+                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * (c0 ^ (t & 15)));
+                xa[u][1] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * ((c0 + 1) ^ (t & 15)));
+            } else {  // 8 chunks per token slice
+                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * ((4 * u + kb) ^ (t & 7)));
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r = 16 * rb + lr;
+                wv[u][rb] = *reinterpret_cast<const uint4 *>(sl + L::ACT + r * 128 + 16 * swz8(r, 4 * u + kb));
+            }
+        }
+        // this wave's reads of the slot are complete before the slot is refilled
+        wait_lgkmcnt0();
+        if (i + L::D < nst) issue(i + L::D);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            v4i a0, a1;
+            if constexpr (ABITS == 8) {
+                a0 = kv[u] ? __builtin_bit_cast(v4i, xa[u][0]) : v4i{0, 0, 0, 0};
+                a1 = kv[u] ? __builtin_bit_cast(v4i, xa[u][1]) : v4i{0, 0, 0, 0};
+            } else {
+                const uint4 x = xa[u][0];
+                a0 = kv[u] ? evod(x.x, x.y) : v4i{0, 0, 0, 0};
+                a1 = kv[u] ? evod(x.z, x.w) : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                uint4 w = wv[u][rb];
+                w.x ^= xr; w.y ^= xr; w.z ^= xr; w.w ^= xr;
+                v4i w0, w1;
+                if constexpr (ABITS == 8) {
+                    uint32_t q[8];
+                    unpack_nat(w.x, q[0], q[1]);
+                    unpack_nat(w.y, q[2], q[3]);
+                    unpack_nat(w.z, q[4], q[5]);
+                    unpack_nat(w.w, q[6], q[7]);
+                    w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                    w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                } else {
+                    w0 = evod(w.x, w.y);
+                    w1 = evod(w.z, w.w);
+                }
+                acc[u][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc[u][rb], 0, 0, 0);
+                acc[u][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc[u][rb], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- fixed-order reduction of the 4 waves' tiles, then the epilogue (wave rb % 4 takes
+    // row block rb)
+    __syncthreads();
+    v4i *red = reinterpret_cast<v4i *>(smem);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) red[(wave * RB + rb) * 64 + lane] = acc[0][rb] + acc[1][rb];
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        if (rb % kWaves != wave) continue;
+        v4i tt = red[rb * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < kWaves; ++q) tt += red[(q * RB + rb) * 64 + lane];
+        const int64_t m = lr;
+        if (m >= M) continue;
+        const int64_t nb = n0 + 16 * rb + 4 * kb;
+        const int rl = 16 * rb + 4 * kb;
+        const float4 sw4 = *reinterpret_cast<const float4 *>(smem + L::C_SW + 4 * rl);
+        const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
+        const float sxm = *reinterpret_cast<const float *>(smem + L::C_SX + 4 * m);
+        int a[4] = {tt[0], tt[1], tt[2], tt[3]};
+        if (asym) {
+            const uint4 z4 = *reinterpret_cast<const uint4 *>(smem + L::C_ZP + 4 * rl);
+            const int rsm = *reinterpret_cast<const int *>(smem + L::C_RS + 4 * m);
+            const uint32_t z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] += ((8 - (int)z[r]) << SHIFT) * rsm;
         }
         if (p.y_i32) {
             int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (nb + r < p.N) Y[nb + r] = yint[r];
-        } else {
-            uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
-            if (nb + 3 < p.N && (p.N & 3) == 0) {
-                *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(ybits[0] | (ybits[1] << 16), ybits[2] | (ybits[3] << 16));
-            } else {
+                if (nb + r < p.N) Y[nb + r] = a[r] >> SHIFT;
+            continue;
+        }
+        float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.bias) {
+            const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + L::C_BIAS + 4 * rl);
+            const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (nb + r < p.N) Y[nb + r] = (uint16_t)ybits[r];
+            for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+        }
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
+        if (p.lr_t) {
+            const float *tr = p.lr_t + m * p.lr_r;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t nc = min<int64_t>(nb + r, p.N - 1);
+                float l = 0.0f;
+                for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
+                y[r] += l;
             }
+        }
+        uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+        const uint32_t b0 = f32_to_bf16(y[0]), b1 = f32_to_bf16(y[1]), b2 = f32_to_bf16(y[2]),
+                       b3 = f32_to_bf16(y[3]);
+        if (nb + 3 < p.N && (p.N & 3) == 0) {
+            *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        } else {
+            const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) Y[nb + r] = (uint16_t)bb[r];
         }
     }
 }
 
-template <int ABITS, int MB, int NCH>
-hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
-    const unsigned grid = (unsigned)((a.N + 15) / 16);
-    if (a.zp)
-        hipLaunchKernelGGL((k_gemv<ABITS, MB, NCH, true>), dim3(grid), dim3(64 * kWaves), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_gemv<ABITS, MB, NCH, false>), dim3(grid), dim3(64 * kWaves), 0, st, a);
+template <int ABITS, int TM, int RB>
+hipError_t launch_stream_t(const LinearArgs &a, hipStream_t st) {
+    using L = SL<ABITS, TM, RB>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_stream<ABITS, TM, RB>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
+    if (attr != hipSuccess) return attr;
+    const unsigned grid = (unsigned)((a.N + L::R - 1) / L::R);
+    hipLaunchKernelGGL((k_gemv_stream<ABITS, TM, RB>), dim3(grid), dim3(kThreads), L::LDS, st, a, a.zp ? 1 : 0);
     return hipGetLastError();
 }
 
-template <int ABITS, int MB>
-hipError_t dispatch_k(const LinearArgs &a, hipStream_t st) {
-    const int64_t kq = ((a.K + 127) / 128 + kWaves - 1) / kWaves;  // chunks per lane
-    if (kq <= 4) return launch_t<ABITS, MB, 4>(a, st);
-    if (kq <= 8) return launch_t<ABITS, MB, 8>(a, st);
-    if (kq <= 16) return launch_t<ABITS, MB, 16>(a, st);
-    return launch_t<ABITS, MB, kMaxChunks>(a, st);
+template <int ABITS, int TM>
+hipError_t stream_rb(const LinearArgs &a, hipStream_t st) {
+    const int64_t rb = (a.N + 16 * 256 - 1) / (16 * 256);
+    if (rb <= 1) return launch_stream_t<ABITS, TM, 1>(a, st);
+    if (rb <= 2) return launch_stream_t<ABITS, TM, 2>(a, st);
+    if (rb <= 3) return launch_stream_t<ABITS, TM, 3>(a, st);
+    return launch_stream_t<ABITS, TM, 4>(a, st);
 }
 
 template <int ABITS>
-hipError_t dispatch_mb(const LinearArgs &a, hipStream_t st) {
-    const int mb = (int)((a.M + 15) / 16);
-    switch (mb) {
-        case 1: return dispatch_k<ABITS, 1>(a, st);
-        case 2: return dispatch_k<ABITS, 2>(a, st);
-        case 3: return dispatch_k<ABITS, 3>(a, st);
-        default: return dispatch_k<ABITS, 4>(a, st);
-    }
+hipError_t launch_stream(const LinearArgs &a, hipStream_t st) {
+    if (a.M <= 1) return stream_rb<ABITS, 1>(a, st);
+    if (a.M <= 2) return stream_rb<ABITS, 2>(a, st);
+    if (a.M <= 4) return stream_rb<ABITS, 4>(a, st);
+    if (a.M <= 8) return stream_rb<ABITS, 8>(a, st);
+    return stream_rb<ABITS, 16>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const LinearArgs &a, int act_bits, hipStream_t st) {
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits) {
+    if (M <= 16) return 0;  // the streaming kernel needs none
+    const SplitPlan pl = plan_split(M, N, K, act_bits);
+    return pl.S > 1 ? (size_t)pl.S * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
+hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st) {
     if (a.M == 0) return hipSuccess;
     if (a.M > 64) return hipErrorInvalidValue;
+    if (a.M <= 16) return act_bits == 8 ? launch_stream<8>(a, st) : launch_stream<4>(a, st);
+    const SplitPlan pl = plan_split(a.M, a.N, a.K, act_bits);
+    const size_t need = pl.S > 1 ? (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(int32_t) : 0;
+    if (pl.S >= 1 && (need == 0 || (ws && ws_bytes >= need))) {
+        int32_t *part = static_cast<int32_t *>(ws);
+        return act_bits == 8 ? split_mb<8>(a, pl, part, st) : split_mb<4>(a, pl, part, st);
+    }
     return act_bits == 8 ? dispatch_mb<8>(a, st) : dispatch_mb<4>(a, st);
 }
 

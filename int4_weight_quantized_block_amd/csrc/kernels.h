@@ -34,7 +34,10 @@ struct LinearArgs {
 };
 
 hipError_t launch_gemm(const LinearArgs &a, int act_bits, hipStream_t st);
-hipError_t launch_gemv(const LinearArgs &a, int act_bits, hipStream_t st);
+// Small-M path (M <= 64).  With a workspace of gemv_workspace_bytes() bytes (0 when none is
+// needed) the K-split kernel runs; without one, the LDS-ring kernel.
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits);
+hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
 
 hipError_t launch_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r,
                                float *t, hipStream_t st);

@@ -88,11 +88,10 @@ const char *w4_status_string(int status) {
 }
 
 size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r) {
-    (void)N;
-    (void)K;
-    (void)act_bits;
-    if (M <= 0 || r <= 0) return 0;
-    return align256((size_t)M * (size_t)r * sizeof(float));
+    if (M <= 0) return 0;
+    const size_t t = r > 0 ? align256((size_t)M * (size_t)r * sizeof(float)) : 0;
+    const size_t part = M <= 64 && N > 0 && K > 0 ? align256(w4::gemv_workspace_bytes(M, N, K, act_bits)) : 0;
+    return t + part;
 }
 
 size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r) {
@@ -171,6 +170,7 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     const float *t = nullptr;
     const uint16_t *l2 = nullptr;
     int r = 0;
+    size_t tbytes = 0;  // workspace bytes taken by the low-rank t
     if (lr && y_kind == W4_OUT_BF16) {
         r = lr->r;
         if (r < 1 || r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: lowrank r=%d (supported 1..64)", fn, r);
@@ -184,12 +184,12 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
             if (!lr->x || !lr->l1) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
             if (!aligned16(lr->x) || !aligned16(lr->l1))
                 return fail(W4_ERR_ALIGN, "%s: lowrank x / l1 not 16-byte aligned", fn);
-            const size_t need = w4_workspace_bytes(M, N, K, act_bits, r);
-            if (!ws || ws_bytes < need)
-                return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-            if (!aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
+            tbytes = align256((size_t)M * (size_t)r * sizeof(float));
+            if (!ws || ws_bytes < tbytes)
+                return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, tbytes);
         }
     }
+    if (ws && !aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
     if (M == 0) return ok();
     if (lr && y_kind == W4_OUT_BF16 && !t) {
         float *tw = static_cast<float *>(ws);
@@ -214,7 +214,10 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     a.M = M;
     a.N = N;
     a.K = K;
-    hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, st) : w4::launch_gemm(a, act_bits, st);
+    // the rest of the workspace (if any) holds the small-M path's K-split partial sums
+    void *gws = ws ? static_cast<uint8_t *>(ws) + tbytes : nullptr;
+    const size_t gbytes = ws ? ws_bytes - tbytes : 0;
+    hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, gws, gbytes, st) : w4::launch_gemm(a, act_bits, st);
     return hip_status(e, fn);
 }
 
