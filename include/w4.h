@@ -151,7 +151,8 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
 
 /* w4_lowrank_down - t = x . l1, f32 [M, r], from bf16 x [M, K] and bf16 l1 [K, r]
  * (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of the low-rank
- *  residual).  Lets linears that read the same input share t.  1 <= r <= 64. */
+ *  residual).  Lets linears that read the same input share t.  1 <= r <= 64; K a multiple
+ *  of 8 (W4_ERR_SHAPE otherwise).  Exact bf16 products, fp32 accumulation. */
 int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t,
                     void *stream);
 

@@ -79,6 +79,10 @@ struct Lay {
     static constexpr int LDS_BYTES = C_ZP + BN * 4;
 };
 
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef float fl8 __attribute__((ext_vector_type(8)));
+typedef float fl16 __attribute__((ext_vector_type(16)));
+
 // physical chunk of logical chunk c in row r (an involution)
 __device__ __forceinline__ int swz_a8(int r, int c) { return c ^ ((r >> 1) & 7); }
 __device__ __forceinline__ int swz_4(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -209,7 +213,7 @@ __device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc
 }
 
 template <int ABITS, bool ASYM, bool KTAIL>
-__global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n) {
+__global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n, int l2_dma) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
     const int tid = threadIdx.x;
@@ -251,6 +255,41 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
                 else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, cb + L::C_BIAS + q * 256);
             }
             if constexpr (ASYM) gl_lds1_so((uint64_t)(p.zp + n0), c, cb + L::C_ZP + q * 256);
+        }
+    }
+    // The low-rank l2 tile [r, BN] (bf16 rows of the tile's features; columns past N hold
+    // clamped copies, never used) goes past the constants: with the same direct loads, spread
+    // over the waves, when its rows are 16-byte aligned (N % 8 == 0), else element by element
+    // through registers (a one-off wait, ragged N only).  The prologue's wait and barrier
+    // make it visible to every wave.
+    if (p.lr_t) {
+        if (l2_dma) {
+            constexpr int CPR = BN * 2 / 16;  // 24 chunks of 16 bytes per row
+            const int nins = (CPR * p.lr_r + 63) / 64;
+            const uint32_t lb = lds_addr(smem) + L::LDS_BYTES;
+            for (int ins = wave; ins < nins; ins += kWaves) {
+                const int c = ins * 64 + lane;
+                const int q = min(c / CPR, p.lr_r - 1);  // whole 1 KB blocks: the tail repeats row r-1
+                const int64_t nn = min<int64_t>(n0 + 8 * (c % CPR), p.N - 8) - n0;
+                gl_lds16_so((uint64_t)(p.lr_l2 + n0), (uint32_t)((int64_t)q * p.N * 2 + nn * 2), lb + ins * 1024);
+            }
+        } else {
+            uint16_t *lt = reinterpret_cast<uint16_t *>(smem + L::LDS_BYTES);
+            const int tot = p.lr_r * BN;
+            for (int e0 = tid; e0 < tot; e0 += 8 * kThreads) {
+                uint16_t v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + u * kThreads;
+                    const int64_t nc = min<int64_t>(n0 + e % BN, p.N - 1);
+                    v[u] = e < tot ? p.lr_l2[(int64_t)(e / BN) * p.N + nc] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (e0 + u * kThreads < tot) lt[e0 + u * kThreads] = v[u];
+            }
+            wait_vmcnt<0>();
+            wait_lgkmcnt0();
         }
     }
     float sxv[FM];
@@ -431,30 +470,64 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     uint8_t *stg = smem + ((nk + 1) % STAGES) * L::STAGE + wave * 32 * SROW;
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     const bool full_n = (p.N & 7) == 0;  // 16-byte aligned rows
+
+    // Low-rank branch on the bf16 MFMA: lr[n][m] = sum_q l2[q][n] t[m][q] comes out in the
+    // accumulators' 32x32 layout when l2 transposed is the A operand (rows = features) and t
+    // the B operand (columns = tokens).  Each lane holds the same 8 consecutive ranks q of
+    // both operands (k-steps of 16, ranks past r zero).  t (f32) goes in as a bf16 high part
+    // plus a bf16 remainder, so its products keep about 16 significant bits; l2 is bf16.
+    const int lrr = p.lr_t ? p.lr_r : 0;
+    const int nks = (lrr + 15) >> 4;  // uniform
+    const uint16_t *l2t = reinterpret_cast<const uint16_t *>(smem + L::LDS_BYTES);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int64_t mrow0 = m0 + wm * WTM + i * 32;
+        bf8 th[4], tl[4];
+        if (nks) {
+            const float *tr = p.lr_t + min<int64_t>(mrow0 + lr, p.M - 1) * lrr;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks >= nks) break;
+                const int q0 = 16 * ks + 8 * kb;
+                fl8 v;
+                if ((lrr & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
+                    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    const float4 u = q0 < lrr ? *reinterpret_cast<const float4 *>(tr + q0) : z;
+                    const float4 w = q0 + 4 < lrr ? *reinterpret_cast<const float4 *>(tr + q0 + 4) : z;
+                    v = fl8{u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = q0 + e < lrr ? tr[q0 + e] : 0.0f;
+                }
+                th[ks] = __builtin_convertvector(v, bf8);
+                tl[ks] = __builtin_convertvector(v - __builtin_convertvector(th[ks], fl8), bf8);
+            }
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+            fl16 lacc = {};
+            const int nl = wn * WTN + j * 32 + lr;  // feature within the tile
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks >= nks) break;
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int q = 16 * ks + 8 * kb + e;
+                    h[e] = q < lrr ? l2t[q * BN + nl] : 0u;
+                }
+                const bf8 la = __builtin_bit_cast(bf8, make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16,
+                                                                  h[4] | h[5] << 16, h[6] | h[7] << 16));
+                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, th[ks], lacc, 0, 0, 0);
+                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, tl[ks], lacc, 0, 0, 0);
+            }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float y[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int a = acc[j][i][4 * g + r] + (ASYM ? zcv[j][g][r] * rsv[i] : 0);
-                    y[r] = fmaf((float)a, sxv[i] * swv[j][g][r], bsv[j][g][r]);
-                }
-                if (p.lr_t) {
-                    const int64_t mc = min<int64_t>(mrow0 + lr, p.M - 1);
-                    const float *tr = p.lr_t + mc * p.lr_r;
-                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * kb;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int64_t nc = min<int64_t>(n + r, p.N - 1);
-                        float l = 0.0f;
-                        for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
-                        y[r] += l;
-                    }
+                    y[r] = fmaf((float)a, sxv[i] * swv[j][g][r], bsv[j][g][r]) + lacc[4 * g + r];
                 }
                 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
                 typedef float fl2 __attribute__((ext_vector_type(2)));
@@ -487,12 +560,18 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 
 template <int ABITS, bool ASYM, bool KTAIL>
 hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
-    constexpr size_t lds = Lay<ABITS>::LDS_BYTES;
+    // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
+    // 24 * r 16-byte chunks, at most 24 KB for r <= 64)
+    constexpr size_t base = Lay<ABITS>::LDS_BYTES, maxl2 = 24 * 1024;
+    static_assert(base + maxl2 <= 160 * 1024, "LDS budget");
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(base + maxl2));
     if (attr != hipSuccess) return attr;
+    const int l2_dma = a.N % 8 == 0;
+    const size_t lds = base + (a.lr_t ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn);
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn,
+                       l2_dma);
     return hipGetLastError();
 }
 

@@ -741,7 +741,8 @@ struct SL {
     static constexpr int WB = R * 128;                                // weight bytes per wave and stage
     static constexpr int SLOT = ACT + WB;
     static constexpr int D0 = kStreamLdsPerWave / SLOT;
-    static constexpr int D = D0 > 8 ? 8 : D0;                         // stages in flight per wave
+    static constexpr int D = D0 > 2 ? 2 : D0;  // stages per wave ring (2 measured fastest; deeper rings
+                                               // only lengthen the initial issue phase)
     static constexpr int LA = ACT / 1024, LB = WB / 1024;             // loads per stage
     static constexpr int LPS = LA + LB;
     static constexpr int RED = kWaves * RB * 1024;

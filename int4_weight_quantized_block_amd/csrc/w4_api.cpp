@@ -143,7 +143,9 @@ int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g,
 
 int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t, void *stream) {
     const char *fn = "w4_lowrank_down";
-    if (M < 0 || K < 1 || K > W4_MAX_K) return fail(W4_ERR_SHAPE, "%s: M=%lld K=%lld", fn, (long long)M, (long long)K);
+    if (M < 0 || K < 8 || K % 8 || K > W4_MAX_K)
+        return fail(W4_ERR_SHAPE, "%s: M=%lld K=%lld (K must be a positive multiple of 8)", fn, (long long)M,
+                    (long long)K);
     if (r < 1 || r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: r=%d (supported 1..64)", fn, r);
     if (M == 0) return ok();
     W4_CHECK_PTR(x);

@@ -201,3 +201,34 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
         low = w4.LowRank(l2=L2.to(DEV), t=t)
     y2 = w4.w4_linear_cached_rot(q, s, rs, bits, *args, bias=bias_d, lowrank=low)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,bits,asym,r", [
+    (300, 384, 512, 8, False, 32), (300, 389, 512, 8, True, 5), (260, 200, 768, 4, False, 20),
+    (300, 392, 256, 4, True, 40), (257, 384, 512, 8, False, 64), (513, 191, 320, 8, False, 63),
+    (8, 389, 512, 8, False, 20), (40, 384, 512, 4, True, 64),
+])
+def test_linear_lowrank_ranks(M, N, K, bits, asym, r):
+    """The low-rank branch at ranks that fill 1..4 k-steps of 16 (r % 4 != 0 included), with
+    factors large enough that the branch carries a good part of the output; ragged N takes
+    the element-wise l2 staging of the large-M kernel."""
+    say("linear lowrank M=%d N=%d K=%d bits=%d asym=%s r=%d" % (M, N, K, bits, asym, r))
+    g = 64
+    rg = rng(7 * M + N + r)
+    X = act_input(M, K, seed=M + 5 * r)
+    W = torch.from_numpy((rg.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    L1 = torch.from_numpy((rg.standard_normal((K, r)) * 0.05).astype(np.float32)).to(torch.bfloat16)
+    L2 = torch.from_numpy((rg.standard_normal((r, N)) * 0.2).astype(np.float32)).to(torch.bfloat16)
+    ref = oracle.linear(X, W, g, bits, asym, L1=L1, L2=L2)
+    # the case can see a wrong branch: without it the output is far off
+    assert rel_frob(torch.from_numpy(ref["y64"] - ref["lr"]), ref["y64"]) > 20 * FROB_TOL
+    pw = ref["w"]
+    Xd = X.to(DEV)
+    args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
+    t = w4.w4_lowrank_down(Xd, L1.to(DEV))
+    tref = oracle.to_f64(X) @ oracle.to_f64(L1)
+    assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
+    y = w4.w4_linear(Xd, g, bits, *args, lowrank=w4.LowRank(l2=L2.to(DEV), t=t))
+    err = rel_frob(y, ref["y64"])
+    say("  rel frob %.3e" % err)
+    assert err <= FROB_TOL
