@@ -156,7 +156,7 @@ def cpu_baseline(layer, rows_wanted):
 
 COPY_BYTES = 512 << 20
 # kernel-name prefix -> (short name, source file)
-KERNEL_SOURCE = {"k_gemm<": ("k_gemm", "gemm.hip"), "k_gemv<": ("k_gemv", "gemv.hip"),
+KERNEL_SOURCE = {"k_gemm<": ("k_gemm", "gemm.hip"), "k_gemv": ("k_gemv", "gemv.hip"),
                  "k_rotquant": ("k_rotquant", "rotquant.hip")}
 
 
