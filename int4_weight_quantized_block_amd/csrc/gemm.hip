@@ -82,6 +82,7 @@ struct Lay {
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float fl8 __attribute__((ext_vector_type(8)));
 typedef float fl16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // physical chunk of logical chunk c in row r (an involution)
 __device__ __forceinline__ int swz_a8(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -212,7 +213,11 @@ __device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc
     if constexpr (NEXT) pin<ABITS>(on);
 }
 
-template <int ABITS, bool ASYM, bool KTAIL>
+// Output forms, one kernel each (the epilogue is straight-line code run once per tile, so
+// leaving out what a launch does not need keeps it short)
+enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2 };
+
+template <int ABITS, bool ASYM, bool KTAIL, int EPI>
 __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n, int l2_dma) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
@@ -262,7 +267,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // over the waves, when its rows are 16-byte aligned (N % 8 == 0), else element by element
     // through registers (a one-off wait, ragged N only).  The prologue's wait and barrier
     // make it visible to every wave.
-    if (p.lr_t) {
+    if constexpr (EPI == kEpiLowRank) {
         if (l2_dma) {
             constexpr int CPR = BN * 2 / 16;  // 24 chunks of 16 bytes per row
             const int nins = (CPR * p.lr_r + 63) / 64;
@@ -448,7 +453,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
             }
         }
     }
-    if (p.y_i32) {
+    if constexpr (EPI == kEpiI32) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int64_t m = m0 + wm * WTM + i * 32 + lr;
@@ -476,13 +481,15 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // the B operand (columns = tokens).  Each lane holds the same 8 consecutive ranks q of
     // both operands (k-steps of 16, ranks past r zero).  t (f32) goes in as a bf16 high part
     // plus a bf16 remainder, so its products keep about 16 significant bits; l2 is bf16.
-    const int lrr = p.lr_t ? p.lr_r : 0;
+    const int lrr = EPI == kEpiLowRank ? p.lr_r : 0;
     const int nks = (lrr + 15) >> 4;  // uniform
     const uint16_t *l2t = reinterpret_cast<const uint16_t *>(smem + L::LDS_BYTES);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int64_t mrow0 = m0 + wm * WTM + i * 32;
         bf8 th[4], tl[4];
+        // (keeps this block's t loads here rather than hoisted for all blocks at once)
+        if constexpr (EPI == kEpiLowRank) asm volatile("" ::: "memory");
         if (nks) {
             const float *tr = p.lr_t + min<int64_t>(mrow0 + lr, p.M - 1) * lrr;
 #pragma unroll
@@ -549,7 +556,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
             const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * SROW + ch * 16);
             if (m >= p.M || n >= p.N) continue;
             if (full_n && n + 7 < p.N) {
-                *reinterpret_cast<uint4 *>(Y + m * p.N + n) = v;
+                // streaming store: the output is not read again by this kernel
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(Y + m * p.N + n));
             } else {
                 const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
                 for (int r = 0; r < 8 && n + r < p.N; ++r) Y[m * p.N + n + r] = h[r];
@@ -558,26 +566,34 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     }
 }
 
-template <int ABITS, bool ASYM, bool KTAIL>
+template <int ABITS, bool ASYM, bool KTAIL, int EPI>
 hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
     // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
     // 24 * r 16-byte chunks, at most 24 KB for r <= 64)
     constexpr size_t base = Lay<ABITS>::LDS_BYTES, maxl2 = 24 * 1024;
     static_assert(base + maxl2 <= 160 * 1024, "LDS budget");
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL, EPI>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(base + maxl2));
     if (attr != hipSuccess) return attr;
     const int l2_dma = a.N % 8 == 0;
-    const size_t lds = base + (a.lr_t ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
+    const size_t lds = base + (EPI == kEpiLowRank ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn,
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn,
                        l2_dma);
     return hipGetLastError();
 }
 
 template <int ABITS, bool ASYM>
 hipError_t launch_k(const LinearArgs &a, hipStream_t st) {
-    return a.K % BK ? launch_t<ABITS, ASYM, true>(a, st) : launch_t<ABITS, ASYM, false>(a, st);
+    const int epi = a.y_i32 ? kEpiI32 : a.lr_t ? kEpiLowRank : kEpiBf16;
+    if (a.K % BK) {
+        if (epi == kEpiI32) return launch_t<ABITS, ASYM, true, kEpiI32>(a, st);
+        if (epi == kEpiLowRank) return launch_t<ABITS, ASYM, true, kEpiLowRank>(a, st);
+        return launch_t<ABITS, ASYM, true, kEpiBf16>(a, st);
+    }
+    if (epi == kEpiI32) return launch_t<ABITS, ASYM, false, kEpiI32>(a, st);
+    if (epi == kEpiLowRank) return launch_t<ABITS, ASYM, false, kEpiLowRank>(a, st);
+    return launch_t<ABITS, ASYM, false, kEpiBf16>(a, st);
 }
 
 }  // namespace
