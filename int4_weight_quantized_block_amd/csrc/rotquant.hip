@@ -376,6 +376,211 @@ k_rotquant_stream(const void *__restrict__ Xv, int64_t M, int K, int T, int R, i
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Row-team variant for K % 1024 == 0 with K / 1024 = C * W, C <= 4 and W in {1, 2, 4, 8}
+// (3072, 4096, 6144, 12288, ...).  A team of W waves owns one token row at a time and walks
+// the rows team, team + nteams, ... with the next row's input loads in flight while it
+// transforms the current one.  Every wave carries the same amount of work, so the waves of
+// a launch (two per SIMD) finish together, and W = 1 needs no workgroup barrier at all.
+//
+// Lane layout: a 16-lane row r16 of wave w holds C 256-element blocks, numbers
+// (4 w + r16) C + c; lane l of that row holds elements 16 (l & 15) .. 16 (l & 15) + 15 of each,
+// so a 16-lane row reads and writes contiguous bytes.  Within a block, element bits 0-3 are
+// butterflies in registers, bits 4-5 quad DPP exchanges, and (g = 256) bits 6-7 exchanges
+// with the lanes 4 and 8 apart through ds_swizzle, which runs on the LDS unit and so adds
+// only the fma to the VALU's load (measured: faster than swizzling all four stages, and than
+// DPP moves for these two).
+template <int PAT>
+__device__ __forceinline__ double swz_f64(double x) {
+    const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(x), PAT);
+    const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(x), PAT);
+    return __hiloint2double(hi, lo);
+}
+constexpr int kSwzXor4 = 0x101F;  // bit-mask mode: and 0x1f, or 0, xor 4
+constexpr int kSwzXor8 = 0x201F;  // xor 8
+
+template <int G, int BITS, bool F32IN, int C>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nteams, void *__restrict__ qv,
+               float *__restrict__ tok_scale, int32_t *__restrict__ tok_rowsum) {
+    __shared__ double red_d[2][8];
+    __shared__ int red_i[2][8];
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
+    constexpr int NW = F32IN ? 4 : 2;  // 16-byte words per 16-element chunk
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cl = lane & 15;
+    const int blk0 = (w * 4 + (lane >> 4)) * C;  // this lane's first 256-element block in the row
+
+    auto load = [&](int64_t row, uint4 (&x)[C][NW]) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t e0 = row * K + (int64_t)(blk0 + c) * 256 + 16 * cl;
+            const uint4 *src = F32IN ? reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(Xv) + e0)
+                                     : reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(Xv) + e0);
+#pragma unroll
+            for (int j = 0; j < NW; ++j) x[c][j] = src[j];
+        }
+    };
+
+    uint4 nxt[C][NW];
+    int64_t row = blockIdx.x;
+    if (row < M) load(row, nxt);
+    int par = 0;
+    for (; row < M; row += nteams, par ^= 1) {
+        double v[C][16];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if constexpr (F32IN) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[c][4 * j + 0] = (double)__uint_as_float(nxt[c][j].x);
+                    v[c][4 * j + 1] = (double)__uint_as_float(nxt[c][j].y);
+                    v[c][4 * j + 2] = (double)__uint_as_float(nxt[c][j].z);
+                    v[c][4 * j + 3] = (double)__uint_as_float(nxt[c][j].w);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    v[c][8 * j + 0] = (double)bf16_lo(nxt[c][j].x);
+                    v[c][8 * j + 1] = (double)bf16_hi(nxt[c][j].x);
+                    v[c][8 * j + 2] = (double)bf16_lo(nxt[c][j].y);
+                    v[c][8 * j + 3] = (double)bf16_hi(nxt[c][j].y);
+                    v[c][8 * j + 4] = (double)bf16_lo(nxt[c][j].z);
+                    v[c][8 * j + 5] = (double)bf16_hi(nxt[c][j].z);
+                    v[c][8 * j + 6] = (double)bf16_lo(nxt[c][j].w);
+                    v[c][8 * j + 7] = (double)bf16_hi(nxt[c][j].w);
+                }
+            }
+        }
+        if (row + nteams < M) load(row + nteams, nxt);  // in flight during the transform
+
+        // ---- Walsh-Hadamard butterflies (unnormalised)
+#pragma unroll
+        for (int c = 0; c < C; ++c) fwht16(v[c]);
+        {
+            const double s1 = (cl & 1) ? -1.0 : 1.0, s2 = (cl & 2) ? -1.0 : 1.0;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s1, dpp_f64<kQuadXor1>(v[c][i]));
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s2, dpp_f64<kQuadXor2>(v[c][i]));
+        }
+        if constexpr (G == 256) {
+            const double s4 = (cl & 4) ? -1.0 : 1.0, s8 = (cl & 8) ? -1.0 : 1.0;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s4, swz_f64<kSwzXor4>(v[c][i]));
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s8, swz_f64<kSwzXor8>(v[c][i]));
+        }
+
+        // ---- per-token absmax: the wave, then (W > 1) the team through LDS
+        double am = 0.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) am = fmax(am, fabs(v[c][i]));
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) am = fmax(am, __shfl_xor(am, off));
+        if (W > 1) {
+            if (lane == 0) red_d[par][w] = am;
+            __syncthreads();
+            am = red_d[par][0];
+            for (int u = 1; u < W; ++u) am = fmax(am, red_d[par][u]);
+        }
+        const float scale = (float)((am * INV_SQRT_G) / (double)QMAX);
+        const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
+        if (w == 0 && lane == 0) tok_scale[row] = scale;
+
+        // ---- quantize, pack, store (each lane's 16 codes of a block are contiguous)
+        int rowsum = 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            uint32_t d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int q4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = __double2loint(fma(v[c][4 * j + r], rr, kRoundMagic));
+                    q4[r] = min(max(qi, -QMAX - 1), QMAX);
+                }
+                d[j] = (uint32_t)(q4[0] & 0xff) | ((uint32_t)(q4[1] & 0xff) << 8) | ((uint32_t)(q4[2] & 0xff) << 16) |
+                       ((uint32_t)(q4[3] & 0xff) << 24);
+                rowsum = __builtin_amdgcn_sdot4((int)d[j], 0x01010101, rowsum, false);
+            }
+            const int64_t e0 = (int64_t)(blk0 + c) * 256 + 16 * cl;
+            if constexpr (BITS == 8) {
+                *reinterpret_cast<uint4 *>(reinterpret_cast<int8_t *>(qv) + row * K + e0) = make_uint4(d[0], d[1], d[2], d[3]);
+            } else {
+                uint32_t x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = d[j] & 0x0F0F0F0Fu;
+                    x[j] = lo | (lo >> 4);
+                }
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(qv) + row * (K / 2) + e0 / 2) =
+                    make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u));
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) rowsum += __shfl_xor(rowsum, off);
+        if (W > 1) {
+            if (lane == 0) red_i[par][w] = rowsum;
+            __syncthreads();
+            rowsum = 0;
+            for (int u = 0; u < W; ++u) rowsum += red_i[par][u];
+        }
+        if (w == 0 && lane == 0) tok_rowsum[row] = rowsum;
+    }
+}
+
+// (C, W) for the row-team kernel, or false
+bool row_team_split(int64_t K, int &C, int &W) {
+    if (K <= 0 || K % 1024) return false;
+    const int64_t n = K / 1024;
+    for (int c : {3, 4, 2, 1}) {
+        if (n % c) continue;
+        const int64_t w = n / c;
+        if (w == 1 || w == 2 || w == 4 || w == 8) {
+            C = c;
+            W = (int)w;
+            return true;
+        }
+    }
+    return false;
+}
+
+template <int G, int BITS, bool F32IN, int C>
+hipError_t launch_row_c(const void *X, int64_t M, int64_t K, int W, void *q, float *s, int32_t *rs, hipStream_t st) {
+    // two waves per SIMD over the whole chip, one team of W waves per workgroup
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t nteams = std::min<int64_t>(M, (int64_t)ncu * 8 / W);
+    hipLaunchKernelGGL((k_rotquant_row<G, BITS, F32IN, C>), dim3((unsigned)nteams), dim3(64 * W), 0, st, X, M,
+                       (int)K, W, nteams, q, s, rs);
+    return hipGetLastError();
+}
+
+template <int G, int BITS, bool F32IN>
+hipError_t launch_row(const void *X, int64_t M, int64_t K, int C, int W, void *q, float *s, int32_t *rs,
+                      hipStream_t st) {
+    switch (C) {
+        case 1: return launch_row_c<G, BITS, F32IN, 1>(X, M, K, W, q, s, rs, st);
+        case 2: return launch_row_c<G, BITS, F32IN, 2>(X, M, K, W, q, s, rs, st);
+        case 3: return launch_row_c<G, BITS, F32IN, 3>(X, M, K, W, q, s, rs, st);
+        default: return launch_row_c<G, BITS, F32IN, 4>(X, M, K, W, q, s, rs, st);
+    }
+}
+
 struct Split {
     int C, T, R;
 };
@@ -456,6 +661,18 @@ bool rotquant_supported(int64_t K, int g) {
 hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st) {
     if (M == 0) return hipSuccess;
+    int C = 0, W = 0;
+    if (row_team_split(K, C, W)) {
+#define W4_RT(G, B, F) return launch_row<G, B, F>(X, M, K, C, W, q, tok_scale, tok_rowsum, st)
+        if (g == 64) {
+            if (bits == 8) { if (f32in) W4_RT(64, 8, true); else W4_RT(64, 8, false); }
+            else { if (f32in) W4_RT(64, 4, true); else W4_RT(64, 4, false); }
+        } else {
+            if (bits == 8) { if (f32in) W4_RT(256, 8, true); else W4_RT(256, 8, false); }
+            else { if (f32in) W4_RT(256, 4, true); else W4_RT(256, 4, false); }
+        }
+#undef W4_RT
+    }
     if (stream_ok(K)) {
 #define W4_RS(G, B, F) return launch_stream<G, B, F>(X, M, K, q, tok_scale, tok_rowsum, st)
         if (g == 64) {

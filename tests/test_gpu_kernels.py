@@ -92,7 +92,8 @@ def test_accumulators_extreme_codes():
     (3, 4096, 256, 8, torch.bfloat16), (300, 768, 256, 8, torch.bfloat16), (21, 192, 64, 4, torch.float32),
     (40, 1280, 64, 8, torch.bfloat16), (2, 4608, 256, 8, torch.float32), (1, 64, 64, 4, torch.bfloat16),
     (37, 9472, 256, 8, torch.bfloat16), (3, 32768, 256, 4, torch.bfloat16), (1000, 256, 64, 8, torch.bfloat16),
-    (129, 1024, 256, 4, torch.float32),
+    (129, 1024, 256, 4, torch.float32), (64, 2048, 64, 8, torch.bfloat16), (50, 6144, 256, 4, torch.bfloat16),
+    (31, 3072, 64, 8, torch.bfloat16), (2100, 1024, 256, 8, torch.bfloat16), (600, 12288, 256, 8, torch.bfloat16),
 ])
 def test_rotate_quant_act_matches_oracle(M, K, g, bits, dtype):
     say("rotquant M=%d K=%d g=%d bits=%d %s" % (M, K, g, bits, dtype))
