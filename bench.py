@@ -11,9 +11,13 @@ once before timing (an offline step).  Inputs are resident in HBM; the timed loo
 cycles through enough distinct input copies (> 256 MB) that reads come from HBM, not
 from the 256 MB Infinity Cache.
 
+The timed steps replay, back to back, a HIP graph holding the step's launches (one graph
+per input copy, captured once before timing; ``--eager`` times plain launches instead).
+
 Prints ONE JSON line.  ``roofline`` describes the dominant kernel, timed live with HIP
-events around its launches on the stream it runs on; ``cpu_baseline`` is the CPU oracle
-timed on this host's cores on a bounded sample of the same workload.
+events around its launches on the stream it runs on (an eager pass of the same K steps
+before the timed replays); ``cpu_baseline`` is the CPU oracle timed on this host's cores on
+a bounded sample of the same workload.
 
 Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
   attn_proj    (default) W4A8 g=256, X [4096, 3072] -> 3072           metric: TOPS
@@ -54,6 +58,7 @@ def parse():
     ap.add_argument("--M", type=int, default=None, help="tokens (small_m: 1, 4, 16 or 64)")
     ap.add_argument("--K", type=int, default=12288, help="small_m: input features (4096 or 12288)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-rows", type=int, default=None, help="token rows in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed loop, run two plain 512 MiB device copies (counter calibration)")
@@ -283,6 +288,7 @@ def main():
     torch.cuda.synchronize()
     log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
                                                                             args.warmup))
+    # per-launch durations: eager launches bracketed by events on the launch stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -296,9 +302,30 @@ def main():
     wall = time.perf_counter() - t0
     t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
     t_mm = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    log("bench: eager %.3f ms/step wall; rotate+quant %.2f us, GEMM %.2f us per launch" % (
+        wall / args.steps * 1e3, t_rq * 1e6, t_mm * 1e6))
+    if not args.eager:
+        # the timed steps: one HIP graph per input copy holding the step's two launches
+        # (captured once, untimed), replayed back to back, so the GPU does not wait for the host
+        side = torch.cuda.Stream()
+        graphs = []
+        for c in range(ncopy):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph, stream=side):
+                st2 = torch.cuda.current_stream().cuda_stream
+                w4._check(f_rq(*(rq_args[c][:-1] + (st2,))))
+                w4._check(f_mm(*(mm_args[c][:-1] + (st2,))))
+            graphs.append(gph)
+        for c in range(ncopy):
+            graphs[c].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % ncopy].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    log("bench: %.3f ms/step wall; rotate+quant %.2f us, GEMM %.2f us per launch" % (ms_step, t_rq * 1e6,
-                                                                                   t_mm * 1e6))
+    log("bench: %.3f ms/step wall (%s)" % (ms_step, "eager" if args.eager else "graph replay"))
     if args.copy_calibration:
         copy_calibration(dev)
 
@@ -322,6 +349,7 @@ def main():
         "gemm_tops": round(lin.ops() / t_mm / 1e12, 2),
         "gemm_weight_gbs": round(lin.weight_bytes() / t_mm / 1e9, 1),
         "gemm_alg_bytes": lin.gemm_bytes(),
+        "timed_launch": "eager" if args.eager else "hip graph replay per step",
         "input_copies": ncopy,
     }
     cpu = None
