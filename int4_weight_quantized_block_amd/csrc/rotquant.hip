@@ -377,8 +377,9 @@ k_rotquant_stream(const void *__restrict__ Xv, int64_t M, int K, int T, int R, i
 }
 
 // ---------------------------------------------------------------------------------------------
-// Row-team variant for K % 1024 == 0 with K / 1024 = C * W, C <= 4 and W in {1, 2, 4, 8}
-// (3072, 4096, 6144, 12288, ...).  A team of W waves owns one token row at a time and walks
+// Row-team variant for K % 1024 == 0 with K / 1024 = C * W: C <= 4 chunks of 16 per lane and
+// W in {1, 2, 4, 8} waves per row, or for a few rows C = 1 and W <= 16 (3072, 4096, 6144,
+// 12288, ...).  A team of W waves owns one token row at a time and walks
 // the rows team, team + nteams, ... with the next row's input loads in flight while it
 // transforms the current one.  Every wave carries the same amount of work, so the waves of
 // a launch (two per SIMD) finish together, and W = 1 needs no workgroup barrier at all.
@@ -400,11 +401,11 @@ constexpr int kSwzXor4 = 0x101F;  // bit-mask mode: and 0x1f, or 0, xor 4
 constexpr int kSwzXor8 = 0x201F;  // xor 8
 
 template <int G, int BITS, bool F32IN, int C>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(C == 1 ? 1024 : 512) __attribute__((amdgpu_waves_per_eu(2)))
 k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nteams, void *__restrict__ qv,
                float *__restrict__ tok_scale, int32_t *__restrict__ tok_rowsum) {
-    __shared__ double red_d[2][8];
-    __shared__ int red_i[2][8];
+    __shared__ double red_d[2][16];
+    __shared__ int red_i[2][16];
     constexpr int QMAX = BITS == 8 ? 127 : 7;
     constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
     constexpr int NW = F32IN ? 4 : 2;  // 16-byte words per 16-element chunk
@@ -543,10 +544,17 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
     }
 }
 
-// (C, W) for the row-team kernel, or false
-bool row_team_split(int64_t K, int &C, int &W) {
+// (C, W) for the row-team kernel, or false.  A few rows (M <= 64) take one chunk per lane and
+// up to 16 waves per row, so that they spread over many compute units and each wave's
+// transform is short; more rows take 2-4 chunks per lane and 1-8 waves per row.
+bool row_team_split(int64_t M, int64_t K, int &C, int &W) {
     if (K <= 0 || K % 1024) return false;
     const int64_t n = K / 1024;
+    if (M <= 64 && n <= 16) {
+        C = 1;
+        W = (int)n;
+        return true;
+    }
     for (int c : {3, 4, 2, 1}) {
         if (n % c) continue;
         const int64_t w = n / c;
@@ -662,7 +670,7 @@ hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int 
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st) {
     if (M == 0) return hipSuccess;
     int C = 0, W = 0;
-    if (row_team_split(K, C, W)) {
+    if (row_team_split(M, K, C, W)) {
 #define W4_RT(G, B, F) return launch_row<G, B, F>(X, M, K, C, W, q, tok_scale, tok_rowsum, st)
         if (g == 64) {
             if (bits == 8) { if (f32in) W4_RT(64, 8, true); else W4_RT(64, 8, false); }
