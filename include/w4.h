@@ -71,10 +71,13 @@ extern "C" {
 /* Low-rank side branch added before the bias: lr = (X . L1) . L2 with the UNROTATED
  * activations (ComfyUI-INT-Crush README, "Forward Pass" step 6 and "LoRA").
  *  x  : bf16 [M, K] unrotated layer input; read only when t == NULL
- *  l1 : bf16 [K, r]; read only when t == NULL
- *  t  : optional f32 [M, r] = x . l1 computed earlier (e.g. by w4_lowrank_down, and
+ *  l1 : bf16 [r, K], rank-major: row q holds the q-th down-projection vector over the K
+ *       inputs (L1 transposed; a LoRA down weight is stored this way); read only when
+ *       t == NULL
+ *  t  : optional f32 [M, r] = x . L1 computed earlier (e.g. by w4_lowrank_down, and
  *       shared by linears that read the same input); NULL -> computed into the workspace
- *  l2 : bf16 [r, N]
+ *  l2 : bf16 [r, N], rank-major: row q holds the q-th up-projection vector over the N
+ *       outputs
  *  r  : rank, 1 <= r <= 64 */
 typedef struct w4_lowrank {
     const void *x;
@@ -149,10 +152,11 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
               int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *ws,
               size_t ws_bytes, void *stream);
 
-/* w4_lowrank_down - t = x . l1, f32 [M, r], from bf16 x [M, K] and bf16 l1 [K, r]
- * (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of the low-rank
- *  residual).  Lets linears that read the same input share t.  1 <= r <= 64; K a multiple
- *  of 8 (W4_ERR_SHAPE otherwise).  Exact bf16 products, fp32 accumulation. */
+/* w4_lowrank_down - t = x . L1, f32 [M, r], from bf16 x [M, K] and bf16 l1 = L1 transposed,
+ * [r, K] rank-major (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of
+ * the low-rank residual).  Lets linears that read the same input share t.  1 <= r <= 64;
+ * K a multiple of 8 (W4_ERR_SHAPE otherwise); x, l1 and t 16-byte aligned.  Exact bf16
+ * products, fp32 accumulation. */
 int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t,
                     void *stream);
 

@@ -167,9 +167,10 @@ def w4_rotate_quant_act(X: torch.Tensor, g: int, act_bits: int):
 
 @dataclass
 class LowRank:
-    """Low-rank side branch (x . l1) . l2 on the unrotated input, added before the bias.
+    """Low-rank side branch (x . L1) . L2 on the unrotated input, added before the bias.
 
-    Give either ``t`` (f32 [M, r] = x . l1, e.g. from ``w4_lowrank_down``) or ``x`` and ``l1``."""
+    Both factors are rank-major: ``l1`` = L1 transposed, bf16 [r, K]; ``l2`` = L2, bf16 [r, N].
+    Give either ``t`` (f32 [M, r] = x . L1, e.g. from ``w4_lowrank_down``) or ``x`` and ``l1``."""
     l2: torch.Tensor
     x: Optional[torch.Tensor] = None
     l1: Optional[torch.Tensor] = None
@@ -265,12 +266,16 @@ def w4_linear(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,
 
 
 def w4_lowrank_down(x: torch.Tensor, l1: torch.Tensor) -> torch.Tensor:
-    """t = x . l1 (f32 [M, r]) for a low-rank branch, shareable by linears reading x."""
+    """t = x . L1 (f32 [M, r]) for a low-rank branch, shareable by linears reading x.
+
+    ``l1`` is L1 transposed, bf16 [r, K] (rank-major, like a LoRA down weight)."""
     lib = load_library()
     _dev(x, "x", (torch.bfloat16,))
     _dev(l1, "l1", (torch.bfloat16,))
     M, K = x.shape
-    r = l1.shape[1]
+    r = l1.shape[0]
+    if l1.dim() != 2 or l1.shape[1] != K:
+        raise ValueError("l1 has shape %s, expected [r, %d]" % (tuple(l1.shape), K))
     t = torch.empty((M, r), dtype=torch.float32, device=x.device)
     _check(lib.w4_lowrank_down(x.data_ptr(), l1.data_ptr(), M, K, r, t.data_ptr(), _stream(x.device)))
     return t

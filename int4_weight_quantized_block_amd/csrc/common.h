@@ -124,6 +124,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Wait until at most r * PER of this wave's loads are in flight (0 <= r <= RMAX).
+template <int PER, int RMAX>
+__device__ __forceinline__ void wait_rem(int r) {
+    if constexpr (RMAX == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (r >= RMAX) wait_vmcnt<(RMAX * PER < 63 ? RMAX * PER : 63)>();
+        else wait_rem<PER, RMAX - 1>(r);
+    }
+}
+
 // Unpack one packed dword (codes k .. k+7) to int8 values 16 * code in natural k order.
 __device__ __forceinline__ void unpack_nat(uint32_t d, uint32_t &lo, uint32_t &hi) {
     const uint32_t e = nib_evens16(d), o = nib_odds16(d);

@@ -375,17 +375,6 @@ SplitPlan plan_split(int64_t M, int64_t N, int64_t K, int act_bits) {
     return SplitPlan{};
 }
 
-// Wait until at most r * PER of this wave's loads are in flight (0 <= r <= RMAX).
-template <int PER, int RMAX>
-__device__ __forceinline__ void wait_rem(int r) {
-    if constexpr (RMAX == 0) {
-        wait_vmcnt<0>();
-    } else {
-        if (r >= RMAX) wait_vmcnt<(RMAX * PER < 63 ? RMAX * PER : 63)>();
-        else wait_rem<PER, RMAX - 1>(r);
-    }
-}
-
 // Per-wave layout: within each 2048-k stage wave w takes k in [512 w, 512 w + 512) and loads
 // exactly the bytes it multiplies (its token-code slices and its 256-byte piece of every
 // weight row) into its own LDS region, so the waves never wait for each other until the

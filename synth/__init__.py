@@ -19,7 +19,7 @@ text tokens, and text-encoder linears with hidden 4096):
                    1% of K outlier channels x30; g = 256, W4A8 asym (zero point).
 * ``double_block`` 20 blocks of {QKV 3072->9216, out 3072->3072, up 3072->12288,
                    down 12288->3072} at M = 4608, rank-32 low-rank side branch
-                   L1 [K, 32], L2 [32, N] ~N(0, 0.01); g = 256, W4A8 sym.
+                   L1 [K, 32] (stored rank-major, [32, K]), L2 [32, N] ~N(0, 0.01); g = 256, W4A8 sym.
 
 "N(0, s)" means standard deviation s.  Values are drawn in fp32 from NumPy's
 PCG64 and cast once to the stored dtype (bf16 casts round to nearest even), so
@@ -113,7 +113,8 @@ def linear_case(workload: str, linear: int, M: int, K: int, N: int, *, x_dtype=t
         "outliers": ch,
     }
     if rank:
-        out["L1"] = _to_torch(_normal(base + T_L1, (K, rank), 0.01), torch.bfloat16, device)
+        # L1 rank-major ([r, K], L1 transposed), as the low-rank calls take it
+        out["L1"] = _to_torch(np.ascontiguousarray(_normal(base + T_L1, (K, rank), 0.01).T), torch.bfloat16, device)
         out["L2"] = _to_torch(_normal(base + T_L2, (rank, N), 0.01), torch.bfloat16, device)
     return out
 
@@ -180,7 +181,7 @@ def double_block(b: int, device, M: int = DOUBLE_BLOCK_TOKENS, rank: int = LOWRA
     """Block ``b`` of the 20-block workload, drawn on ``device`` with torch's generator.
 
     Returns dict(x: block input [M, 3072], attn: out-proj input proxy [M, 3072],
-    and per linear name: W [N, K], bias [N], L1 [K, r], L2 [r, N])."""
+    and per linear name: W [N, K], bias [N], L1 [r, K] (rank-major, L1 transposed), L2 [r, N])."""
     base = 4000 + 100 * b
     K = DIT_HIDDEN
     out = {}
@@ -196,7 +197,7 @@ def double_block(b: int, device, M: int = DOUBLE_BLOCK_TOKENS, rank: int = LOWRA
         out[name] = {
             "W": _device_normal(s + T_W, (n, k), 0.02, device),
             "bias": _device_normal(s + T_BIAS, (n,), 0.01, device),
-            "L1": _device_normal(s + T_L1, (k, rank), 0.01, device),
+            "L1": _device_normal(s + T_L1, (k, rank), 0.01, device).t().contiguous(),  # rank-major [r, K]
             "L2": _device_normal(s + T_L2, (rank, n), 0.01, device),
         }
     return out

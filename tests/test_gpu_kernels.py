@@ -187,7 +187,7 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
     pw = ref["w"]
     Xd = X.to(DEV)
     args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
-    low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.to(DEV)) if lr else None
+    low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.t().contiguous().to(DEV)) if lr else None
     bias_d = bias.to(DEV) if bias is not None else None
     y = w4.w4_linear(Xd, g, bits, *args, bias=bias_d, lowrank=low)
     err = rel_frob(y, ref["y64"])
@@ -196,7 +196,7 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
     # the same through the cached half, with a precomputed low-rank t
     q, s, rs = w4.w4_rotate_quant_act(Xd, g, bits)
     if lr:
-        t = w4.w4_lowrank_down(Xd, L1.to(DEV))
+        t = w4.w4_lowrank_down(Xd, L1.t().contiguous().to(DEV))
         tref = oracle.to_f64(X) @ oracle.to_f64(L1)
         assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
         low = w4.LowRank(l2=L2.to(DEV), t=t)
@@ -226,7 +226,7 @@ def test_linear_lowrank_ranks(M, N, K, bits, asym, r):
     pw = ref["w"]
     Xd = X.to(DEV)
     args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
-    t = w4.w4_lowrank_down(Xd, L1.to(DEV))
+    t = w4.w4_lowrank_down(Xd, L1.t().contiguous().to(DEV))
     tref = oracle.to_f64(X) @ oracle.to_f64(L1)
     assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
     y = w4.w4_linear(Xd, g, bits, *args, lowrank=w4.LowRank(l2=L2.to(DEV), t=t))

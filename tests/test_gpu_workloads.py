@@ -83,7 +83,7 @@ def check_layer(X, W, bias, g, bits, asym, rows, lowrank=None, cache=None, tag="
     lr64 = None
     if lowrank is not None:
         L1, L2, low = lowrank
-        lr64 = oracle.lowrank(Xr, L1.cpu(), L2.cpu())
+        lr64 = oracle.lowrank(Xr, L1.cpu().t(), L2.cpu())  # L1 is held rank-major, [r, K]
     y = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, bias=bias.to(DEV), lowrank=low if lowrank else None)
     y64 = oracle.epilogue(acc_o, ra["scale"], pw["scale"], bias.cpu(), lr64)
     err = rel_frob(y[torch.as_tensor(sel).to(DEV)] if rows is not None else y, y64)
@@ -147,7 +147,7 @@ def test_double_block_cached_lowrank(b):
     p = blk["up"]
     say("oracle up-projection + low-rank for the down-proj input (all %d rows)" % M)
     ref_up = oracle.linear(blk["x"].cpu(), p["W"].cpu(), 256, 8, False, bias=p["bias"].cpu(),
-                           L1=p["L1"].cpu(), L2=p["L2"].cpu())
+                           L1=p["L1"].cpu().t(), L2=p["L2"].cpu())
     h = oracle.gelu_bf16(ref_up["y"]).to(DEV)
     p = blk["down"]
     low = w4.LowRank(l2=p["L2"], x=h, l1=p["L1"])
