@@ -15,9 +15,9 @@ The timed steps replay, back to back, a HIP graph holding the step's launches (o
 per input copy, captured once before timing; ``--eager`` times plain launches instead).
 
 Prints ONE JSON line.  ``roofline`` describes the dominant kernel, timed live with HIP
-events around its launches on the stream it runs on (an eager pass of the same K steps
-before the timed replays); ``cpu_baseline`` is the CPU oracle timed on this host's cores on
-a bounded sample of the same workload.
+events on the stream it runs on around K back-to-back launches of it (before the timed
+replays); ``cpu_baseline`` is the CPU oracle timed on this host's cores on a bounded sample
+of the same workload.
 
 Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
   attn_proj    (default) W4A8 g=256, X [4096, 3072] -> 3072           metric: TOPS
@@ -288,22 +288,31 @@ def main():
     torch.cuda.synchronize()
     log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
                                                                             args.warmup))
-    # per-launch durations: eager launches bracketed by events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # per-launch durations: each kernel launched K times back to back on the launch stream
+    # between two HIP events (the host enqueues faster than the kernels run, so the events
+    # see the kernels and the GPU's own launch gaps, not host time)
+    def per_launch(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e-3
+
+    t_rq = per_launch(rotquant)
+    t_mm = per_launch(gemm)
+    log("bench: rotate+quant %.2f us, GEMM %.2f us per launch" % (t_rq * 1e6, t_mm * 1e6))
+    # eager steps (both launches per step), timed as a whole
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
         rotquant(i)
-        ev[i][1].record(stream)
         gemm(i)
-        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
-    t_mm = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
-    log("bench: eager %.3f ms/step wall; rotate+quant %.2f us, GEMM %.2f us per launch" % (
-        wall / args.steps * 1e3, t_rq * 1e6, t_mm * 1e6))
+    log("bench: eager %.3f ms/step wall" % (wall / args.steps * 1e3))
     if not args.eager:
         # the timed steps: one HIP graph per input copy holding the step's two launches
         # (captured once, untimed), replayed back to back, so the GPU does not wait for the host
@@ -458,7 +467,9 @@ def bench_double_block(args, dev):
     roof = {"bound": "mfma", "achieved": g_ops / t_g / 1e12, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "k_gemm"
-    roof["traffic"] = None
+    roof["traffic"] = None  # four GEMM shapes per block: no single per-launch figure
+    if args.copy_calibration:
+        copy_calibration(dev)
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
