@@ -114,9 +114,10 @@ int w4_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int g, int
  *  tok_scale : out f32 [M]
  *  tok_rowsum: out int32 [M] = sum_k q[m, k] (used by the asymmetric-weight correction)
  * The rotation runs in fp64 (exact for bf16 inputs); codes equal rint(X'/s_x) up to the
- * last fp64 bit of the quotient.  Requires K % g == 0 and K/16 = C * T for some
- * C in 1..4 and T a multiple of g/16 with T <= 512 (every K used by DiT / text-encoder
- * linears qualifies); else W4_ERR_UNSUPPORTED. */
+ * last fp64 bit of the quotient.  Requires K % g == 0 and one of: K % 256 == 0 with
+ * K <= 32768 (K % 1024 == 0 takes the row-team kernel), or K/16 = C * T for some C in 1..4
+ * and T a multiple of g/16 with T <= 512 (every K used by DiT / text-encoder linears
+ * qualifies); else W4_ERR_UNSUPPORTED. */
 int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
                         void *q, float *tok_scale, int32_t *tok_rowsum, void *stream);
 
