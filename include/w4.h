@@ -134,9 +134,12 @@ int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g,
  *  Y         : out [M, N], bf16 for W4_OUT_BF16, int32 for W4_OUT_I32 (bias and lr unused)
  *  ws        : workspace, w4_workspace_bytes(M, N, K, act_bits, r_needed) bytes where
  *              r_needed = lr->r when lr && !lr->t, else 0.  It holds the low-rank t (first,
- *              required when r_needed > 0) and, for M <= 64, the int32 partial sums of the
- *              K-split small-M kernel (optional: with less room, or ws == NULL, the small-M
- *              path runs without splitting K).  Contents are scratch; nothing persists.
+ *              required when r_needed > 0) and then int32 partial sums: for M <= 64 those of
+ *              the K-split small-M kernel, for larger M those of the last partial round of
+ *              GEMM tiles when it is split along K (both optional: with less room, or
+ *              ws == NULL, the kernels run without splitting K; the results are the same,
+ *              bit for bit without a low-rank branch).  Contents are scratch; nothing
+ *              persists.
  * M <= 64 runs the HBM-streaming small-M kernels, larger M the MFMA GEMM. */
 int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *tok_rowsum,
                          int act_bits, const uint8_t *packed, const float *row_scale,
@@ -162,9 +165,11 @@ int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, 
                     void *stream);
 
 /* Workspace sizes in bytes (0 when nothing is needed).
- * w4_workspace_bytes: for w4_linear_cached_rot (the low-rank t when not supplied, and for
- * M <= 64 the K-split partial sums, S * M * N int32 with S in {2, 4, 8}, when the kernel
- * splits K for this shape).
+ * w4_workspace_bytes: for w4_linear_cached_rot (the low-rank t when not supplied, and the
+ * K-split partial sums when the kernels split K for this shape: for M <= 64, S * M * N int32
+ * with S in {2, 4, 8}; for larger M, when the 256 x 192 output tiles fill whole rounds of the
+ * compute units plus a tail of at most a quarter round, tail * S * 256 * 192 int32 with S in
+ * 4..8).
  * w4_linear_workspace_bytes: for w4_linear (activation codes, token scales and row sums,
  * plus the above).  Each piece is 256-byte aligned inside the workspace. */
 size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);

@@ -215,10 +215,31 @@ __device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc
 
 // Output forms, one kernel each (the epilogue is straight-line code run once per tile, so
 // leaving out what a launch does not need keeps it short)
-enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2 };
+// kEpiPartial: raw int32 partial tiles of one K range (the split tail, summed by k_gemm_tail)
+enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2, kEpiPartial = 3 };
+
+// The tiles one launch covers: ids [base, base + count); with kEpiPartial each tile is split
+// into kparts equal K ranges (one workgroup each) whose partial tiles go to part.
+struct TileRange {
+    int base, count, kparts;
+    int32_t *part;
+};
+
+// Tile id -> (tile row, tile column): ids walk M within groups of GN column tiles, so the
+// workgroups that share A and B panels run close together.
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int &tm, int &tn) {
+    constexpr int GN = 4;
+    const int gsize = GN * tiles_m;
+    const int grp = tile / gsize;
+    const int first_n = grp * GN;
+    const int gn = min(GN, tiles_n - first_n);
+    const int in = tile - grp * gsize;
+    tm = in / gn;
+    tn = first_n + in % gn;
+}
 
 template <int ABITS, bool ASYM, bool KTAIL, int EPI>
-__global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n, int l2_dma) {
+__global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n, int l2_dma, TileRange tr) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
     const int tid = threadIdx.x;
@@ -226,30 +247,30 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
     const int lr = lane & 31, kb = lane >> 5;
 
-    // ---- XCD-aware tile order: XCD x = blockIdx % 8 gets a contiguous run of tile ids, and
-    // tile ids walk M within groups of 4 column tiles.
-    const int ntiles = tiles_m * tiles_n;
-    int tile = blockIdx.x;
-    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
-    constexpr int GN = 4;
-    int tm, tn;
-    {
-        const int gsize = GN * tiles_m;
-        const int grp = tile / gsize;
-        const int first_n = grp * GN;
-        const int gn = min(GN, tiles_n - first_n);
-        const int in = tile - grp * gsize;
-        tm = in / gn;
-        tn = first_n + in % gn;
+    // ---- XCD-aware tile order: XCD x = blockIdx % 8 gets a contiguous run of tile ids
+    // (a split tail: consecutive workgroups are the K ranges of one tile)
+    int tile, kpart = 0;
+    if constexpr (EPI == kEpiPartial) {
+        tile = tr.base + (int)blockIdx.x / tr.kparts;
+        kpart = (int)blockIdx.x % tr.kparts;
+    } else {
+        tile = blockIdx.x;
+        if (tr.count % 8 == 0) tile = (blockIdx.x % 8) * (tr.count / 8) + blockIdx.x / 8;
+        tile += tr.base;
     }
+    int tm, tn;
+    tile_coords(tile, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t K = p.K;
-    const int nk = (int)((K + BK - 1) / BK);  // the last stage holds 64 valid k when KTAIL
+    // stages of this workgroup (the last holds 64 valid k when KTAIL); a K range of a split
+    // tail starts ks0 stages in (K % BK == 0 there)
+    const int nk = EPI == kEpiPartial ? (int)(K / BK) / tr.kparts : (int)((K + BK - 1) / BK);
+    const int ks0 = EPI == kEpiPartial ? kpart * nk : 0;
 
     // ---- the tile's per-feature constants go to LDS with the same direct loads (ahead of the
     // pipeline's loads, so the first stage's wait covers them); per-lane token constants go to
     // registers and are first used in the epilogue.
-    if (wave == 0) {
+    if (EPI != kEpiPartial && wave == 0) {
         const uint32_t cb = lds_addr(smem);
 #pragma unroll
         for (int q = 0; q < BN / 64; ++q) {
@@ -302,8 +323,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int64_t m = min<int64_t>(m0 + wm * WTM + i * 32 + lr, p.M - 1);
-        sxv[i] = p.sx[m];
-        rsv[i] = ASYM ? p.rowsum[m] : 0;
+        sxv[i] = EPI == kEpiPartial ? 0.0f : p.sx[m];
+        rsv[i] = ASYM && EPI != kEpiPartial ? p.rowsum[m] : 0;
     }
 
     // ---- per-lane DMA byte offsets relative to the tile's row panel (rows clamped: rows >= M
@@ -334,8 +355,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         chB[i] = c;
         offB[i] = (uint32_t)(rc * (K / 2) + 16 * c);
     }
-    const uint8_t *panelA = p.A + m0 * rowbA;
-    const uint8_t *panelB = p.B + n0 * (K / 2);
+    const uint8_t *panelA = p.A + m0 * rowbA + (int64_t)ks0 * L::A_ROW;
+    const uint8_t *panelB = p.B + n0 * (K / 2) + (int64_t)ks0 * L::B_ROW;
     const uint32_t smem_base = lds_addr(smem);
     // Load number idx of stage kt (into ring slot `slot`); in a 64-wide last stage the chunks
     // past K re-read chunk 0 of the same row and stage (in bounds; that half is never
@@ -418,6 +439,22 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         half_stage<ABITS, ASYM, false, false>(fa, oa, fb, ob, nullptr, 0, wm, wn, lr, kb, acc, load_one, 0, 0);
     }
 
+    if constexpr (EPI == kEpiPartial) {
+        // raw accumulators of this K range: lane l holds features 4 consecutive n of token
+        // l % 32 per register group (the layout described below), stored as 16-byte pieces
+        int32_t *P = tr.part + ((int64_t)(tile - tr.base) * tr.kparts + kpart) * (BM * BN);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int ml = wm * WTM + i * 32 + lr, nl = wn * WTN + j * 32 + 8 * g + 4 * kb;
+                    *reinterpret_cast<int4 *>(P + ml * BN + nl) =
+                        make_int4(acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]);
+                }
+        return;
+    }
     // ---- epilogue.  32x32 block layout: lane l, register v holds output feature
     // n = 8 * (v / 4) + 4 * (l / 32) + v % 4 of token m = l % 32, so registers 4g .. 4g+3 are
     // four consecutive features of one token.  Each wave finishes on its own (no workgroup
@@ -566,8 +603,106 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     }
 }
 
+// ---- split tail: the last partial round of tiles (fewer tiles than compute units) runs as
+// S K ranges per tile, and this kernel sums the S int32 partials (exact, fixed order) and
+// applies the epilogue of k_gemm (the same arithmetic; the low-rank term on the VALU).
+// One thread per 4 consecutive outputs of a tile.
+template <int ABITS, bool ASYM>
+__global__ void __launch_bounds__(256) k_gemm_tail(LinearArgs p, int tiles_m, int tiles_n, TileRange tr) {
+    constexpr int SHIFT = ABITS == 8 ? 4 : 8;
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    constexpr int PER_TILE = BM * BN / 4 / 256;  // workgroups per tile
+    const int t = (int)blockIdx.x / PER_TILE;
+    const int idx = ((int)blockIdx.x % PER_TILE) * 256 + (int)threadIdx.x;
+    const int ml = idx / (BN / 4), nl = 4 * (idx % (BN / 4));
+    int tm, tn;
+    tile_coords(tr.base + t, tiles_m, tiles_n, tm, tn);
+    const int64_t m = (int64_t)tm * BM + ml, n = (int64_t)tn * BN + nl;
+    if (m >= p.M || n >= p.N) return;
+    const int32_t *P = tr.part + (int64_t)t * tr.kparts * (BM * BN) + ml * BN + nl;
+    int4 s = *reinterpret_cast<const int4 *>(P);
+    for (int q = 1; q < tr.kparts; ++q) {
+        const int4 v = *reinterpret_cast<const int4 *>(P + (int64_t)q * (BM * BN));
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    int a[4] = {s.x, s.y, s.z, s.w};
+    const int nv = (int)min<int64_t>(4, p.N - n);
+    if constexpr (ASYM) {
+        const int rs = p.rowsum[m];
+        for (int r = 0; r < nv; ++r) a[r] += ((8 - (int)p.zp[n + r]) << SHIFT) * rs;
+    }
+    if (p.y_i32) {
+        int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N + n;
+        for (int r = 0; r < nv; ++r) Y[r] = a[r] >> SHIFT;
+        return;
+    }
+    // low-rank term of the 4 outputs: independent loads per rank (unrolled, so many are in
+    // flight), 8-byte l2 reads when the rows allow it
+    float lw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.lr_t) {
+        const float *tm_ = p.lr_t + m * p.lr_r;
+        const uint16_t *l2 = p.lr_l2 + n;
+        if (nv == 4 && (p.N & 3) == 0) {
+#pragma unroll 8
+            for (int q = 0; q < p.lr_r; ++q) {
+                const float tq = tm_[q];
+                const uint2 w = *reinterpret_cast<const uint2 *>(l2 + (int64_t)q * p.N);
+                lw[0] = fmaf(tq, bf16_lo(w.x), lw[0]);
+                lw[1] = fmaf(tq, bf16_hi(w.x), lw[1]);
+                lw[2] = fmaf(tq, bf16_lo(w.y), lw[2]);
+                lw[3] = fmaf(tq, bf16_hi(w.y), lw[3]);
+            }
+        } else {
+            for (int r = 0; r < nv; ++r)
+#pragma unroll 8
+                for (int q = 0; q < p.lr_r; ++q) lw[r] = fmaf(tm_[q], bf16_to_f32(l2[(int64_t)q * p.N + r]), lw[r]);
+        }
+    }
+    const float sx = p.sx[m];
+    uint32_t h[4] = {0, 0, 0, 0};
+    for (int r = 0; r < nv; ++r) {
+        const float sw = p.sw[n + r] * kUnscale;
+        const float b = !p.bias ? 0.0f
+                        : p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n + r])
+                                      : reinterpret_cast<const float *>(p.bias)[n + r];
+        h[r] = f32_to_bf16(fmaf((float)a[r], sx * sw, b) + lw[r]);
+    }
+    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N + n;
+    if (nv == 4 && (p.N & 3) == 0) {
+        *reinterpret_cast<uint2 *>(Y) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    } else {
+        for (int r = 0; r < nv; ++r) Y[r] = (uint16_t)h[r];
+    }
+}
+
+// Tiles in whole rounds over the compute units (tmain) and the tail split into S K ranges,
+// S the largest of 8 .. 4 that divides the stage count with ttail * S <= units; S = 1: no
+// split (at most one round, K % BK != 0, or a tail of more than a quarter round: there the
+// partial sums' extra traffic and the summing launch cost more than the idle units; measured
+// on the 20-block workload: a tail of 32 tiles gains, tails of 96 and 128 lose).
+struct TailPlan {
+    int tmain, ttail, S;
+};
+
+TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
+    const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    TailPlan pl{tiles, 0, 1};
+    if (K % BK || tiles <= ncu) return pl;
+    const int tmain = tiles / ncu * ncu, ttail = tiles - tmain, nk = (int)(K / BK);
+    if (ttail == 0) return pl;
+    for (int S = std::min(8, ncu / ttail); S >= 4; --S) {
+        if (nk % S == 0) return TailPlan{tmain, ttail, S};
+    }
+    return pl;
+}
+
 template <int ABITS, bool ASYM, bool KTAIL, int EPI>
-hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
+hipError_t launch_t(const LinearArgs &a, const TileRange &tr, unsigned grid, hipStream_t st) {
     // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
     // 24 * r 16-byte chunks, at most 24 KB for r <= 64)
     constexpr size_t base = Lay<ABITS>::LDS_BYTES, maxl2 = 24 * 1024;
@@ -578,30 +713,50 @@ hipError_t launch_t(const LinearArgs &a, hipStream_t st) {
     const int l2_dma = a.N % 8 == 0;
     const size_t lds = base + (EPI == kEpiLowRank ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3((unsigned)(tm * tn)), dim3(kThreads), lds, st, a, tm, tn,
-                       l2_dma);
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, a, tm, tn, l2_dma, tr);
     return hipGetLastError();
 }
 
+template <int ABITS, bool ASYM, bool KTAIL>
+hipError_t launch_epi(const LinearArgs &a, const TileRange &tr, hipStream_t st) {
+    const unsigned grid = (unsigned)tr.count;
+    if (a.y_i32) return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(a, tr, grid, st);
+    if (a.lr_t) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(a, tr, grid, st);
+    return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(a, tr, grid, st);
+}
+
 template <int ABITS, bool ASYM>
-hipError_t launch_k(const LinearArgs &a, hipStream_t st) {
-    const int epi = a.y_i32 ? kEpiI32 : a.lr_t ? kEpiLowRank : kEpiBf16;
-    if (a.K % BK) {
-        if (epi == kEpiI32) return launch_t<ABITS, ASYM, true, kEpiI32>(a, st);
-        if (epi == kEpiLowRank) return launch_t<ABITS, ASYM, true, kEpiLowRank>(a, st);
-        return launch_t<ABITS, ASYM, true, kEpiBf16>(a, st);
-    }
-    if (epi == kEpiI32) return launch_t<ABITS, ASYM, false, kEpiI32>(a, st);
-    if (epi == kEpiLowRank) return launch_t<ABITS, ASYM, false, kEpiLowRank>(a, st);
-    return launch_t<ABITS, ASYM, false, kEpiBf16>(a, st);
+hipError_t launch_k(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t st) {
+    const TailPlan pl = tail_plan(a.M, a.N, a.K);
+    const int tiles = pl.tmain + pl.ttail;
+    const size_t need = (size_t)pl.ttail * pl.S * BM * BN * sizeof(int32_t);
+    const TileRange all{0, tiles, 1, nullptr};
+    if (a.K % BK) return launch_epi<ABITS, ASYM, true>(a, all, st);
+    if (pl.S < 2 || !ws || ws_bytes < need) return launch_epi<ABITS, ASYM, false>(a, all, st);
+    // whole rounds, then the tail's K ranges, then their sum and epilogue
+    hipError_t e = launch_epi<ABITS, ASYM, false>(a, TileRange{0, pl.tmain, 1, nullptr}, st);
+    if (e != hipSuccess) return e;
+    const TileRange tail{pl.tmain, pl.ttail, pl.S, static_cast<int32_t *>(ws)};
+    e = launch_t<ABITS, ASYM, false, kEpiPartial>(a, tail, (unsigned)(pl.ttail * pl.S), st);
+    if (e != hipSuccess) return e;
+    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_gemm_tail<ABITS, ASYM>), dim3((unsigned)(pl.ttail * (BM * BN / 4 / 256))), dim3(256), 0, st,
+                       a, tm, tn, tail);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const LinearArgs &a, int act_bits, hipStream_t st) {
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 64 || N <= 0 || K <= 0) return 0;
+    const TailPlan pl = tail_plan(M, N, K);
+    return pl.S > 1 ? (size_t)pl.ttail * pl.S * BM * BN * sizeof(int32_t) : 0;
+}
+
+hipError_t launch_gemm(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st) {
     if (a.M == 0) return hipSuccess;
-    if (act_bits == 8) return a.zp ? launch_k<8, true>(a, st) : launch_k<8, false>(a, st);
-    return a.zp ? launch_k<4, true>(a, st) : launch_k<4, false>(a, st);
+    if (act_bits == 8) return a.zp ? launch_k<8, true>(a, ws, ws_bytes, st) : launch_k<8, false>(a, ws, ws_bytes, st);
+    return a.zp ? launch_k<4, true>(a, ws, ws_bytes, st) : launch_k<4, false>(a, ws, ws_bytes, st);
 }
 
 }  // namespace w4

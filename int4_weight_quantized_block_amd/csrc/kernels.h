@@ -33,7 +33,10 @@ struct LinearArgs {
     int64_t M, N, K;
 };
 
-hipError_t launch_gemm(const LinearArgs &a, int act_bits, hipStream_t st);
+// Large-M path (M > 64).  With a workspace of gemm_workspace_bytes() bytes (0 when the tiles
+// fill whole rounds of the compute units) the last partial round is split along K.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
 // Small-M path (M <= 64).  With a workspace of gemv_workspace_bytes() bytes (0 when none is
 // needed) the K-split kernel runs; without one, the LDS-ring kernel.
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits);

@@ -90,7 +90,9 @@ const char *w4_status_string(int status) {
 size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r) {
     if (M <= 0) return 0;
     const size_t t = r > 0 ? align256((size_t)M * (size_t)r * sizeof(float)) : 0;
-    const size_t part = M <= 64 && N > 0 && K > 0 ? align256(w4::gemv_workspace_bytes(M, N, K, act_bits)) : 0;
+    const size_t part = N <= 0 || K <= 0 ? 0
+                        : M <= 64      ? align256(w4::gemv_workspace_bytes(M, N, K, act_bits))
+                                       : align256(w4::gemm_workspace_bytes(M, N, K));
     return t + part;
 }
 
@@ -216,10 +218,12 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     a.M = M;
     a.N = N;
     a.K = K;
-    // the rest of the workspace (if any) holds the small-M path's K-split partial sums
+    // the rest of the workspace (if any) holds the K-split partial sums (small-M path, or the
+    // last partial round of tiles of the large-M path)
     void *gws = ws ? static_cast<uint8_t *>(ws) + tbytes : nullptr;
     const size_t gbytes = ws ? ws_bytes - tbytes : 0;
-    hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, gws, gbytes, st) : w4::launch_gemm(a, act_bits, st);
+    hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, gws, gbytes, st)
+                           : w4::launch_gemm(a, act_bits, gws, gbytes, st);
     return hip_status(e, fn);
 }
 

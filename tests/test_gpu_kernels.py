@@ -233,3 +233,39 @@ def test_linear_lowrank_ranks(M, N, K, bits, asym, r):
     err = rel_frob(y, ref["y64"])
     say("  rel frob %.3e" % err)
     assert err <= FROB_TOL
+
+
+@pytest.mark.parametrize("M,N,K,bits,asym", [(4608, 3072, 3072, 4, True), (4608, 2880, 2048, 8, False),
+                                             (2500, 5996, 1024, 8, True)])
+def test_gemm_split_tail_equals_single_pass(M, N, K, bits, asym):
+    """More tiles than compute units: the last partial round runs as K ranges plus a sum and
+    epilogue kernel (given the workspace).  The int32 outputs equal the single-pass kernel's
+    bit for bit, the bf16 outputs too without a low-rank branch (same epilogue arithmetic) and
+    within the bar with one (VALU instead of MFMA for T . L2)."""
+    say("split tail M=%d N=%d K=%d bits=%d asym=%s" % (M, N, K, bits, asym))
+    g = torch.Generator(device=DEV).manual_seed(M + N + K)
+    X = torch.randn(M, K, generator=g, device=DEV).to(torch.bfloat16)
+    W = (torch.randn(N, K, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    bias = (torch.randn(N, generator=g, device=DEV) * 0.01).to(torch.bfloat16)
+    L1t = (torch.randn(16, K, generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    L2 = (torch.randn(16, N, generator=g, device=DEV) * 0.2).to(torch.bfloat16)
+    packed, s_w, zp = w4.w4_pack_weights(W, 256, asym)
+    q, sx, rs = w4.w4_rotate_quant_act(X, 256, bits)
+    L = w4.load_library()
+    need = L.w4_workspace_bytes(M, N, K, bits, 0)
+    assert need > 0, "shape must have a split tail"
+    tiny = torch.empty(256, dtype=torch.uint8, device=DEV)   # too small: single pass
+    big = torch.empty(need, dtype=torch.uint8, device=DEV)
+    a1 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, out_i32=True, ws=big)
+    a0 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, out_i32=True, ws=tiny)
+    assert torch.equal(a1, a0)
+    y1 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, bias=bias, ws=big)
+    y0 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, bias=bias, ws=tiny)
+    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
+    t = w4.w4_lowrank_down(X, L1t)
+    low = w4.LowRank(l2=L2, t=t)
+    y1 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, bias=bias, lowrank=low, ws=big)
+    y0 = w4.w4_linear_cached_rot(q, sx, rs, bits, packed, s_w, zp, bias=bias, lowrank=low, ws=tiny)
+    err = (y1.float() - y0.float()).norm() / y0.float().norm()
+    say("  low-rank split vs single pass rel frob %.3e" % err.item())
+    assert err.item() <= FROB_TOL
