@@ -67,6 +67,13 @@ def test_workspace_sizes(lib):
     assert lib.w4_linear_workspace_bytes(100, 8, 256, 8, 0) == 25600 + 512 + 512
     assert lib.w4_linear_workspace_bytes(100, 8, 256, 4, 0) == 12800 + 512 + 512
     assert lib.w4_linear_workspace_bytes(100, 8, 256, 8, 32) == 25600 + 1024 + 12800
+    # large M: partial sums only when the 256 x 192 tiles leave a tail of at most a quarter
+    # round of the 256 compute units (the count this host reports when it has no GPU)
+    tile = 256 * 192 * 4
+    assert lib.w4_workspace_bytes(4096, 3072, 3072, 8, 0) == 0            # 256 tiles: whole rounds
+    assert lib.w4_workspace_bytes(4608, 3072, 3072, 8, 0) == 32 * 8 * tile  # 288 = 256 + 32, 8 K ranges
+    assert lib.w4_workspace_bytes(4608, 9216, 3072, 8, 0) == 0            # tail of 96: one pass
+    assert lib.w4_workspace_bytes(4608, 3072, 3008, 8, 0) == 0            # K % 128 != 0: one pass
 
 
 def pack(lib, W=A, dt=w4.W4_BF16, N=8, K=256, g=64, mode=w4.W4_SYM, packed=A, scale=A, zp=None):
