@@ -16,7 +16,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("M,N,K,bits", [(300, 384, 1024, 8), (40, 256, 3072, 4), (8, 512, 4096, 8)])
+@pytest.mark.parametrize("M,N,K,bits", [(300, 384, 1024, 8), (40, 256, 3072, 4), (8, 512, 4096, 8),
+                                         (4608, 3072, 3072, 8)])  # the last: split tail (3 launches)
 def test_graph_replay_matches_eager(M, N, K, bits):
     say("graph replay M=%d N=%d K=%d bits=%d" % (M, N, K, bits))
     g = torch.Generator().manual_seed(M + N + K)
