@@ -26,6 +26,8 @@ Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
   small_m      asym W4A8 g=256, M in {1,4,16,64}, K/N 4096/12288     metric: weight GB/s
   double_block 20 blocks x {QKV, out, up, down} at M=4608, cached    metric: TOPS
   tiny         W4A8 g=64, 16 x 256 -> 256                            metric: TOPS
+  mfma_peak    the library's int8 MFMA rate probe (not a layer): the chip's sustained
+               dense int8 rate with random and with constant operands
 """
 import argparse
 import hashlib
@@ -54,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="attn_proj",
-                    choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny"])
+                    choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny", "mfma_peak"])
     ap.add_argument("--M", type=int, default=None, help="tokens (small_m: 1, 4, 16 or 64)")
     ap.add_argument("--K", type=int, default=12288, help="small_m: input features (4096 or 12288)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -243,6 +245,8 @@ def main():
 
     if args.workload == "double_block":
         return bench_double_block(args, dev)
+    if args.workload == "mfma_peak":
+        return bench_mfma_peak(args, dev)
 
     layer_specs, cfg = build_workload(args, dev)
     name, X, W, bias, g, bits, asym = layer_specs[0][0]
@@ -396,6 +400,47 @@ def measured_traffic(kernel, cfg):
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["sha256"]:
         return None  # the kernel changed since the counters were taken
     return ent["bytes"]
+
+
+def bench_mfma_peak(args, dev):
+    """The chip's sustained dense int8 MFMA rate: the library's probe (back-to-back
+    v_mfma_i32_32x32x32_i8, eight waves per SIMD) with pseudo-random and with constant
+    operands, K launches each between HIP events.  Not a step of the layer: it measures the
+    ceiling the GEMM's roofline fraction should be read against."""
+    import torch
+    import int4_weight_quantized_block_amd as w4
+    L = w4.load_library()
+    blocks, iters = 256 * 8, 4000
+    ops = blocks * 4.0 * iters * 4 * 2 * 32 ** 3
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream(dev)
+    rate = {}
+    for rnd in (0, 1):
+        for _ in range(2):
+            w4._check(L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(args.steps):
+            w4._check(L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream))
+        e1.record(st)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / args.steps * 1e-3
+        rate[rnd] = ops / t / 1e12
+        log("bench: probe %s operands: %.1f TOPS (%.3f ms per launch)" % ("random" if rnd else "constant", rate[rnd],
+                                                                          t * 1e3))
+    roof = {"bound": "mfma", "achieved": rate[1], "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+            "frac": rate[1] / PEAK_INT8_TOPS, "kernel": "k_mfma_rate", "traffic": None}
+    out = {
+        "metric": "sustained dense int8 MFMA rate (probe, random operands)", "value": round(rate[1], 1),
+        "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": 2, "ms_per_step": round(ops / rate[1] / 1e9, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "mfma_peak", "blocks": blocks, "iters_per_wave": iters,
+                   "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": None,
+        "detail": {"constant_operands_tops": round(rate[0], 1), "random_operands_tops": round(rate[1], 1)},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_double_block(args, dev):

@@ -27,7 +27,7 @@ __all__ = [
     "w4_linear_cached_rot", "w4_linear", "w4_lowrank_down", "w4_workspace_bytes",
     "w4_linear_workspace_bytes", "LowRank", "RotationCache", "W4_OK", "W4_ERR_INVALID_ARG",
     "W4_ERR_SHAPE", "W4_ERR_UNSUPPORTED", "W4_ERR_ALIGN", "W4_ERR_HIP", "W4_ERR_WORKSPACE",
-    "W4_MAX_K", "EXPORTS",
+    "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate",
 ]
 
 W4_OK, W4_ERR_INVALID_ARG, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_HIP, \
@@ -71,6 +71,7 @@ EXPORTS = {
     "w4_status_string": (ctypes.c_char_p, [_I]),
     "w4_last_error": (ctypes.c_char_p, []),
     "w4_version": (ctypes.c_char_p, []),
+    "w4_probe_mfma_rate": (_I, [_I64, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -279,6 +280,16 @@ def w4_lowrank_down(x: torch.Tensor, l1: torch.Tensor) -> torch.Tensor:
     t = torch.empty((M, r), dtype=torch.float32, device=x.device)
     _check(lib.w4_lowrank_down(x.data_ptr(), l1.data_ptr(), M, K, r, t.data_ptr(), _stream(x.device)))
     return t
+
+
+def w4_probe_mfma_rate(blocks: int, iters: int, random_operands: bool, device="cuda") -> torch.Tensor:
+    """Launch the int8 MFMA rate probe (a measurement tool, not a step of the layer) on the
+    current stream; returns the checksum tensor it writes.  Work: blocks * 4 * iters * 4 *
+    2 * 32**3 int ops."""
+    lib = load_library()
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=device)
+    _check(lib.w4_probe_mfma_rate(blocks, iters, 1 if random_operands else 0, sink.data_ptr(), _stream(sink.device)))
+    return sink
 
 
 class RotationCache:

@@ -146,6 +146,12 @@ def test_linear_validation(lib):
     assert lin(M=0, ws=None) == w4.W4_OK
 
 
+def test_probe_validation(lib):
+    assert lib.w4_probe_mfma_rate(0, 10, 1, A, None) == w4.W4_ERR_INVALID_ARG
+    assert lib.w4_probe_mfma_rate(8, 0, 1, A, None) == w4.W4_ERR_INVALID_ARG
+    assert lib.w4_probe_mfma_rate(8, 10, 1, None, None) == w4.W4_ERR_INVALID_ARG
+
+
 def test_error_message_is_per_thread(lib):
     import threading
     assert pack(lib, g=128) == w4.W4_ERR_UNSUPPORTED
