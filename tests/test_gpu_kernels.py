@@ -43,6 +43,7 @@ def act_input(M, K, seed, dtype=torch.bfloat16, n_out=None, scale=30.0):
     (16, 128, 256, 8, False), (1, 64, 256, 8, True), (5, 48, 320, 8, False), (64, 256, 512, 4, False),
     (33, 272, 1024, 4, True), (128, 128, 256, 8, False), (200, 136, 448, 8, True), (300, 520, 3072, 4, False),
     (257, 256, 4096, 8, False), (130, 1000, 192, 4, True), (65, 17, 64, 8, False),
+    (70, 64, 32768, 8, True), (8, 96, 32768, 4, False),   # K = W4_MAX_K, both paths
 ])
 def test_accumulators_bit_exact_on_oracle_codes(M, N, K, bits, asym):
     """acc[m, n] = sum_k q (c - z) from the oracle's own codes, through W4_OUT_I32."""
@@ -66,6 +67,31 @@ def test_accumulators_bit_exact_on_oracle_codes(M, N, K, bits, asym):
     bad = np.argwhere(got != acc)
     assert bad.size == 0, "first mismatches %s: gpu %s oracle %s" % (
         bad[:4].tolist(), got[tuple(bad[:4].T)].tolist(), acc[tuple(bad[:4].T)].tolist())
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_accumulators_extreme_asym_max_k(bits):
+    """The largest accumulators the kernels form: asymmetric weights (codes 15, zero point 0)
+    against the most negative activation code at K = W4_MAX_K.  The kernels scale the
+    operands by 16 (int8) or 256 (int4) and add (8 - z) * rowsum separately, so their int32
+    intermediates reach about 1.0e9; the result must still be exact (GEMM and small-M)."""
+    say("acc extreme asym bits=%d" % bits)
+    N, K = 64, 32768
+    qmin = -128 if bits == 8 else -8
+    for M in (80, 8):
+        q = np.full((M, K), qmin, np.int8)
+        q[1::2] = 127 if bits == 8 else 7
+        codes = np.full((N, K), 15)
+        codes[1::2] = 0
+        zp = np.zeros(N, np.uint8)
+        zp[1::2] = 15
+        packed = oracle.pack_nibbles(codes)
+        acc = oracle.gemm_i64(q, oracle.weight_operand(packed, zp, True))
+        qa = q if bits == 8 else oracle.pack_nibbles(q)
+        y = w4.w4_linear_cached_rot(to_dev(qa), to_dev(np.ones(M, np.float32)),
+                                    to_dev(q.astype(np.int64).sum(1).astype(np.int32)), bits, to_dev(packed),
+                                    to_dev(np.ones(N, np.float32)), to_dev(zp), out_i32=True)
+        assert np.array_equal(np_(y).astype(np.int64), acc)
 
 
 def test_accumulators_extreme_codes():
