@@ -450,8 +450,13 @@ def bench_double_block(args, dev):
     nb = synth.N_BLOCKS
     M = args.M or synth.DOUBLE_BLOCK_TOKENS
     blocks = []
+    cpu_block = None  # block 0's inputs on the host, for the CPU oracle baseline
     for b in range(nb):
         blk = synth.double_block(b, dev, M=M)
+        if b == 0 and not args.no_cpu_baseline:
+            cpu_block = {"x": blk["x"].cpu(), "attn": blk["attn"].cpu()}
+            for name, _, _ in synth.DOUBLE_BLOCK_LINEARS:
+                cpu_block[name] = {key: blk[name][key].cpu() for key in ("W", "bias", "L1", "L2")}
         lins = {}
         for name, k, n in synth.DOUBLE_BLOCK_LINEARS:
             p = blk[name]
@@ -538,7 +543,42 @@ def bench_double_block(args, dev):
                    "lowrank": synth.LOWRANK, "parallelism": "single-gpu"},
         "roofline": roof, "cpu_baseline": None,
     }
+    if cpu_block is not None:
+        rows = args.cpu_rows or 3072
+        log("bench: timing the CPU oracle on block 0, %d rows" % rows)
+        out["cpu_baseline"] = cpu_baseline_block(cpu_block, rows, M, nb)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_block(blk, rows, M, nb):
+    """The oracle as it stands on this host's cores over the first ``rows`` token rows of
+    block 0: the same step as the GPU's (rotation shared by QKV and MLP-up, low-rank branch
+    on every linear, host GELU between the MLP linears); rows are independent, so the rate
+    extrapolates to the whole workload.  Weight packing is done before timing."""
+    import oracle
+    import synth
+    pw = {name: oracle.pack_weights(blk[name]["W"], 256, False) for name, _, _ in synth.DOUBLE_BLOCK_LINEARS}
+    x, attn = blk["x"][:rows], blk["attn"][:rows]
+
+    def lin(name, inp, qa):
+        p = blk[name]
+        lr = oracle.lowrank(inp, p["L1"].t(), p["L2"])  # L1 is held rank-major, [r, K]
+        return oracle.linear_from_codes(qa["q"], qa["scale"], pw[name]["packed"], pw[name]["scale"], None, False,
+                                        p["bias"], lr)
+
+    t1 = time.perf_counter()
+    qx = oracle.rotate_quant_act(x, 256, 8)  # shared by QKV and MLP-up
+    lin("qkv", x, qx)
+    up = lin("up", x, qx)
+    lin("out", attn, oracle.rotate_quant_act(attn, 256, 8))
+    h = oracle.gelu_bf16(up["y"])
+    lin("down", h, oracle.rotate_quant_act(h, 256, 8))
+    sec = time.perf_counter() - t1
+    ops = sum(2.0 * rows * k * n for _, k, n in synth.DOUBLE_BLOCK_LINEARS)
+    return {"cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "block 0 of %d: %d of %d token rows, all four linears with the rotation cache, low-rank "
+                      "branches and GELU (rate extrapolates: rows and blocks are independent)" % (nb, rows, M),
+            "seconds": round(sec, 3), "value": round(ops / sec / 1e12, 6), "unit": "TOPS"}
 
 
 if __name__ == "__main__":
