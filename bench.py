@@ -292,21 +292,36 @@ def main():
     torch.cuda.synchronize()
     log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
                                                                             args.warmup))
-    # per-launch durations: each kernel launched K times back to back on the launch stream
-    # between two HIP events (the host enqueues faster than the kernels run, so the events
-    # see the kernels and the GPU's own launch gaps, not host time)
-    def per_launch(fn):
+    # per-launch durations: each kernel launched K times back to back between two HIP events.
+    # The K launches are captured once in a HIP graph and the replay is timed, so the events
+    # see the kernels and the GPU's own launch gaps, not the host's per-call cost (a ctypes
+    # call takes longer than a small-M kernel runs); --eager times plain launches instead.
+    def per_launch(f, argl):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.eager:
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.steps):
+                w4._check(f(*argl[i % ncopy]))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps * 1e-3
+        side = torch.cuda.Stream()
+        gk = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gk, stream=side):
+            sk = torch.cuda.current_stream().cuda_stream
+            for i in range(args.steps):
+                w4._check(f(*(argl[i % ncopy][:-1] + (sk,))))
+        gk.replay()
         torch.cuda.synchronize()
         e0.record(stream)
-        for i in range(args.steps):
-            fn(i)
+        gk.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps * 1e-3
 
-    t_rq = per_launch(rotquant)
-    t_mm = per_launch(gemm)
+    t_rq = per_launch(f_rq, rq_args)
+    t_mm = per_launch(f_mm, mm_args)
     log("bench: rotate+quant %.2f us, GEMM %.2f us per launch" % (t_rq * 1e6, t_mm * 1e6))
     # eager steps (both launches per step), timed as a whole
     torch.cuda.synchronize()

@@ -124,14 +124,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Wait until at most r * PER of this wave's loads are in flight (0 <= r <= RMAX).
-template <int PER, int RMAX>
+// Wait until at most r * PER + EXTRA of this wave's loads are in flight (0 <= r <= RMAX).
+template <int PER, int RMAX, int EXTRA = 0>
 __device__ __forceinline__ void wait_rem(int r) {
     if constexpr (RMAX == 0) {
-        wait_vmcnt<0>();
+        wait_vmcnt<EXTRA>();
     } else {
-        if (r >= RMAX) wait_vmcnt<(RMAX * PER < 63 ? RMAX * PER : 63)>();
-        else wait_rem<PER, RMAX - 1>(r);
+        if (r >= RMAX) wait_vmcnt<(RMAX * PER + EXTRA < 63 ? RMAX * PER + EXTRA : 63)>();
+        else wait_rem<PER, RMAX - 1, EXTRA>(r);
     }
 }
 

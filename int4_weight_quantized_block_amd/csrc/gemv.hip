@@ -713,45 +713,56 @@ hipError_t split_mb(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hip
 
 // ---------------------------------------------------------------------------------------
 // Streaming path for M <= 16 (no workspace, one pass over K): every wave streams its own
-// slices through its own LDS ring.  In each 1024-k stage wave w takes k in [256 w, 256 w +
-// 256): it loads its 256-byte (int8) or 128-byte (int4) slice of each staged token and its
-// 128-byte piece of each of the workgroup's R weight rows (8 rows x 128 bytes per 1 KB
-// load), D stages ahead, and multiplies a stage as soon as its own loads have landed; no
-// workgroup barrier until the final reduction.  The ring keeps D stages per wave in flight
-// instead of the whole stream, so the wave alternates between issuing and multiplying.
-constexpr int KST = 1024;         // k per stage of the streaming kernel (256 per wave)
-constexpr int kStreamLdsPerWave = 36 * 1024;
+// slices through its own LDS ring.  A workgroup of NW waves owns R = 16 RB weight rows; in
+// each stage of 256 NW k, wave w takes k in [256 w, 256 w + 256): it loads its 256-byte
+// (int8) or 128-byte (int4) slice of each staged token and its 128-byte piece of each of the
+// R rows (8 rows x 128 bytes per 1 KB load), D stages ahead, and multiplies a stage as soon
+// as its own loads have landed; no workgroup barrier until the final reduction.
+//
+// With one workgroup per CU a SIMD runs NW / 4 waves, so little hides a wave's own latency:
+// the time from a stage landing to the next stage being issued (LDS reads, the issue's
+// address arithmetic) throttles the stream.  The loop therefore keeps that path short: load
+// offsets advance by a fixed stride per stage, and when K is a whole number of stages
+// (KFULL) there is no clamping of chunks past K and no masking of their codes.
+constexpr int kStreamLds = 144 * 1024;
+constexpr int kStreamDepth = 2;   // stages in flight per wave (2 to 4 measured: deeper only
+                                  // lengthens the start, as every wave waits for its first stage)
+constexpr int kNC = 5;            // constant loads of wave 0
 
-template <int ABITS, int TM, int RB>
+template <int ABITS, int TM, int RB, int NW>
 struct SL {
+    static constexpr int KS = 256 * NW;                               // k per stage
     static constexpr int R = 16 * RB;
     static constexpr int TB = ABITS == 8 ? 256 : 128;                 // token bytes per wave and stage
     static constexpr int ACT = TM * TB < 1024 ? 1024 : TM * TB;       // whole 1 KB loads
     static constexpr int WB = R * 128;                                // weight bytes per wave and stage
     static constexpr int SLOT = ACT + WB;
-    static constexpr int D0 = kStreamLdsPerWave / SLOT;
-    static constexpr int D = D0 > 2 ? 2 : D0;  // stages per wave ring (2 measured fastest; deeper rings
-                                               // only lengthen the initial issue phase)
+    static constexpr int D0 = kStreamLds / NW / SLOT;
+    static constexpr int D = D0 > kStreamDepth ? kStreamDepth : D0;   // stages per wave ring
     static constexpr int LA = ACT / 1024, LB = WB / 1024;             // loads per stage
     static constexpr int LPS = LA + LB;
-    static constexpr int RED = kWaves * RB * 1024;
-    static constexpr int RING = kWaves * D * SLOT > RED ? kWaves * D * SLOT : RED;
+    static constexpr int RED = NW * RB * 1024;
+    static constexpr int RING = NW * D * SLOT > RED ? NW * D * SLOT : RED;
     static constexpr int RP = (R + 63) / 64 * 64;
     static constexpr int C_SW = RING, C_BIAS = C_SW + 4 * RP, C_ZP = C_BIAS + 4 * RP, C_SX = C_ZP + 4 * RP,
                          C_RS = C_SX + 256;
     static constexpr int LDS = C_RS + 256;
-    static_assert(D >= 2 && (D - 1) * LPS + 8 <= 63 && LDS <= 160 * 1024, "streaming ring");
+    static_assert(D >= 2 && (D - 1) * LPS + kNC <= 63 && LDS <= 160 * 1024 && RP == 64, "streaming ring");
 };
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int ABITS, int TM, int RB>
-__global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym) {
+template <int ABITS, int TM, int RB, int NW, bool KFULL>
+__global__ void __launch_bounds__(64 * NW) k_gemv_stream(LinearArgs p, int asym) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    using L = SL<ABITS, TM, RB>;
+    using L = SL<ABITS, TM, RB, NW>;
+    constexpr int KST = L::KS;
     constexpr int R = L::R;
     constexpr int SHIFT = ABITS == 8 ? 4 : 8;
     constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    constexpr int CPT = L::TB / 16;                  // 16-byte chunks per token slice
+    constexpr uint32_t ASTEP = KST * ABITS / 8;      // token bytes per stage
+    constexpr uint32_t BSTEP = KST / 2;              // weight bytes per stage
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kb = lane >> 4;
@@ -764,43 +775,39 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
     const uint32_t xr = asym ? 0x88888888u : 0u;
     const int ring = wave * L::D * L::SLOT;  // this wave's ring
 
-    if (wave == 0) {  // constants: one dword per row (RP rows) and per token
+    // Stage i of this wave goes into ring slot i % D.  Token slice chunk c of token t sits at
+    // position c ^ (t & (CPT - 1)); weight chunk c of row r at position swz8(r, c).  Per lane
+    // and load: the byte offset of the row (token rows clamped to M - 1, weight rows to N - 1:
+    // their outputs are never stored) and the offset inside it at stage 0.  Without KFULL,
+    // chunks past K read the last valid chunk of the row and their codes are masked to zero.
+    uint32_t arow[L::LA], ain[L::LA], brow[L::LB], bin[L::LB];
 #pragma unroll
-        for (int h = 0; h < L::RP / 64; ++h) {
-            const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(64 * h + lane, R - 1), p.N - 1) - n0);
-            gl_lds4_so((uint64_t)(p.sw + n0), 4 * c, smem_base + L::C_SW + 256 * h);
-            if (p.bias) {
-                if (p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + L::C_BIAS + 256 * h);
-                else gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + L::C_BIAS + 256 * h);
-            }
-            if (asym) gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + L::C_ZP + 256 * h);
-        }
-        const uint32_t t = (uint32_t)min<int64_t>(lane, M - 1);
-        if (asym) gl_lds4_so((uint64_t)p.rowsum, 4 * t, smem_base + L::C_RS);
-        gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + L::C_SX);
+    for (int j = 0; j < L::LA; ++j) {
+        const int f = min(j * 64 + lane, TM * CPT - 1);
+        const int t = f / CPT, c = f % CPT;
+        arow[j] = (uint32_t)(min<int64_t>(t, M - 1) * rowA);
+        ain[j] = (uint32_t)(256 * wave * ABITS / 8 + 16 * (c ^ (t & (CPT - 1))));
     }
-
-    // stage i of this wave into ring slot i % D.  Token slice chunk c of token t sits at
-    // position c ^ (t & (chunks per slice - 1)); weight chunk c of row r at position swz8(r, c).  Bytes past K
-    // come from the last valid chunk of the row (those k are multiplied by zero codes).
+#pragma unroll
+    for (int j = 0; j < L::LB; ++j) {
+        const int r = 8 * j + lane / 8;
+        brow[j] = (uint32_t)((min<int64_t>(n0 + r, p.N - 1) - n0) * rowB);
+        bin[j] = (uint32_t)(128 * wave + 16 * swz8(r, lane & 7));
+    }
+    const uint64_t bbase = (uint64_t)(p.B + n0 * rowB);
     auto issue = [&](int i) __attribute__((always_inline)) {
         const uint32_t slot = smem_base + (uint32_t)(ring + (i % L::D) * L::SLOT);
-        const int64_t kw = (int64_t)i * KST + 256 * wave;  // first k of this wave's slice
 #pragma unroll
         for (int j = 0; j < L::LA; ++j) {
-            constexpr int CPT = L::TB / 16;  // chunks per token slice
-            const int f = min(j * 64 + lane, TM * CPT - 1);
-            const int t = f / CPT, c = f % CPT;
-            const int64_t tc = min<int64_t>(t, M - 1);
-            const int64_t off = min<int64_t>(kw * ABITS / 8 + 16 * (c ^ (t & (CPT - 1))), rowA - 16);
-            gl_lds16_so((uint64_t)p.A, (uint32_t)(tc * rowA + off), slot + 1024 * j);
+            uint32_t in = ain[j] + (uint32_t)i * ASTEP;
+            if constexpr (!KFULL) in = min(in, (uint32_t)(rowA - 16));
+            gl_lds16_so((uint64_t)p.A, arow[j] + in, slot + 1024 * j);
         }
 #pragma unroll
         for (int j = 0; j < L::LB; ++j) {
-            const int r = 8 * j + lane / 8;
-            const int64_t rc = min<int64_t>(n0 + r, p.N - 1) - n0;
-            const int64_t off = min<int64_t>(kw / 2 + 16 * swz8(r, lane & 7), rowB - 16);
-            gl_lds16_so((uint64_t)(p.B + n0 * rowB), (uint32_t)(rc * rowB + off), slot + L::ACT + 1024 * j);
+            uint32_t in = bin[j] + (uint32_t)i * BSTEP;
+            if constexpr (!KFULL) in = min(in, (uint32_t)(rowB - 16));
+            gl_lds16_so(bbase, brow[j] + in, slot + L::ACT + 1024 * j);
         }
     };
 
@@ -812,21 +819,40 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
 
     for (int i = 0; i < L::D; ++i)
         if (i < nst) issue(i);
+    // Constants (wave 0): row scales, biases, zero points, token scales and rowsums, one dword
+    // per row and per token, always kNC loads (a missing bias, zero point or rowsum loads the
+    // row scales or token scales into its unused slot).  They are issued after the first D
+    // stages so that the weight stream starts at once; wave 0's waits for those stages allow
+    // for them.
+    if (wave == 0) {
+        const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(lane, R - 1), p.N - 1) - n0);
+        const uint64_t sw = (uint64_t)(p.sw + n0);
+        gl_lds4_so(sw, 4 * c, smem_base + L::C_SW);
+        if (p.bias && p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + L::C_BIAS);
+        else if (p.bias) gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + L::C_BIAS);
+        else gl_lds4_so(sw, 4 * c, smem_base + L::C_BIAS);
+        if (asym) gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + L::C_ZP);
+        else gl_lds4_so(sw, 4 * c, smem_base + L::C_ZP);
+        const uint32_t t = (uint32_t)min<int64_t>(lane, M - 1);
+        gl_lds4_so(asym ? (uint64_t)p.rowsum : (uint64_t)p.sx, 4 * t, smem_base + L::C_RS);
+        gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + L::C_SX);
+    }
+    const int tt = min(lr, (int)M - 1);
     for (int i = 0; i < nst; ++i) {
-        wait_rem<L::LPS, L::D - 1>(min(L::D - 1, nst - 1 - i));
+        if (wave == 0 && i < L::D) wait_rem<L::LPS, L::D - 1, kNC>(min(L::D - 1, nst - 1 - i));
+        else wait_rem<L::LPS, L::D - 1>(min(L::D - 1, nst - 1 - i));
         const uint8_t *sl = smem + ring + (i % L::D) * L::SLOT;
-        const int t = min(lr, (int)M - 1);
         uint4 xa[2][ABITS == 8 ? 2 : 1], wv[2][RB];
-        bool kv[2];
+        bool kv[2] = {true, true};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            kv[u] = (int64_t)i * KST + 256 * wave + 128 * u + 32 * kb < K;
+            if constexpr (!KFULL) kv[u] = (int64_t)i * KST + 256 * wave + 128 * u + 32 * kb < K;
             if constexpr (ABITS == 8) {  // 16 chunks per token slice
                 const int c0 = 8 * u + 2 * kb;
-                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * (c0 ^ (t & 15)));
-                xa[u][1] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * ((c0 + 1) ^ (t & 15)));
+                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + tt * L::TB + 16 * (c0 ^ (tt & 15)));
+                xa[u][1] = *reinterpret_cast<const uint4 *>(sl + tt * L::TB + 16 * ((c0 + 1) ^ (tt & 15)));
             } else {  // 8 chunks per token slice
-                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + t * L::TB + 16 * ((4 * u + kb) ^ (t & 7)));
+                xa[u][0] = *reinterpret_cast<const uint4 *>(sl + tt * L::TB + 16 * ((4 * u + kb) ^ (tt & 7)));
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -841,12 +867,14 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
         for (int u = 0; u < 2; ++u) {
             v4i a0, a1;
             if constexpr (ABITS == 8) {
-                a0 = kv[u] ? __builtin_bit_cast(v4i, xa[u][0]) : v4i{0, 0, 0, 0};
-                a1 = kv[u] ? __builtin_bit_cast(v4i, xa[u][1]) : v4i{0, 0, 0, 0};
+                a0 = __builtin_bit_cast(v4i, xa[u][0]);
+                a1 = __builtin_bit_cast(v4i, xa[u][1]);
             } else {
-                const uint4 x = xa[u][0];
-                a0 = kv[u] ? evod(x.x, x.y) : v4i{0, 0, 0, 0};
-                a1 = kv[u] ? evod(x.z, x.w) : v4i{0, 0, 0, 0};
+                a0 = evod(xa[u][0].x, xa[u][0].y);
+                a1 = evod(xa[u][0].z, xa[u][0].w);
+            }
+            if constexpr (!KFULL) {
+                if (!kv[u]) a0 = a1 = v4i{0, 0, 0, 0};
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -871,7 +899,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
         }
     }
 
-    // ---- fixed-order reduction of the 4 waves' tiles, then the epilogue (wave rb % 4 takes
+    // ---- fixed-order reduction of the NW waves' tiles, then the epilogue (wave rb % NW takes
     // row block rb)
     __syncthreads();
     v4i *red = reinterpret_cast<v4i *>(smem);
@@ -880,10 +908,10 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        if (rb % kWaves != wave) continue;
+        if (rb % NW != wave) continue;
         v4i tt = red[rb * 64 + lane];
 #pragma unroll
-        for (int q = 1; q < kWaves; ++q) tt += red[(q * RB + rb) * 64 + lane];
+        for (int q = 1; q < NW; ++q) tt += red[(q * RB + rb) * 64 + lane];
         const int64_t m = lr;
         if (m >= M) continue;
         const int64_t nb = n0 + 16 * rb + 4 * kb;
@@ -940,24 +968,44 @@ __global__ void __launch_bounds__(kThreads) k_gemv_stream(LinearArgs p, int asym
     }
 }
 
-template <int ABITS, int TM, int RB>
-hipError_t launch_stream_t(const LinearArgs &a, hipStream_t st) {
-    using L = SL<ABITS, TM, RB>;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_stream<ABITS, TM, RB>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
+template <int ABITS, int TM, int RB, int NW, bool KFULL>
+hipError_t launch_stream_k(const LinearArgs &a, hipStream_t st) {
+    using L = SL<ABITS, TM, RB, NW>;
+    const void *fn = reinterpret_cast<const void *>(&k_gemv_stream<ABITS, TM, RB, NW, KFULL>);
+    static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
     if (attr != hipSuccess) return attr;
     const unsigned grid = (unsigned)((a.N + L::R - 1) / L::R);
-    hipLaunchKernelGGL((k_gemv_stream<ABITS, TM, RB>), dim3(grid), dim3(kThreads), L::LDS, st, a, a.zp ? 1 : 0);
+    hipLaunchKernelGGL((k_gemv_stream<ABITS, TM, RB, NW, KFULL>), dim3(grid), dim3(64 * NW), L::LDS, st, a,
+                       a.zp ? 1 : 0);
     return hipGetLastError();
 }
 
+template <int ABITS, int TM, int RB, int NW>
+hipError_t launch_stream_t(const LinearArgs &a, hipStream_t st) {
+    return a.K % (256 * NW) == 0 ? launch_stream_k<ABITS, TM, RB, NW, true>(a, st)
+                                 : launch_stream_k<ABITS, TM, RB, NW, false>(a, st);
+}
+
+// Shape of the streaming launch (measured at M = 1 to 16, K = 3072 to 12288, N = 3072 to
+// 12288).  Up to 8 tokens the staged token slices are small, so 16 rows per workgroup (the
+// most workgroups): 8 waves when that gives about one workgroup per CU (two waves per SIMD
+// to overlap one wave's stage turnaround with another's), else 4.  At 16 tokens every
+// workgroup re-reads 4 KB of token codes per wave and stage from L2, so rows per workgroup
+// grow with N to keep the grid near one workgroup per CU.
 template <int ABITS, int TM>
 hipError_t stream_rb(const LinearArgs &a, hipStream_t st) {
-    const int64_t rb = (a.N + 16 * 256 - 1) / (16 * 256);
-    if (rb <= 1) return launch_stream_t<ABITS, TM, 1>(a, st);
-    if (rb <= 2) return launch_stream_t<ABITS, TM, 2>(a, st);
-    if (rb <= 3) return launch_stream_t<ABITS, TM, 3>(a, st);
-    return launch_stream_t<ABITS, TM, 4>(a, st);
+    if constexpr (TM <= 8) {
+        int dev = 0, ncu = 256;
+        if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if ((a.N + 15) / 16 <= ncu) return launch_stream_t<ABITS, TM, 1, 8>(a, st);
+        return launch_stream_t<ABITS, TM, 1, 4>(a, st);
+    } else {
+        const int64_t rb = (a.N + 16 * 256 - 1) / (16 * 256);
+        if (rb <= 1) return launch_stream_t<ABITS, TM, 1, 4>(a, st);
+        if (rb <= 2) return launch_stream_t<ABITS, TM, 2, 4>(a, st);
+        if (rb <= 3) return launch_stream_t<ABITS, TM, 3, 4>(a, st);
+        return launch_stream_t<ABITS, TM, 4, 4>(a, st);
+    }
 }
 
 template <int ABITS>

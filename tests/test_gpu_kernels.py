@@ -44,6 +44,11 @@ def act_input(M, K, seed, dtype=torch.bfloat16, n_out=None, scale=30.0):
     (33, 272, 1024, 4, True), (128, 128, 256, 8, False), (200, 136, 448, 8, True), (300, 520, 3072, 4, False),
     (257, 256, 4096, 8, False), (130, 1000, 192, 4, True), (65, 17, 64, 8, False),
     (70, 64, 32768, 8, True), (8, 96, 32768, 4, False),   # K = W4_MAX_K, both paths
+    # small-M streaming launch shapes: 8 waves with whole 2048-k stages and with a K tail inside
+    # a stage, 4 waves once the grid passes one workgroup per CU, 16 tokens over 3 and 4 row
+    # blocks; ragged N throughout
+    (3, 1000, 4096, 4, False), (7, 520, 3072, 8, True), (1, 4100, 2048, 8, True),
+    (16, 9000, 2048, 4, True), (12, 12300, 1024, 8, False),
 ])
 def test_accumulators_bit_exact_on_oracle_codes(M, N, K, bits, asym):
     """acc[m, n] = sum_k q (c - z) from the oracle's own codes, through W4_OUT_I32."""
