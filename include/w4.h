@@ -150,7 +150,11 @@ int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *t
 /* w4_linear - the whole layer: w4_rotate_quant_act into the workspace, then
  * w4_linear_cached_rot.  Arguments as above; ws must hold at least
  * w4_workspace_bytes(M, N, K, act_bits, r) + room for the activation codes, i.e.
- * w4_linear_workspace_bytes(M, N, K, act_bits, r_needed). */
+ * w4_linear_workspace_bytes(M, N, K, act_bits, r_needed).  For one bf16 token (M = 1,
+ * K <= 16384, N <= 16 x the compute units, K a multiple of 2048) a single kernel rotates,
+ * quantizes and multiplies, the fused ConvRot path of the INT4 README ("Inference / INT4");
+ * Y is the same bit for bit, and the workspace then holds no codes (its contents are
+ * scratch either way). */
 int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
               const uint8_t *packed, const float *row_scale, const uint8_t *zp, const void *bias,
               int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *ws,
@@ -174,6 +178,11 @@ int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, 
  * plus the above).  Each piece is 256-byte aligned inside the workspace. */
 size_t w4_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);
 size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int r);
+
+/* 1 when w4_linear on this shape runs as the single fused kernel (rotation, quantization and
+ * GEMM in one launch, no codes written to the workspace), else 0 (also for shapes w4_linear
+ * rejects).  Host-only query: launches nothing, needs no stream. */
+int w4_linear_fused(int64_t M, int64_t N, int64_t K, int g, int act_bits, int x_dtype);
 
 /* Human-readable name of a status code (static string). */
 const char *w4_status_string(int status);

@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "W4Error", "library_path", "load_library", "w4_pack_weights", "w4_rotate_quant_act",
     "w4_linear_cached_rot", "w4_linear", "w4_lowrank_down", "w4_workspace_bytes",
-    "w4_linear_workspace_bytes", "LowRank", "RotationCache", "W4_OK", "W4_ERR_INVALID_ARG",
+    "w4_linear_workspace_bytes", "w4_linear_fused", "LowRank", "RotationCache", "W4_OK", "W4_ERR_INVALID_ARG",
     "W4_ERR_SHAPE", "W4_ERR_UNSUPPORTED", "W4_ERR_ALIGN", "W4_ERR_HIP", "W4_ERR_WORKSPACE",
     "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate",
 ]
@@ -68,6 +68,7 @@ EXPORTS = {
     "w4_lowrank_down": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
     "w4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "w4_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
+    "w4_linear_fused": (_I, [_I64, _I64, _I64, _I, _I, _I]),
     "w4_status_string": (ctypes.c_char_p, [_I]),
     "w4_last_error": (ctypes.c_char_p, []),
     "w4_version": (ctypes.c_char_p, []),
@@ -130,6 +131,11 @@ def w4_workspace_bytes(M, N, K, act_bits, r=0) -> int:
 
 def w4_linear_workspace_bytes(M, N, K, act_bits, r=0) -> int:
     return int(load_library().w4_linear_workspace_bytes(M, N, K, act_bits, r))
+
+
+def w4_linear_fused(M, N, K, g, act_bits, x_dtype=torch.bfloat16) -> bool:
+    """True when w4_linear on this shape runs as one fused rotate + quantize + GEMM kernel."""
+    return bool(load_library().w4_linear_fused(M, N, K, g, act_bits, W4_BF16 if x_dtype == torch.bfloat16 else W4_F32))
 
 
 def w4_pack_weights(W: torch.Tensor, g: int, asym: bool = False):

@@ -51,6 +51,16 @@ __device__ __forceinline__ double dpp_f64(double x) {
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
 
+// Lane exchange for a double through ds_swizzle (bit-mask mode), for lanes 4 and 8 apart.
+template <int PAT>
+__device__ __forceinline__ double swz_f64(double x) {
+    const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(x), PAT);
+    const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(x), PAT);
+    return __hiloint2double(hi, lo);
+}
+constexpr int kSwzXor4 = 0x101F;  // and 0x1f, or 0, xor 4
+constexpr int kSwzXor8 = 0x201F;  // xor 8
+
 // In-register Walsh-Hadamard butterflies over 16 values (Sylvester order, unnormalised):
 // after the call v[i] = sum_j (-1)^popcount(i & j) * v_in[j].
 __device__ __forceinline__ void fwht16(double (&v)[16]) {

@@ -752,6 +752,85 @@ struct SL {
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// Fixed-order reduction of the NW waves' tiles through LDS (from offset 0), then the dequant
+// epilogue: wave rb % NW takes row block rb.  16x16 layout: lane l, register r holds weight
+// row 4 (l / 16) + r of token l % 16.  The per-row and per-token constants sit in LDS at the
+// given offsets, one dword per entry.
+template <int ABITS, int RB, int NW>
+__device__ __forceinline__ void stream_epilogue(const LinearArgs &p, uint8_t *smem, const v4i (&acc)[2][RB], int64_t n0,
+                                                int asym, int c_sw, int c_bias, int c_zp, int c_sx, int c_rs) {
+    constexpr int SHIFT = ABITS == 8 ? 4 : 8;
+    constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int64_t M = p.M;
+    __syncthreads();
+    v4i *red = reinterpret_cast<v4i *>(smem);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) red[(wave * RB + rb) * 64 + lane] = acc[0][rb] + acc[1][rb];
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        if (rb % NW != wave) continue;
+        v4i tt = red[rb * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) tt += red[(q * RB + rb) * 64 + lane];
+        const int64_t m = lr;
+        if (m >= M) continue;
+        const int64_t nb = n0 + 16 * rb + 4 * kb;
+        const int rl = 16 * rb + 4 * kb;
+        const float4 sw4 = *reinterpret_cast<const float4 *>(smem + c_sw + 4 * rl);
+        const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
+        const float sxm = *reinterpret_cast<const float *>(smem + c_sx + 4 * m);
+        int a[4] = {tt[0], tt[1], tt[2], tt[3]};
+        if (asym) {
+            const uint4 z4 = *reinterpret_cast<const uint4 *>(smem + c_zp + 4 * rl);
+            const int rsm = *reinterpret_cast<const int *>(smem + c_rs + 4 * m);
+            const uint32_t z[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] += ((8 - (int)z[r]) << SHIFT) * rsm;
+        }
+        if (p.y_i32) {
+            int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) Y[nb + r] = a[r] >> SHIFT;
+            continue;
+        }
+        float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.bias) {
+            const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + c_bias + 4 * rl);
+            const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+        }
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
+        if (p.lr_t) {
+            const float *tr = p.lr_t + m * p.lr_r;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t nc = min<int64_t>(nb + r, p.N - 1);
+                float l = 0.0f;
+                for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
+                y[r] += l;
+            }
+        }
+        uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+        const uint32_t b0 = f32_to_bf16(y[0]), b1 = f32_to_bf16(y[1]), b2 = f32_to_bf16(y[2]),
+                       b3 = f32_to_bf16(y[3]);
+        if (nb + 3 < p.N && (p.N & 3) == 0) {
+            *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        } else {
+            const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) Y[nb + r] = (uint16_t)bb[r];
+        }
+    }
+}
+
 template <int ABITS, int TM, int RB, int NW, bool KFULL>
 __global__ void __launch_bounds__(64 * NW) k_gemv_stream(LinearArgs p, int asym) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -899,73 +978,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemv_stream(LinearArgs p, int asym)
         }
     }
 
-    // ---- fixed-order reduction of the NW waves' tiles, then the epilogue (wave rb % NW takes
-    // row block rb)
-    __syncthreads();
-    v4i *red = reinterpret_cast<v4i *>(smem);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) red[(wave * RB + rb) * 64 + lane] = acc[0][rb] + acc[1][rb];
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        if (rb % NW != wave) continue;
-        v4i tt = red[rb * 64 + lane];
-#pragma unroll
-        for (int q = 1; q < NW; ++q) tt += red[(q * RB + rb) * 64 + lane];
-        const int64_t m = lr;
-        if (m >= M) continue;
-        const int64_t nb = n0 + 16 * rb + 4 * kb;
-        const int rl = 16 * rb + 4 * kb;
-        const float4 sw4 = *reinterpret_cast<const float4 *>(smem + L::C_SW + 4 * rl);
-        const float sw[4] = {sw4.x * kUnscale, sw4.y * kUnscale, sw4.z * kUnscale, sw4.w * kUnscale};
-        const float sxm = *reinterpret_cast<const float *>(smem + L::C_SX + 4 * m);
-        int a[4] = {tt[0], tt[1], tt[2], tt[3]};
-        if (asym) {
-            const uint4 z4 = *reinterpret_cast<const uint4 *>(smem + L::C_ZP + 4 * rl);
-            const int rsm = *reinterpret_cast<const int *>(smem + L::C_RS + 4 * m);
-            const uint32_t z[4] = {z4.x, z4.y, z4.z, z4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] += ((8 - (int)z[r]) << SHIFT) * rsm;
-        }
-        if (p.y_i32) {
-            int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nb + r < p.N) Y[nb + r] = a[r] >> SHIFT;
-            continue;
-        }
-        float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (p.bias) {
-            const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + L::C_BIAS + 4 * rl);
-            const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
-        }
-        float y[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
-        if (p.lr_t) {
-            const float *tr = p.lr_t + m * p.lr_r;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t nc = min<int64_t>(nb + r, p.N - 1);
-                float l = 0.0f;
-                for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
-                y[r] += l;
-            }
-        }
-        uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
-        const uint32_t b0 = f32_to_bf16(y[0]), b1 = f32_to_bf16(y[1]), b2 = f32_to_bf16(y[2]),
-                       b3 = f32_to_bf16(y[3]);
-        if (nb + 3 < p.N && (p.N & 3) == 0) {
-            *reinterpret_cast<uint2 *>(Y + nb) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-        } else {
-            const uint32_t bb[4] = {b0, b1, b2, b3};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (nb + r < p.N) Y[nb + r] = (uint16_t)bb[r];
-        }
-    }
+    stream_epilogue<ABITS, RB, NW>(p, smem, acc, n0, asym, L::C_SW, L::C_BIAS, L::C_ZP, L::C_SX, L::C_RS);
 }
 
 template <int ABITS, int TM, int RB, int NW, bool KFULL>
@@ -1017,6 +1030,311 @@ hipError_t launch_stream(const LinearArgs &a, hipStream_t st) {
     return stream_rb<ABITS, 16>(a, st);
 }
 
+// ---------------------------------------------------------------------------------------
+// Fused path for one token (K <= 16384, bf16 X, K a whole number of stages; the kernel takes
+// up to 4 tokens): rotation, quantization and the streaming GEMM in one launch, the single-kernel
+// ConvRot path of the INT4 README ("Inference / INT4").  Every workgroup rotates and
+// quantizes the whole token block itself (at most 16384 elements; the fp64 work overlaps the
+// first weight stages in flight) and keeps the codes in LDS for the whole K, so the stream
+// carries weights only and the separate rotate launch, with its gap, disappears.
+//   1. direct loads: X (M K bf16 in 1 KB pieces), the first 2 weight stages, the constants
+//      (as in the streaming kernel);
+//   2. each 16-lane group takes 256-element blocks (token t, block j), lane c elements
+//      16 c .. 16 c + 15, in fp64 with the row rotate-quant kernel's butterflies, amax, scale
+//      and rounding, so codes, scales and rowsums are the same bit for bit;
+//   3. per-token amax and rowsum through LDS across the workgroup; the int8 (or packed int4)
+//      codes go to LDS over X, in the streaming kernel's token layout (window of 256 k,
+//      16-byte chunk c of token t at position c ^ (t & (chunks - 1)));
+//   4. the streaming loop over the weights, token fragments from the resident codes, and the
+//      streaming epilogue with the token scales and rowsums of step 3.
+constexpr int kFuseMaxElems = 16384;  // M K per workgroup
+constexpr int kFuseNW = 8;            // waves per workgroup (one workgroup per CU)
+constexpr int kFuseDMax = 2;          // weight stages in flight per wave (deeper rings measured
+                                      // slower: the rotation then trails the stream)
+constexpr int kFusePMax = kFuseMaxElems / (4 * kFuseNW * 256);  // 256-element blocks per 16-lane group
+
+template <int ABITS, int TM, int G>
+struct FL {
+    static constexpr int NW = kFuseNW;
+    static constexpr int D = kFuseDMax;
+    static constexpr int LB = 2;         // weight loads per stage: 16 rows x 128 bytes
+    static constexpr int WB = LB * 1024;
+    static constexpr int RING = NW * D * WB;
+    static constexpr int XOFF = RING;    // X (bf16), then the codes over it
+    static constexpr int C_SW = XOFF + kFuseMaxElems * 2, C_BIAS = C_SW + 256, C_ZP = C_BIAS + 256,
+                         C_DUMMY = C_ZP + 256, C_SX = C_DUMMY + 512, C_RS = C_SX + 64, C_RD = C_RS + 64,
+                         C_RI = C_RD + 8 * NW * TM;
+    static constexpr int LDS = C_RI + 4 * NW * TM;
+    static_assert(TM <= 4 && LDS <= 160 * 1024 && D * LB + kNC + kFuseMaxElems * 2 / 1024 / NW <= 63 &&
+                      4 * NW * kFusePMax * 256 == kFuseMaxElems && RING >= NW * 1024,
+                  "fused layout");
+};
+
+template <int ABITS, int TM, int G>
+__global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const uint16_t *__restrict__ X, int asym) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using F = FL<ABITS, TM, G>;
+    constexpr int NW = F::NW;
+    constexpr int R = 16;
+    constexpr int DM = F::D, LB = F::LB;
+    constexpr int KST = 256 * NW;
+    constexpr int QMAX = ABITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
+    constexpr int TB = ABITS == 8 ? 256 : 128;  // code bytes per token and 256-k window
+    constexpr int CPT = TB / 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * R;
+    const int K = (int)p.K, M = (int)p.M;
+    const int nst = K / KST;
+    const int64_t rowB = K / 2;
+    const int CB = K * ABITS / 8;  // code bytes per token
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t xr = asym ? 0x88888888u : 0u;
+    const int D = min(nst, DM);  // stages in flight: all of them when they fit
+    const int ring = wave * DM * F::WB;
+
+    // ---- 1. loads: X, the first D weight stages, the constants
+    const int nx = M * K * 2 / 1024;
+    for (int q = wave; q < nx; q += NW)
+        gl_lds16_so((uint64_t)X, (uint32_t)(1024 * q + 16 * lane), smem_base + F::XOFF + 1024 * q);
+    uint32_t brow[LB], bin[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int r = 8 * j + lane / 8;
+        brow[j] = (uint32_t)((min<int64_t>(n0 + r, p.N - 1) - n0) * rowB);
+        bin[j] = (uint32_t)(128 * wave + 16 * swz8(r, lane & 7));
+    }
+    const uint64_t bbase = (uint64_t)(p.B + n0 * rowB);
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const uint32_t slot = smem_base + (uint32_t)(ring + (i % D) * F::WB);
+#pragma unroll
+        for (int j = 0; j < LB; ++j) gl_lds16_so(bbase, brow[j] + bin[j] + (uint32_t)i * (KST / 2), slot + 1024 * j);
+    };
+    const int D0 = min(nst, kStreamDepth);  // stages issued before X has landed
+    for (int i = 0; i < D0; ++i) issue(i);
+    if (wave == 0) {  // kNC loads like the streaming kernel; token scales and rowsums come from step 3
+        const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(lane, R - 1), p.N - 1) - n0);
+        const uint64_t sw = (uint64_t)(p.sw + n0);
+        gl_lds4_so(sw, 4 * c, smem_base + F::C_SW);
+        if (p.bias && p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + F::C_BIAS);
+        else if (p.bias) gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + F::C_BIAS);
+        else gl_lds4_so(sw, 4 * c, smem_base + F::C_BIAS);
+        if (asym) gl_lds1_so((uint64_t)(p.zp + n0), c, smem_base + F::C_ZP);
+        else gl_lds4_so(sw, 4 * c, smem_base + F::C_ZP);
+        gl_lds4_so(sw, 4 * c, smem_base + F::C_DUMMY);
+        gl_lds4_so(sw, 4 * c, smem_base + F::C_DUMMY + 256);
+    }
+    // this wave's X pieces have landed (the stages and constants issued after them may still
+    // be in flight); then the rest of the first D stages, so the weight stream runs on while
+    // the tokens are rotated.  (Issuing all of them before X lands delays X behind the
+    // workgroups' weight requests.)
+    if (wave == 0) wait_rem<LB, kStreamDepth, kNC>(D0);
+    else wait_rem<LB, kStreamDepth>(D0);
+    __syncthreads();  // every wave's X pieces
+    for (int i = D0; i < D; ++i) issue(i);
+
+    // ---- 2. rotate: 16-lane group lg takes blocks u = lg + 4 NW pp (pp < P, uniform)
+    const int lg = tid >> 4, cl = tid & 15;
+    const int nblk = K / 256, U = M * nblk, P = (U + 4 * NW - 1) / (4 * NW);
+    double v[kFusePMax][16];
+    double am[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) am[t] = 0.0;
+#pragma unroll
+    for (int pp = 0; pp < kFusePMax; ++pp) {
+        if (pp >= P) break;
+        const int u = lg + 4 * NW * pp;
+        const bool ok = u < U;
+        const int t = ok ? u / nblk : 0, j = ok ? u - t * nblk : 0;
+        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+        if (ok) {
+            const uint8_t *src = smem + F::XOFF + 2 * (t * K + 256 * j + 16 * cl);
+            w0 = *reinterpret_cast<const uint4 *>(src);
+            w1 = *reinterpret_cast<const uint4 *>(src + 16);
+        }
+        const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v[pp][2 * e] = (double)bf16_lo(wd[e]);
+            v[pp][2 * e + 1] = (double)bf16_hi(wd[e]);
+        }
+        fwht16(v[pp]);
+        // lane exchanges stay inside the 16-lane group (quads; lanes 4 and 8 apart)
+        const double s1 = (cl & 1) ? -1.0 : 1.0, s2 = (cl & 2) ? -1.0 : 1.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[pp][i] = fma(v[pp][i], s1, dpp_f64<kQuadXor1>(v[pp][i]));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[pp][i] = fma(v[pp][i], s2, dpp_f64<kQuadXor2>(v[pp][i]));
+        if constexpr (G == 256) {
+            const double s4 = (cl & 4) ? -1.0 : 1.0, s8 = (cl & 8) ? -1.0 : 1.0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[pp][i] = fma(v[pp][i], s4, swz_f64<kSwzXor4>(v[pp][i]));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[pp][i] = fma(v[pp][i], s8, swz_f64<kSwzXor8>(v[pp][i]));
+        }
+        double mx = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmax(mx, fabs(v[pp][i]));
+        if (ok) {
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt)
+                if (tt == t) am[tt] = fmax(am[tt], mx);
+        }
+    }
+
+    // ---- 3. per-token amax across the workgroup, scales, codes, rowsums
+    double *rd = reinterpret_cast<double *>(smem + F::C_RD);
+    int *ri = reinterpret_cast<int *>(smem + F::C_RI);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) am[t] = fmax(am[t], __shfl_xor(am[t], off));
+        if (lane == 0) rd[wave * TM + t] = am[t];
+    }
+    __syncthreads();  // also: every lane is past its reads of X
+    double rr[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+        double a = rd[t];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a = fmax(a, rd[w * TM + t]);
+        const float scale = (float)((a * INV_SQRT_G) / (double)QMAX);
+        rr[t] = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
+        if (tid == 0) *reinterpret_cast<float *>(smem + F::C_SX + 4 * t) = scale;
+    }
+    int rsum[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t) rsum[t] = 0;
+#pragma unroll
+    for (int pp = 0; pp < kFusePMax; ++pp) {
+        if (pp >= P) break;
+        const int u = lg + 4 * NW * pp;
+        if (u < U) {
+            const int t = u / nblk, j = u - t * nblk;
+            double rt = 0.0;
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt)
+                if (tt == t) rt = rr[tt];
+            uint32_t d[4];
+            int rs = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int q4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qi = __double2loint(fma(v[pp][4 * q + r], rt, kRoundMagic));
+                    q4[r] = min(max(qi, -QMAX - 1), QMAX);
+                }
+                d[q] = (uint32_t)(q4[0] & 0xff) | ((uint32_t)(q4[1] & 0xff) << 8) | ((uint32_t)(q4[2] & 0xff) << 16) |
+                       ((uint32_t)(q4[3] & 0xff) << 24);
+                rs = __builtin_amdgcn_sdot4((int)d[q], 0x01010101, rs, false);
+            }
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt)
+                if (tt == t) rsum[tt] += rs;
+            uint8_t *dst = smem + F::XOFF + t * CB + j * TB;
+            if constexpr (ABITS == 8) {
+                *reinterpret_cast<uint4 *>(dst + 16 * (cl ^ (t & 15))) = make_uint4(d[0], d[1], d[2], d[3]);
+            } else {
+                uint32_t x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = d[q] & 0x0F0F0F0Fu;
+                    x[q] = lo | (lo >> 4);
+                }
+                *reinterpret_cast<uint2 *>(dst + 16 * ((cl >> 1) ^ (t & 7)) + 8 * (cl & 1)) =
+                    make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u));
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) rsum[t] += __shfl_xor(rsum[t], off);
+        if (lane == 0) ri[wave * TM + t] = rsum[t];
+    }
+    __syncthreads();  // codes and per-wave rowsums
+    if (tid < TM) {
+        int a = 0;
+        for (int w = 0; w < NW; ++w) a += ri[w * TM + tid];
+        *reinterpret_cast<int *>(smem + F::C_RS + 4 * tid) = a;
+    }
+
+    // ---- 4. the streaming loop over the weights
+    v4i acc[2][1];
+    acc[0][0] = acc[1][0] = v4i{0, 0, 0, 0};
+    const int tt = min(lr, M - 1);
+    const uint8_t *codes = smem + F::XOFF + tt * CB;
+    for (int i = 0; i < nst; ++i) {
+        if (wave == 0 && i < D0) wait_rem<LB, DM - 1, kNC>(min(D - 1, nst - 1 - i));
+        else wait_rem<LB, DM - 1>(min(D - 1, nst - 1 - i));
+        const uint8_t *sl = smem + ring + (i % D) * F::WB;
+        const uint8_t *cw = codes + (i * NW + wave) * TB;  // this wave's 256-k window
+        uint4 xa[2][ABITS == 8 ? 2 : 1], wv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if constexpr (ABITS == 8) {
+                const int c0 = 8 * u + 2 * kb;
+                xa[u][0] = *reinterpret_cast<const uint4 *>(cw + 16 * (c0 ^ (tt & 15)));
+                xa[u][1] = *reinterpret_cast<const uint4 *>(cw + 16 * ((c0 + 1) ^ (tt & 15)));
+            } else {
+                xa[u][0] = *reinterpret_cast<const uint4 *>(cw + 16 * ((4 * u + kb) ^ (tt & 7)));
+            }
+            wv[u] = *reinterpret_cast<const uint4 *>(sl + lr * 128 + 16 * swz8(lr, 4 * u + kb));
+        }
+        wait_lgkmcnt0();
+        if (i + D < nst) issue(i + D);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            v4i a0, a1;
+            if constexpr (ABITS == 8) {
+                a0 = __builtin_bit_cast(v4i, xa[u][0]);
+                a1 = __builtin_bit_cast(v4i, xa[u][1]);
+            } else {
+                a0 = evod(xa[u][0].x, xa[u][0].y);
+                a1 = evod(xa[u][0].z, xa[u][0].w);
+            }
+            uint4 w = wv[u];
+            w.x ^= xr; w.y ^= xr; w.z ^= xr; w.w ^= xr;
+            v4i w0, w1;
+            if constexpr (ABITS == 8) {
+                uint32_t q[8];
+                unpack_nat(w.x, q[0], q[1]);
+                unpack_nat(w.y, q[2], q[3]);
+                unpack_nat(w.z, q[4], q[5]);
+                unpack_nat(w.w, q[6], q[7]);
+                w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+            } else {
+                w0 = evod(w.x, w.y);
+                w1 = evod(w.z, w.w);
+            }
+            acc[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc[u][0], 0, 0, 0);
+            acc[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc[u][0], 0, 0, 0);
+        }
+    }
+    stream_epilogue<ABITS, 1, NW>(p, smem, acc, n0, asym, F::C_SW, F::C_BIAS, F::C_ZP, F::C_SX, F::C_RS);
+}
+
+template <int ABITS, int TM, int G>
+hipError_t launch_fused_t(const LinearArgs &a, const void *X, hipStream_t st) {
+    using F = FL<ABITS, TM, G>;
+    const void *fn = reinterpret_cast<const void *>(&k_gemv_fused<ABITS, TM, G>);
+    static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS);
+    if (attr != hipSuccess) return attr;
+    const unsigned grid = (unsigned)((a.N + 15) / 16);
+    hipLaunchKernelGGL((k_gemv_fused<ABITS, TM, G>), dim3(grid), dim3(64 * kFuseNW), F::LDS, st, a,
+                       static_cast<const uint16_t *>(X), a.zp ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int ABITS, int G>
+hipError_t fused_tm(const LinearArgs &a, const void *X, hipStream_t st) {
+    return launch_fused_t<ABITS, 1, G>(a, X, st);
+}
+
 }  // namespace
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits) {
@@ -1036,6 +1354,23 @@ hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_by
         return act_bits == 8 ? split_mb<8>(a, pl, part, st) : split_mb<4>(a, pl, part, st);
     }
     return act_bits == 8 ? dispatch_mb<8>(a, st) : dispatch_mb<4>(a, st);
+}
+
+// Fused where it measured faster than the two launches: one token (at 2 to 4 tokens the
+// rotation outlasts the weight stages in flight), one workgroup per CU (more would repeat
+// the rotation on each CU), whole stages.  The kernel itself takes up to 4 tokens.
+bool gemv_fusable(int64_t M, int64_t N, int64_t K, int g, int act_bits, bool f32in) {
+    if (f32in || M != 1 || M * K > kFuseMaxElems || (g != 64 && g != 256) || (act_bits != 8 && act_bits != 4))
+        return false;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return (N + 15) / 16 <= ncu && K % (256 * kFuseNW) == 0;
+}
+
+hipError_t launch_gemv_fused(const LinearArgs &a, const void *X, int g, int act_bits, hipStream_t st) {
+    if (!gemv_fusable(a.M, a.N, a.K, g, act_bits, false)) return hipErrorInvalidValue;
+    if (act_bits == 8) return g == 64 ? fused_tm<8, 64>(a, X, st) : fused_tm<8, 256>(a, X, st);
+    return g == 64 ? fused_tm<4, 64>(a, X, st) : fused_tm<4, 256>(a, X, st);
 }
 
 }  // namespace w4

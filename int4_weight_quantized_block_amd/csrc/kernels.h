@@ -41,6 +41,11 @@ hipError_t launch_gemm(const LinearArgs &a, int act_bits, void *ws, size_t ws_by
 // needed) the K-split kernel runs; without one, the LDS-ring kernel.
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits);
 hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
+// Fused rotate + quantize + small-M GEMM from bf16 X [M, K] (a.A, a.sx and a.rowsum unused),
+// for the shapes gemv_fusable() accepts (one token); the result equals launch_rotquant +
+// launch_gemv bit for bit.
+bool gemv_fusable(int64_t M, int64_t N, int64_t K, int g, int act_bits, bool f32in);
+hipError_t launch_gemv_fused(const LinearArgs &a, const void *X, int g, int act_bits, hipStream_t st);
 
 // Measurement probe: blocks workgroups of 4 waves, each wave iters rounds of 4 int8 MFMAs.
 hipError_t launch_mfma_rate(int64_t blocks, int iters, bool random_operands, int32_t *sink, hipStream_t st);

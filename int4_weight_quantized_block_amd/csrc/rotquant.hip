@@ -391,14 +391,6 @@ k_rotquant_stream(const void *__restrict__ Xv, int64_t M, int K, int T, int R, i
 // with the lanes 4 and 8 apart through ds_swizzle, which runs on the LDS unit and so adds
 // only the fma to the VALU's load (measured: faster than swizzling all four stages, and than
 // DPP moves for these two).
-template <int PAT>
-__device__ __forceinline__ double swz_f64(double x) {
-    const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(x), PAT);
-    const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(x), PAT);
-    return __hiloint2double(hi, lo);
-}
-constexpr int kSwzXor4 = 0x101F;  // bit-mask mode: and 0x1f, or 0, xor 4
-constexpr int kSwzXor8 = 0x201F;  // xor 8
 
 template <int G, int BITS, bool F32IN, int C>
 __global__ void __launch_bounds__(C == 1 ? 1024 : 512) __attribute__((amdgpu_waves_per_eu(2)))

@@ -102,6 +102,12 @@ size_t w4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, 
     return align256(qb) + 2 * align256((size_t)M * 4) + w4_workspace_bytes(M, N, K, act_bits, r);
 }
 
+int w4_linear_fused(int64_t M, int64_t N, int64_t K, int g, int act_bits, int x_dtype) {
+    if ((x_dtype != W4_F32 && x_dtype != W4_BF16) || N < 1 || K < 1 || (g != 64 && g != 256) || K % g)
+        return 0;
+    return w4::gemv_fusable(M, N, K, g, act_bits, x_dtype == W4_F32) ? 1 : 0;
+}
+
 int w4_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int g, int wmode, uint8_t *packed,
                     float *row_scale, uint8_t *zp, void *stream) {
     const char *fn = "w4_pack_weights";
@@ -165,10 +171,13 @@ int w4_probe_mfma_rate(int64_t blocks, int iters, int random_operands, int32_t *
                       fn);
 }
 
+// xf: NULL, or bf16 X for the fused small-M kernel (rotation and quantization inside the GEMM
+// launch; q, tok_scale and tok_rowsum are then not read).
 static int linear_impl(const char *fn, const void *q, const float *tok_scale, const int32_t *tok_rowsum,
                        int act_bits, const uint8_t *packed, const float *row_scale, const uint8_t *zp,
                        const void *bias, int bias_dtype, const w4_lowrank *lr, int64_t M, int64_t N, int64_t K,
-                       void *Y, int y_kind, void *ws, size_t ws_bytes, hipStream_t st) {
+                       void *Y, int y_kind, void *ws, size_t ws_bytes, hipStream_t st, const void *xf = nullptr,
+                       int g = 0) {
     if (y_kind != W4_OUT_BF16 && y_kind != W4_OUT_I32) return fail(W4_ERR_INVALID_ARG, "%s: y_kind=%d", fn, y_kind);
     if (bias && bias_dtype != W4_F32 && bias_dtype != W4_BF16)
         return fail(W4_ERR_INVALID_ARG, "%s: bias_dtype=%d", fn, bias_dtype);
@@ -231,8 +240,9 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     // last partial round of tiles of the large-M path)
     void *gws = ws ? static_cast<uint8_t *>(ws) + tbytes : nullptr;
     const size_t gbytes = ws ? ws_bytes - tbytes : 0;
-    hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, gws, gbytes, st)
-                           : w4::launch_gemm(a, act_bits, gws, gbytes, st);
+    hipError_t e = xf        ? w4::launch_gemv_fused(a, xf, g, act_bits, st)
+                   : M <= 64 ? w4::launch_gemv(a, act_bits, gws, gbytes, st)
+                             : w4::launch_gemm(a, act_bits, gws, gbytes, st);
     return hip_status(e, fn);
 }
 
@@ -287,6 +297,10 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
         }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // a few tokens: one launch rotates, quantizes and multiplies (same result, no codes written)
+    if (w4::gemv_fusable(M, N, K, g, act_bits, x_dtype == W4_F32))
+        return linear_impl(fn, qbuf, sx, rs, act_bits, packed, row_scale, zp, bias, bias_dtype, lr, M, N, K, Y, y_kind,
+                           rest, rest_bytes, st, X, g);
     hipError_t e = w4::launch_rotquant(X, x_dtype == W4_F32, M, K, g, act_bits, qbuf, sx, rs, st);
     if (e != hipSuccess) return hip_status(e, fn);
     return linear_impl(fn, qbuf, sx, rs, act_bits, packed, row_scale, zp, bias, bias_dtype, lr, M, N, K, Y, y_kind,

@@ -300,3 +300,43 @@ def test_gemm_split_tail_equals_single_pass(M, N, K, bits, asym):
     err = (y1.float() - y0.float()).norm() / y0.float().norm()
     say("  low-rank split vs single pass rel frob %.3e" % err.item())
     assert err.item() <= FROB_TOL
+
+
+# --------------------------------------------------------------------------- fused small-M path
+@pytest.mark.parametrize("M,N,K,g,bits,asym,bias_dtype,lr", [
+    (1, 4096, 12288, 256, 8, True, torch.bfloat16, False),   # text-encoder shape, fused
+    (1, 1000, 8192, 64, 4, True, None, False),               # fused W4A4, g = 64, ragged N
+    (1, 520, 4096, 256, 4, False, torch.bfloat16, True),     # fused W4A4, low-rank, ragged N
+    (1, 300, 16384, 64, 8, False, None, False),              # fused, largest K (8 stages, ring of 2)
+    (1, 64, 2048, 256, 8, True, torch.float32, True),        # fused, one stage (fewer than the ring)
+    (1, 12288, 4096, 256, 8, True, torch.bfloat16, False),   # past one workgroup per CU: two launches
+    (1, 4100, 4096, 256, 8, True, torch.bfloat16, False),    # two launches, ragged N
+    (2, 2048, 4096, 256, 8, True, torch.bfloat16, True),     # two tokens: two launches
+    (4, 1000, 4096, 256, 8, False, torch.float32, True),     # two launches
+])
+def test_fused_small_m_equals_two_launches(M, N, K, g, bits, asym, bias_dtype, lr):
+    """w4_linear at one token rotates, quantizes and multiplies in one launch; its output must
+    equal w4_rotate_quant_act followed by w4_linear_cached_rot bit for bit, for bf16 and raw
+    int32 outputs (the rotate-quant kernel itself is pinned to the oracle elsewhere).  The
+    cases next to the fusion limits check the same equality on the two-launch side."""
+    say("fused small-M M=%d N=%d K=%d g=%d bits=%d asym=%s bias=%s lr=%s" % (M, N, K, g, bits, asym, bias_dtype, lr))
+    r = rng(M * 11 + N + K + g + bits)
+    X = act_input(M, K, seed=M + 3 * K).to(DEV)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    packed, scale, zp = w4.w4_pack_weights(W, g, asym)
+    bias = None
+    if bias_dtype is not None:
+        bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(bias_dtype).to(DEV)
+    low = None
+    if lr:
+        L1t = torch.from_numpy((r.standard_normal((16, K)) * 0.01).astype(np.float32)).to(torch.bfloat16).to(DEV)
+        L2 = torch.from_numpy((r.standard_normal((16, N)) * 0.05).astype(np.float32)).to(torch.bfloat16).to(DEV)
+        low = w4.LowRank(l2=L2, x=X, l1=L1t)
+    y1 = w4.w4_linear(X, g, bits, packed, scale, zp, bias=bias, lowrank=low)
+    q, s, rs = w4.w4_rotate_quant_act(X, g, bits)
+    y2 = w4.w4_linear_cached_rot(q, s, rs, bits, packed, scale, zp, bias=bias, lowrank=low)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    a1 = w4.w4_linear(X, g, bits, packed, scale, zp, out_i32=True)
+    a2 = w4.w4_linear_cached_rot(q, s, rs, bits, packed, scale, zp, out_i32=True)
+    assert torch.equal(a1, a2)
+    assert bool(torch.isfinite(y1.float()).all()) and float(y1.float().abs().max()) > 0
