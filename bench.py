@@ -3,9 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--M M]
 
-One "step" is one pass of the whole layer over one batch: rotate + quantize the
-activations (w4_rotate_quant_act) and the integer GEMM with the fused dequant
-epilogue (w4_linear_cached_rot); for the 20-block workload a step is all 80 linears
+One "step" is one pass of the whole layer over one batch, the w4_linear call: rotate +
+quantize the activations and the integer GEMM with the fused dequant epilogue (two
+launches, or one fused launch for a single token); for the 20-block workload a step is all 80 linears
 of the 20 blocks with the rotation cache and the low-rank branches.  Weights are packed
 once before timing (an offline step).  Inputs are resident in HBM; the timed loop
 cycles through enough distinct input copies (> 256 MB) that reads come from HBM, not
@@ -96,6 +96,11 @@ class Linear:
 
     def weight_bytes(self):
         return self.N * self.K // 2 + 4 * self.N + (self.N if self.asym else 0)
+
+    def fused_bytes(self):
+        """Algorithmic HBM bytes of the fused single-token launch (bf16 X instead of codes)."""
+        M, N, K = self.M, self.N, self.K
+        return 2 * M * K + self.weight_bytes() + 2 * N + 2 * M * N
 
     def rotquant_bytes(self):
         M, K = self.M, self.K
@@ -274,21 +279,22 @@ def main():
     mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
                 z.data_ptr() if z is not None else None, lin.bias.data_ptr(), w4.W4_BF16, None, M, N, K,
                 Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
-    f_rq, f_mm = L.w4_rotate_quant_act, L.w4_linear_cached_rot
+    # the step: the whole layer through w4_linear (rotate + quantize into its workspace, then
+    # the GEMM; one fused launch for a single token, see w4_linear_fused)
+    wsl = torch.empty((max(256, w4.w4_linear_workspace_bytes(M, N, K, bits)),), dtype=torch.uint8, device=dev)
+    lin_args = [(x.data_ptr(), xdt, M, K, g, bits, p.data_ptr(), s.data_ptr(), z.data_ptr() if z is not None else None,
+                 lin.bias.data_ptr(), w4.W4_BF16, None, N, Y.data_ptr(), w4.W4_OUT_BF16, wsl.data_ptr(), wsl.numel(),
+                 sptr) for x, (p, s, z) in zip(Xs, Ps)]
+    f_rq, f_mm, f_lin = L.w4_rotate_quant_act, L.w4_linear_cached_rot, L.w4_linear
+    fused = bool(L.w4_linear_fused(M, N, K, g, bits, xdt))
 
-    def rotquant(i):
-        rc = f_rq(*rq_args[i % ncopy])
-        if rc:
-            w4._check(rc)
-
-    def gemm(i):
-        rc = f_mm(*mm_args[i % ncopy])
+    def step(i):
+        rc = f_lin(*lin_args[i % ncopy])
         if rc:
             w4._check(rc)
 
     for i in range(args.warmup):
-        rotquant(i)
-        gemm(i)
+        step(i)
     torch.cuda.synchronize()
     log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
                                                                             args.warmup))
@@ -320,15 +326,17 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps * 1e-3
 
-    t_rq = per_launch(f_rq, rq_args)
-    t_mm = per_launch(f_mm, mm_args)
-    log("bench: rotate+quant %.2f us, GEMM %.2f us per launch" % (t_rq * 1e6, t_mm * 1e6))
-    # eager steps (both launches per step), timed as a whole
+    if fused:  # one kernel per step
+        t_rq, t_mm = None, per_launch(f_lin, lin_args)
+        log("bench: fused rotate+quant+GEMM %.2f us per launch" % (t_mm * 1e6))
+    else:
+        t_rq, t_mm = per_launch(f_rq, rq_args), per_launch(f_mm, mm_args)
+        log("bench: rotate+quant %.2f us, GEMM %.2f us per launch" % (t_rq * 1e6, t_mm * 1e6))
+    # eager steps, timed as a whole
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        rotquant(i)
-        gemm(i)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log("bench: eager %.3f ms/step wall" % (wall / args.steps * 1e3))
@@ -341,8 +349,7 @@ def main():
         with torch.cuda.graph(gph, stream=side):
             st2 = torch.cuda.current_stream().cuda_stream
             for i in range(args.steps):
-                w4._check(f_rq(*(rq_args[i % ncopy][:-1] + (st2,))))
-                w4._check(f_mm(*(mm_args[i % ncopy][:-1] + (st2,))))
+                w4._check(f_lin(*(lin_args[i % ncopy][:-1] + (st2,))))
         gph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -358,22 +365,24 @@ def main():
     if small:
         value = lin.weight_bytes() / (wall / args.steps) / 1e9
         unit = "GB/s"
-        roof = {"bound": "hbm", "achieved": lin.gemm_bytes() / t_mm / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        alg = lin.fused_bytes() if fused else lin.gemm_bytes()
+        roof = {"bound": "hbm", "achieved": alg / t_mm / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         value = lin.ops() / (wall / args.steps) / 1e12
         unit = "TOPS"
         roof = {"bound": "mfma", "achieved": lin.ops() / t_mm / 1e12, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "k_gemv" if M <= 64 else "k_gemm"
-    roof["traffic"] = measured_traffic(roof["kernel"], cfg)
+    roof["kernel"] = "k_gemv_fused" if fused else ("k_gemv" if M <= 64 else "k_gemm")
+    roof["traffic"] = measured_traffic("k_gemv" if M <= 64 else "k_gemm", cfg)
     roof["launch_us"] = round(t_mm * 1e6, 3)
     extra = {
-        "rotquant_us": round(t_rq * 1e6, 3),
-        "rotquant_hbm_gbs": round(lin.rotquant_bytes() / t_rq / 1e9, 1),
-        "rotquant_hbm_frac": round(lin.rotquant_bytes() / t_rq / 1e9 / PEAK_HBM_GBS, 4),
+        "fused": fused,
+        "rotquant_us": round(t_rq * 1e6, 3) if t_rq else None,
+        "rotquant_hbm_gbs": round(lin.rotquant_bytes() / t_rq / 1e9, 1) if t_rq else None,
+        "rotquant_hbm_frac": round(lin.rotquant_bytes() / t_rq / 1e9 / PEAK_HBM_GBS, 4) if t_rq else None,
         "gemm_tops": round(lin.ops() / t_mm / 1e12, 2),
         "gemm_weight_gbs": round(lin.weight_bytes() / t_mm / 1e9, 1),
-        "gemm_alg_bytes": lin.gemm_bytes(),
+        "gemm_alg_bytes": lin.fused_bytes() if fused else lin.gemm_bytes(),
         "timed_launch": "eager" if args.eager else "one hip graph of the K steps",
         "input_copies": ncopy,
     }
