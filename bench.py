@@ -185,6 +185,11 @@ def copy_calibration(dev):
     log("bench: %d MiB calibration copies done" % (COPY_BYTES >> 20))
 
 
+def traffic_workload(workload, M, K):
+    """Key of a workload in profiles/traffic.json (small-M entries carry their shape)."""
+    return "small_m_M%d_K%d" % (M, K) if workload == "small_m" else workload
+
+
 def ingest_counters(fetch_dir, write_dir, workload):
     """Per-dispatch FETCH_SIZE and WRITE_SIZE of the dominant kernels, each scaled by the bytes
     per counter unit that the same counter shows for the calibration copy (which reads and
@@ -234,7 +239,8 @@ def ingest_counters(fetch_dir, write_dir, workload):
 def main():
     args = parse()
     if args.ingest_counters:
-        return ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.workload)
+        return ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
+                               traffic_workload(args.workload, args.M or 16, args.K))
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -416,7 +422,7 @@ def measured_traffic(kernel, cfg):
         data = json.load(open(path))
     except ValueError:
         return None
-    key = "%s:%s" % (kernel, cfg["workload"])
+    key = "%s:%s" % (kernel, traffic_workload(cfg["workload"], cfg.get("M"), cfg.get("K")))
     ent = data.get(key)
     if not ent:
         return None
