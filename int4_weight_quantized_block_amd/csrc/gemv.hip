@@ -1092,7 +1092,7 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
     const int CB = K * ABITS / 8;  // code bytes per token
     const uint32_t smem_base = lds_addr(smem);
     const uint32_t xr = asym ? 0x88888888u : 0u;
-    const int D = min(nst, DM);  // stages in flight: all of them when they fit
+    const int D = min(nst, DM);  // stages in flight
     const int ring = wave * DM * F::WB;
 
     // ---- 1. loads: X, the first D weight stages, the constants
@@ -1112,8 +1112,7 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
 #pragma unroll
         for (int j = 0; j < LB; ++j) gl_lds16_so(bbase, brow[j] + bin[j] + (uint32_t)i * (KST / 2), slot + 1024 * j);
     };
-    const int D0 = min(nst, kStreamDepth);  // stages issued before X has landed
-    for (int i = 0; i < D0; ++i) issue(i);
+    for (int i = 0; i < D; ++i) issue(i);
     if (wave == 0) {  // kNC loads like the streaming kernel; token scales and rowsums come from step 3
         const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(lane, R - 1), p.N - 1) - n0);
         const uint64_t sw = (uint64_t)(p.sw + n0);
@@ -1126,14 +1125,11 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
         gl_lds4_so(sw, 4 * c, smem_base + F::C_DUMMY);
         gl_lds4_so(sw, 4 * c, smem_base + F::C_DUMMY + 256);
     }
-    // this wave's X pieces have landed (the stages and constants issued after them may still
-    // be in flight); then the rest of the first D stages, so the weight stream runs on while
-    // the tokens are rotated.  (Issuing all of them before X lands delays X behind the
-    // workgroups' weight requests.)
-    if (wave == 0) wait_rem<LB, kStreamDepth, kNC>(D0);
-    else wait_rem<LB, kStreamDepth>(D0);
+    // this wave's X pieces have landed; the stages and constants issued after them may still
+    // be in flight, so the weight stream runs on while the tokens are rotated
+    if (wave == 0) wait_rem<LB, DM, kNC>(D);
+    else wait_rem<LB, DM>(D);
     __syncthreads();  // every wave's X pieces
-    for (int i = D0; i < D; ++i) issue(i);
 
     // ---- 2. rotate: 16-lane group lg takes blocks u = lg + 4 NW pp (pp < P, uniform)
     const int lg = tid >> 4, cl = tid & 15;
@@ -1268,7 +1264,7 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
     const int tt = min(lr, M - 1);
     const uint8_t *codes = smem + F::XOFF + tt * CB;
     for (int i = 0; i < nst; ++i) {
-        if (wave == 0 && i < D0) wait_rem<LB, DM - 1, kNC>(min(D - 1, nst - 1 - i));
+        if (wave == 0 && i < D) wait_rem<LB, DM - 1, kNC>(min(D - 1, nst - 1 - i));
         else wait_rem<LB, DM - 1>(min(D - 1, nst - 1 - i));
         const uint8_t *sl = smem + ring + (i % D) * F::WB;
         const uint8_t *cw = codes + (i * NW + wave) * TB;  // this wave's 256-k window
