@@ -340,3 +340,23 @@ def test_fused_small_m_equals_two_launches(M, N, K, g, bits, asym, bias_dtype, l
     a2 = w4.w4_linear_cached_rot(q, s, rs, bits, packed, scale, zp, out_i32=True)
     assert torch.equal(a1, a2)
     assert bool(torch.isfinite(y1.float()).all()) and float(y1.float().abs().max()) > 0
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_fused_small_m_zero_token(asym):
+    """An all-zero token through the fused launch: token scale 0, codes 0, so the output is the
+    bias alone (rounded to bf16), and it equals the two-launch path bit for bit."""
+    N, K = 2048, 4096
+    say("fused small-M zero token N=%d K=%d asym=%s" % (N, K, asym))
+    assert w4.w4_linear_fused(1, N, K, 256, 8)
+    r = rng(N + K + asym)
+    X = torch.zeros((1, K), dtype=torch.bfloat16, device=DEV)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    packed, scale, zp = w4.w4_pack_weights(W, 256, asym)
+    y1 = w4.w4_linear(X, 256, 8, packed, scale, zp, bias=bias)
+    q, s, rs = w4.w4_rotate_quant_act(X, 256, 8)
+    assert float(s[0]) == 0.0 and int(rs[0]) == 0 and not bool(q.any())
+    y2 = w4.w4_linear_cached_rot(q, s, rs, 8, packed, scale, zp, bias=bias)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1[0].view(torch.int16), bias.view(torch.int16))
