@@ -719,11 +719,11 @@ hipError_t split_mb(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hip
 // R rows (8 rows x 128 bytes per 1 KB load), D stages ahead, and multiplies a stage as soon
 // as its own loads have landed; no workgroup barrier until the final reduction.
 //
-// With one workgroup per CU a SIMD runs NW / 4 waves, so little hides a wave's own latency:
-// the time from a stage landing to the next stage being issued (LDS reads, the issue's
-// address arithmetic) throttles the stream.  The loop therefore keeps that path short: load
-// offsets advance by a fixed stride per stage, and when K is a whole number of stages
-// (KFULL) there is no clamping of chunks past K and no masking of their codes.
+// With one workgroup per CU a SIMD runs NW / 4 waves, so little hides a wave's own latency.
+// The loop is kept short (measured): load offsets advance by a fixed stride per stage, and
+// when K is a whole number of stages (KFULL) there is no clamping of chunks past K and no
+// masking of their codes.  Deeper rings, and issuing a stage before waiting for the oldest
+// one, measured slower.
 constexpr int kStreamLds = 144 * 1024;
 constexpr int kStreamDepth = 2;   // stages in flight per wave (2 to 4 measured: deeper only
                                   // lengthens the start, as every wave waits for its first stage)
