@@ -151,7 +151,7 @@ int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *t
  * w4_linear_cached_rot.  Arguments as above; ws must hold at least
  * w4_workspace_bytes(M, N, K, act_bits, r) + room for the activation codes, i.e.
  * w4_linear_workspace_bytes(M, N, K, act_bits, r_needed).  For one bf16 token (M = 1,
- * K <= 16384, N <= 16 x the compute units, K a multiple of 2048) a single kernel rotates,
+ * K <= 16384, N <= 32 x the compute units, K a multiple of 2048) a single kernel rotates,
  * quantizes and multiplies, the fused ConvRot path of the INT4 README ("Inference / INT4");
  * Y is the same bit for bit, and the workspace then holds no codes (its contents are
  * scratch either way). */

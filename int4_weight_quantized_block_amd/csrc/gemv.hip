@@ -978,6 +978,9 @@ __global__ void __launch_bounds__(64 * NW) k_gemv_stream(LinearArgs p, int asym)
         }
     }
 
+    // wave 0's constants were issued after the first D stages; with nst <= D no wait of the
+    // loop covered them, so drain every load before the epilogue reads them
+    wait_vmcnt<0>();
     stream_epilogue<ABITS, RB, NW>(p, smem, acc, n0, asym, L::C_SW, L::C_BIAS, L::C_ZP, L::C_SX, L::C_RS);
 }
 
@@ -1053,11 +1056,11 @@ constexpr int kFuseDMax = 2;          // weight stages in flight per wave (deepe
                                       // slower: the rotation then trails the stream)
 constexpr int kFusePMax = kFuseMaxElems / (4 * kFuseNW * 256);  // 256-element blocks per 16-lane group
 
-template <int ABITS, int TM, int G>
+template <int ABITS, int TM, int G, int RB>
 struct FL {
     static constexpr int NW = kFuseNW;
     static constexpr int D = kFuseDMax;
-    static constexpr int LB = 2;         // weight loads per stage: 16 rows x 128 bytes
+    static constexpr int LB = 2 * RB;    // weight loads per stage: 16 RB rows x 128 bytes
     static constexpr int WB = LB * 1024;
     static constexpr int RING = NW * D * WB;
     static constexpr int XOFF = RING;    // X (bf16), then the codes over it
@@ -1070,12 +1073,12 @@ struct FL {
                   "fused layout");
 };
 
-template <int ABITS, int TM, int G>
+template <int ABITS, int TM, int G, int RB>
 __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const uint16_t *__restrict__ X, int asym) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-    using F = FL<ABITS, TM, G>;
+    using F = FL<ABITS, TM, G, RB>;
     constexpr int NW = F::NW;
-    constexpr int R = 16;
+    constexpr int R = 16 * RB;
     constexpr int DM = F::D, LB = F::LB;
     constexpr int KST = 256 * NW;
     constexpr int QMAX = ABITS == 8 ? 127 : 7;
@@ -1259,8 +1262,11 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
     }
 
     // ---- 4. the streaming loop over the weights
-    v4i acc[2][1];
-    acc[0][0] = acc[1][0] = v4i{0, 0, 0, 0};
+    v4i acc[2][RB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[h][rb] = v4i{0, 0, 0, 0};
     const int tt = min(lr, M - 1);
     const uint8_t *codes = smem + F::XOFF + tt * CB;
     for (int i = 0; i < nst; ++i) {
@@ -1268,7 +1274,7 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
         else wait_rem<LB, DM - 1>(min(D - 1, nst - 1 - i));
         const uint8_t *sl = smem + ring + (i % D) * F::WB;
         const uint8_t *cw = codes + (i * NW + wave) * TB;  // this wave's 256-k window
-        uint4 xa[2][ABITS == 8 ? 2 : 1], wv[2];
+        uint4 xa[2][ABITS == 8 ? 2 : 1], wv[2][RB];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             if constexpr (ABITS == 8) {
@@ -1278,7 +1284,11 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
             } else {
                 xa[u][0] = *reinterpret_cast<const uint4 *>(cw + 16 * ((4 * u + kb) ^ (tt & 7)));
             }
-            wv[u] = *reinterpret_cast<const uint4 *>(sl + lr * 128 + 16 * swz8(lr, 4 * u + kb));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r = 16 * rb + lr;
+                wv[u][rb] = *reinterpret_cast<const uint4 *>(sl + r * 128 + 16 * swz8(r, 4 * u + kb));
+            }
         }
         wait_lgkmcnt0();
         if (i + D < nst) issue(i + D);
@@ -1292,43 +1302,57 @@ __global__ void __launch_bounds__(64 * kFuseNW) k_gemv_fused(LinearArgs p, const
                 a0 = evod(xa[u][0].x, xa[u][0].y);
                 a1 = evod(xa[u][0].z, xa[u][0].w);
             }
-            uint4 w = wv[u];
-            w.x ^= xr; w.y ^= xr; w.z ^= xr; w.w ^= xr;
-            v4i w0, w1;
-            if constexpr (ABITS == 8) {
-                uint32_t q[8];
-                unpack_nat(w.x, q[0], q[1]);
-                unpack_nat(w.y, q[2], q[3]);
-                unpack_nat(w.z, q[4], q[5]);
-                unpack_nat(w.w, q[6], q[7]);
-                w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
-                w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
-            } else {
-                w0 = evod(w.x, w.y);
-                w1 = evod(w.z, w.w);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                uint4 w = wv[u][rb];
+                w.x ^= xr; w.y ^= xr; w.z ^= xr; w.w ^= xr;
+                v4i w0, w1;
+                if constexpr (ABITS == 8) {
+                    uint32_t q[8];
+                    unpack_nat(w.x, q[0], q[1]);
+                    unpack_nat(w.y, q[2], q[3]);
+                    unpack_nat(w.z, q[4], q[5]);
+                    unpack_nat(w.w, q[6], q[7]);
+                    w0 = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+                    w1 = v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+                } else {
+                    w0 = evod(w.x, w.y);
+                    w1 = evod(w.z, w.w);
+                }
+                acc[u][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc[u][rb], 0, 0, 0);
+                acc[u][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc[u][rb], 0, 0, 0);
             }
-            acc[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc[u][0], 0, 0, 0);
-            acc[u][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc[u][0], 0, 0, 0);
         }
     }
-    stream_epilogue<ABITS, 1, NW>(p, smem, acc, n0, asym, F::C_SW, F::C_BIAS, F::C_ZP, F::C_SX, F::C_RS);
+    // as in the streaming kernel: with nst <= D no wait of the loop covered the constants
+    wait_vmcnt<0>();
+    stream_epilogue<ABITS, RB, NW>(p, smem, acc, n0, asym, F::C_SW, F::C_BIAS, F::C_ZP, F::C_SX, F::C_RS);
 }
 
-template <int ABITS, int TM, int G>
+template <int ABITS, int TM, int G, int RB>
 hipError_t launch_fused_t(const LinearArgs &a, const void *X, hipStream_t st) {
-    using F = FL<ABITS, TM, G>;
-    const void *fn = reinterpret_cast<const void *>(&k_gemv_fused<ABITS, TM, G>);
+    using F = FL<ABITS, TM, G, RB>;
+    const void *fn = reinterpret_cast<const void *>(&k_gemv_fused<ABITS, TM, G, RB>);
     static const hipError_t attr = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, F::LDS);
     if (attr != hipSuccess) return attr;
-    const unsigned grid = (unsigned)((a.N + 15) / 16);
-    hipLaunchKernelGGL((k_gemv_fused<ABITS, TM, G>), dim3(grid), dim3(64 * kFuseNW), F::LDS, st, a,
+    const unsigned grid = (unsigned)((a.N + 16 * RB - 1) / (16 * RB));
+    hipLaunchKernelGGL((k_gemv_fused<ABITS, TM, G, RB>), dim3(grid), dim3(64 * kFuseNW), F::LDS, st, a,
                        static_cast<const uint16_t *>(X), a.zp ? 1 : 0);
     return hipGetLastError();
 }
 
+// Rows per workgroup of the fused launch: enough 16-row blocks that the grid stays within
+// one workgroup per CU (each workgroup repeats the rotation); at most 2 by gemv_fusable.
+int fused_row_blocks(int64_t N) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return (int)((N + 16 * (int64_t)ncu - 1) / (16 * (int64_t)ncu));
+}
+
 template <int ABITS, int G>
 hipError_t fused_tm(const LinearArgs &a, const void *X, hipStream_t st) {
-    return launch_fused_t<ABITS, 1, G>(a, X, st);
+    return fused_row_blocks(a.N) <= 1 ? launch_fused_t<ABITS, 1, G, 1>(a, X, st)
+                                      : launch_fused_t<ABITS, 1, G, 2>(a, X, st);
 }
 
 }  // namespace
@@ -1353,14 +1377,15 @@ hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_by
 }
 
 // Fused where it measured faster than the two launches: one token (at 2 to 4 tokens the
-// rotation outlasts the weight stages in flight), one workgroup per CU (more would repeat
-// the rotation on each CU), whole stages.  The kernel itself takes up to 4 tokens.
+// rotation outlasts the weight stages in flight), at most one workgroup per CU with up to 32
+// rows each (more workgroups would repeat the rotation on each CU; 48 rows measured level
+// with the two launches), whole stages.  The kernel itself takes up to 4 tokens.
 bool gemv_fusable(int64_t M, int64_t N, int64_t K, int g, int act_bits, bool f32in) {
     if (f32in || M != 1 || M * K > kFuseMaxElems || (g != 64 && g != 256) || (act_bits != 8 && act_bits != 4))
         return false;
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    return (N + 15) / 16 <= ncu && K % (256 * kFuseNW) == 0;
+    return (N + 31) / 32 <= ncu && K % (256 * kFuseNW) == 0;
 }
 
 hipError_t launch_gemv_fused(const LinearArgs &a, const void *X, int g, int act_bits, hipStream_t st) {

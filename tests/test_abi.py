@@ -190,13 +190,15 @@ def test_rotation_cache_keys(monkeypatch):
 
 def test_linear_fused_query(lib):
     """w4_linear runs fused only for one bf16 token with K <= 16384 in whole 2048-k stages and
-    N within one 16-row workgroup per compute unit (256 on MI355X, the default without a GPU)."""
+    N within one workgroup of up to 32 rows per compute unit (256 on MI355X, the default
+    without a GPU)."""
     bf, f32 = w4.W4_BF16, w4.W4_F32
     assert lib.w4_linear_fused(1, 4096, 12288, 256, 8, bf) == 1
     assert lib.w4_linear_fused(1, 4096, 16384, 64, 4, bf) == 1
     assert lib.w4_linear_fused(1, 4096, 12288, 256, 8, f32) == 0      # fp32 input
     assert lib.w4_linear_fused(2, 4096, 4096, 256, 8, bf) == 0        # two tokens
-    assert lib.w4_linear_fused(1, 4097, 4096, 256, 8, bf) == 0        # more than one workgroup per CU
+    assert lib.w4_linear_fused(1, 8192, 4096, 256, 8, bf) == 1        # 32 rows per workgroup
+    assert lib.w4_linear_fused(1, 8193, 4096, 256, 8, bf) == 0        # more than one workgroup per CU
     assert lib.w4_linear_fused(1, 4096, 3072, 256, 8, bf) == 0        # not whole 2048-k stages
     assert lib.w4_linear_fused(1, 4096, 18432, 256, 8, bf) == 0       # K past 16384
     assert lib.w4_linear_fused(1, 4096, 4096, 128, 8, bf) == 0        # unsupported g

@@ -309,8 +309,10 @@ def test_gemm_split_tail_equals_single_pass(M, N, K, bits, asym):
     (1, 520, 4096, 256, 4, False, torch.bfloat16, True),     # fused W4A4, low-rank, ragged N
     (1, 300, 16384, 64, 8, False, None, False),              # fused, largest K (8 stages, ring of 2)
     (1, 64, 2048, 256, 8, True, torch.float32, True),        # fused, one stage (fewer than the ring)
-    (1, 12288, 4096, 256, 8, True, torch.bfloat16, False),   # past one workgroup per CU: two launches
-    (1, 4100, 4096, 256, 8, True, torch.bfloat16, False),    # two launches, ragged N
+    (1, 8192, 4096, 256, 8, True, torch.bfloat16, False),    # fused, 32 rows per workgroup
+    (1, 4100, 4096, 256, 8, True, torch.bfloat16, False),    # fused, 32 rows per workgroup, ragged N
+    (1, 12288, 4096, 256, 8, True, torch.bfloat16, False),   # past 32 rows per CU: two launches
+    (1, 12300, 2048, 64, 4, True, torch.bfloat16, True),     # two launches, ragged N
     (2, 2048, 4096, 256, 8, True, torch.bfloat16, True),     # two tokens: two launches
     (4, 1000, 4096, 256, 8, False, torch.float32, True),     # two launches
 ])
@@ -360,3 +362,34 @@ def test_fused_small_m_zero_token(asym):
     y2 = w4.w4_linear_cached_rot(q, s, rs, 8, packed, scale, zp, bias=bias)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(y1[0].view(torch.int16), bias.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,g,bits,asym", [
+    (1, 12300, 2048, 64, 4, True),     # 4 waves, 3 workgroups per CU, 2 stages = the ring depth
+    (4, 12288, 1024, 256, 8, True),    # one stage
+    (16, 8192, 2048, 256, 4, False),   # 16 tokens, 2 row blocks, 2 stages
+    (8, 5000, 2048, 256, 8, True),     # ragged N
+    (1, 2048, 2048, 256, 8, True),     # fused, one stage
+    (1, 4096, 4096, 64, 8, True),      # fused, 2 stages = the ring depth
+])
+def test_small_m_short_k_constants(M, N, K, g, bits, asym):
+    """Small-M kernels whose whole K fits in the stages issued up front: the per-row constants
+    (row scales, bias, zero points) must have landed before the epilogue reads them.  The
+    bf16 output is the same on every launch, equals w4_linear's, and matches the fp64
+    epilogue of the (exact) int32 accumulators."""
+    say("small-M short K M=%d N=%d K=%d g=%d bits=%d asym=%s" % (M, N, K, g, bits, asym))
+    r = rng(M + N + K + g + 3 * bits)
+    X = act_input(M, K, seed=N + K).to(DEV)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    packed, scale, zp = w4.w4_pack_weights(W, g, asym)
+    q, s, rs = w4.w4_rotate_quant_act(X, g, bits)
+    ys = [w4.w4_linear_cached_rot(q, s, rs, bits, packed, scale, zp, bias=bias) for _ in range(6)]
+    yl = [w4.w4_linear(X, g, bits, packed, scale, zp, bias=bias) for _ in range(6)]
+    for y in ys[1:] + yl:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    acc = np_(w4.w4_linear_cached_rot(q, s, rs, bits, packed, scale, zp, out_i32=True)).astype(np.int64)
+    y64 = oracle.epilogue(acc, np_(s), np_(scale), bias.cpu())
+    err = rel_frob(ys[0], y64)
+    say("  rel frob %.3e" % err)
+    assert err <= FROB_TOL
