@@ -281,6 +281,100 @@ def test_gemm_extremes_and_empty():
         oracle.gemm_i64(np.full((1, 2), 300), np.zeros((1, 2)))
 
 
+# --------------------------------------------------------------------------- bf16 inputs
+def bf16_ieee_value(bits: int) -> float:
+    """Value of a bf16 bit pattern from the IEEE binary format itself: 1 sign bit, 8 exponent
+    bits with bias 127, 7 fraction bits; exponent 0 is subnormal (0.f * 2^-126), exponent 255
+    is inf (fraction 0) or NaN."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_bf16_widening_all_bit_patterns():
+    """Every one of the 65536 bf16 patterns widens to its exact IEEE value, and torch's own
+    bf16 -> float64 cast agrees (NaN patterns stay NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_bits_to_f64(bits)
+    ieee = np.array([bf16_ieee_value(int(b)) for b in bits], dtype=np.float64)
+    nan = np.isnan(ieee)
+    assert nan.sum() == 2 * 127                                 # exponent 255 with a nonzero fraction
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ieee[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ieee[~nan]))   # -0 stays -0
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    via_torch = t.to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(via_torch), nan)
+    assert np.array_equal(via_torch[~nan], mine[~nan])
+    # to_f64 on a bf16 tensor (any shape) is the same widening
+    w = oracle.to_f64(t.reshape(256, 256))
+    assert w.shape == (256, 256) and w.dtype == np.float64
+    assert np.array_equal(np.isnan(w.ravel()), nan)
+    assert np.array_equal(w.ravel()[~nan], ieee[~nan])
+
+
+def test_bf16_widening_hand_values():
+    # 0x3F80 = 1, 0xC000 = -2, 0x3F81 = 1 + 2^-7, 0x0001 = 2^-133 (smallest subnormal), 0x7F7F = max
+    hand = {0x3F80: 1.0, 0xC000: -2.0, 0x3F81: 1.0 + 2.0 ** -7, 0x0001: 2.0 ** -133,
+            0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x8000: -0.0, 0x4049: 3.140625}
+    got = oracle.bf16_bits_to_f64(np.array(list(hand), dtype=np.uint16))
+    assert got.tolist() == list(hand.values())
+
+
+def test_to_f64_widens_f32_exactly_and_rejects_ints():
+    v = np.array([1.0 + 2.0 ** -23, -3.0e38, 1e-45], dtype=np.float32)
+    assert oracle.to_f64(torch.from_numpy(v)).tolist() == [float(x) for x in v]
+    with pytest.raises(TypeError):
+        oracle.to_f64(torch.zeros(3, dtype=torch.int32))
+
+
+# --------------------------------------------------------------------------- GELU glue
+# Standard normal CDF values from printed tables (Phi(x) to 9 decimals).
+PHI_TABLE = {0.0: 0.5, 0.5: 0.691462461, 1.0: 0.841344746, 1.5: 0.933192799, 2.0: 0.977249868,
+             3.0: 0.998650102, -1.0: 0.158655254, -2.0: 0.022750132}
+
+
+def test_gelu_glue_against_normal_cdf_table():
+    """gelu(x) = x * Phi(x): the table's Phi values, rounded once to bf16."""
+    xs = np.array(list(PHI_TABLE), dtype=np.float32)        # every x here is a bf16 value
+    got = oracle.gelu_bf16(torch.from_numpy(xs).to(torch.bfloat16)).float().numpy()
+    want = np.array([float(bf16_exact(Fraction(x) * Fraction(p))) for x, p in PHI_TABLE.items()])
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_gelu_glue_limits_and_symmetry():
+    x = torch.tensor([0.0, 64.0, -64.0, 1000.0, -1000.0], dtype=torch.bfloat16)
+    got = oracle.gelu_bf16(x).float().tolist()
+    assert got == [0.0, 64.0, 0.0, 1000.0, 0.0]
+    # Phi(x) + Phi(-x) = 1, so gelu(x) - gelu(-x) = x before rounding
+    r = rng(31)
+    v = torch.from_numpy(r.standard_normal(4096).astype(np.float32)).to(torch.bfloat16)
+    a = oracle.gelu_bf16(v).double()
+    b = oracle.gelu_bf16(-v).double()
+    assert torch.allclose(a - b, v.double(), rtol=0, atol=2 * 2.0 ** -8 * float(v.double().abs().max()))
+
+
+def test_gelu_glue_matches_library_erf_gelu():
+    """torch's exact (erf) GELU in fp64, rounded to bf16, gives the same bits except where the
+    fp64 value sits within 1e-12 (relative) of a bf16 rounding midpoint."""
+    r = rng(32)
+    v = torch.from_numpy((r.standard_normal(1 << 16) * 3).astype(np.float32)).to(torch.bfloat16)
+    mine = oracle.gelu_bf16(v).view(torch.int16)
+    y64 = torch.nn.functional.gelu(v.double(), approximate="none")
+    ref = y64.to(torch.bfloat16).view(torch.int16)       # fp64 -> bf16 is one RNE rounding in torch
+    diff = (mine != ref).nonzero().flatten()
+    for i in diff.tolist():
+        lo, hi = sorted([float(mine.view(torch.bfloat16)[i]), float(ref.view(torch.bfloat16)[i])])
+        mid = (lo + hi) / 2
+        assert abs(float(y64[i]) - mid) <= 1e-12 * abs(mid), (i, float(v[i]))
+    assert len(diff) <= 4
+
+
 # --------------------------------------------------------------------------- bf16 output
 def test_bf16_rne_matches_torch_cast():
     r = rng(9)
