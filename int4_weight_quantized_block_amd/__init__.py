@@ -21,6 +21,7 @@ from dataclasses import dataclass
 from typing import Optional
 
 import torch
+from torch.autograd.graph import increment_version
 
 __all__ = [
     "W4Error", "library_path", "load_library", "w4_pack_weights", "w4_rotate_quant_act",
@@ -117,6 +118,35 @@ def _opt(t, name, dtypes):
     return None if t is None else _dev(t, name, dtypes)
 
 
+def _shape(t, name: str, shape) -> None:
+    """Raise ValueError unless tensor ``t`` (if given) has exactly ``shape``.
+
+    The C ABI takes bare pointers and cannot see sizes, so every tensor is checked against
+    (M, N, K, r) here, before anything is launched: a short bias or a mis-shaped code
+    buffer would otherwise be read past its end by the kernels."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _matrix(t, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _check_weights(packed, row_scale, zp, bias, N: int, K: int):
+    _shape(packed, "packed", (N, K // 2))
+    _shape(row_scale, "row_scale", (N,))
+    _shape(zp, "zp", (N,))
+    _shape(bias, "bias", (N,))
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -143,8 +173,8 @@ def w4_pack_weights(W: torch.Tensor, g: int, asym: bool = False):
 
     Returns (packed uint8 [N, K/2], row_scale f32 [N], zp uint8 [N] or None)."""
     lib = load_library()
+    N, K = _matrix(W, "W")
     _dev(W, "W", (torch.float32, torch.bfloat16))
-    N, K = W.shape
     packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
     scale = torch.empty((N,), dtype=torch.float32, device=W.device)
     zp = torch.empty((N,), dtype=torch.uint8, device=W.device) if asym else None
@@ -159,8 +189,8 @@ def w4_rotate_quant_act(X: torch.Tensor, g: int, act_bits: int):
 
     Returns (q int8 [M, K] or packed uint8 [M, K/2], tok_scale f32 [M], tok_rowsum int32 [M])."""
     lib = load_library()
+    M, K = _matrix(X, "X")
     _dev(X, "X", (torch.float32, torch.bfloat16))
-    M, K = X.shape
     if act_bits == 8:
         q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     else:
@@ -187,6 +217,19 @@ class LowRank:
     def r(self) -> int:
         return int(self.l2.shape[0])
 
+    def check(self, M: int, N: int, K: int, need_t: bool) -> None:
+        """Shapes against the layer: l2 [r, N]; t [M, r], or x [M, K] and l1 [r, K]."""
+        r, n2 = _matrix(self.l2, "lowrank.l2")
+        if n2 != N:
+            raise ValueError("lowrank.l2 has shape %s, expected [r, %d]" % (tuple(self.l2.shape), N))
+        if self.t is not None:
+            _shape(self.t, "lowrank.t", (M, r))
+        elif need_t:
+            if self.x is None or self.l1 is None:
+                raise ValueError("lowrank needs t, or x and l1")
+            _shape(self.x, "lowrank.x", (M, K))
+            _shape(self.l1, "lowrank.l1", (r, K))
+
     def as_c(self):
         c = _LowRankC()
         c.x = _opt(self.x, "lowrank.x", (torch.bfloat16,))
@@ -199,9 +242,8 @@ class LowRank:
 
 def _y(M, N, out_i32, device, out):
     if out is not None:
+        _shape(out, "out", (M, N))
         _dev(out, "out", (torch.int32,) if out_i32 else (torch.bfloat16,))
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out has shape %s, expected %s" % (tuple(out.shape), (M, N)))
         return out
     return torch.empty((M, N), dtype=torch.int32 if out_i32 else torch.bfloat16, device=device)
 
@@ -219,6 +261,17 @@ def w4_linear_cached_rot(q, tok_scale, tok_rowsum, act_bits: int, packed, row_sc
                          out=None, ws=None):
     """GEMM + fused dequant on codes from ``w4_rotate_quant_act``.  Returns Y [M, N]."""
     lib = load_library()
+    if act_bits not in (4, 8):
+        raise ValueError("act_bits must be 4 or 8, got %r" % (act_bits,))
+    N, Kh = _matrix(packed, "packed")
+    K = 2 * Kh
+    M = _matrix(q, "q")[0]
+    _shape(q, "q", (M, K) if act_bits == 8 else (M, K // 2))
+    _shape(tok_scale, "tok_scale", (M,))
+    _shape(tok_rowsum, "tok_rowsum", (M,))
+    _check_weights(packed, row_scale, zp, bias, N, K)
+    if lowrank is not None:
+        lowrank.check(M, N, K, need_t=not out_i32)
     _dev(q, "q", (torch.int8,) if act_bits == 8 else (torch.uint8,))
     _dev(tok_scale, "tok_scale", (torch.float32,))
     _dev(tok_rowsum, "tok_rowsum", (torch.int32,))
@@ -226,8 +279,6 @@ def w4_linear_cached_rot(q, tok_scale, tok_rowsum, act_bits: int, packed, row_sc
     _dev(row_scale, "row_scale", (torch.float32,))
     _opt(zp, "zp", (torch.uint8,))
     _opt(bias, "bias", (torch.float32, torch.bfloat16))
-    M = tok_scale.shape[0]
-    N, K = packed.shape[0], packed.shape[1] * 2
     Y = _y(M, N, out_i32, packed.device, out)
     lrc = lowrank.as_c() if lowrank is not None else None
     r = lowrank.r if (lowrank is not None and lowrank.t is None and not out_i32) else 0
@@ -241,6 +292,8 @@ def w4_linear_cached_rot(q, tok_scale, tok_rowsum, act_bits: int, packed, row_sc
         W4_OUT_I32 if out_i32 else W4_OUT_BF16,
         ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
         _stream(packed.device)))
+    if out is not None:
+        increment_version(out)  # the library wrote it through a raw pointer
     return Y
 
 
@@ -248,15 +301,16 @@ def w4_linear(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,
               lowrank: Optional[LowRank] = None, out_i32: bool = False, out=None, ws=None):
     """The whole layer on X [M, K]: rotate + quantize, GEMM, fused dequant.  Returns Y [M, N]."""
     lib = load_library()
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    _check_weights(packed, row_scale, zp, bias, N, K)
+    if lowrank is not None:
+        lowrank.check(M, N, K, need_t=not out_i32)
     _dev(X, "X", (torch.float32, torch.bfloat16))
     _dev(packed, "packed", (torch.uint8,))
     _dev(row_scale, "row_scale", (torch.float32,))
     _opt(zp, "zp", (torch.uint8,))
     _opt(bias, "bias", (torch.float32, torch.bfloat16))
-    M, K = X.shape
-    N = packed.shape[0]
-    if packed.shape[1] * 2 != K:
-        raise ValueError("packed is [%d, %d] but X has K=%d" % (N, packed.shape[1], K))
     Y = _y(M, N, out_i32, X.device, out)
     lrc = lowrank.as_c() if lowrank is not None else None
     r = lowrank.r if (lowrank is not None and lowrank.t is None and not out_i32) else 0
@@ -269,6 +323,8 @@ def w4_linear(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,
         W4_OUT_I32 if out_i32 else W4_OUT_BF16,
         ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
         _stream(X.device)))
+    if out is not None:
+        increment_version(out)  # the library wrote it through a raw pointer
     return Y
 
 
@@ -277,12 +333,11 @@ def w4_lowrank_down(x: torch.Tensor, l1: torch.Tensor) -> torch.Tensor:
 
     ``l1`` is L1 transposed, bf16 [r, K] (rank-major, like a LoRA down weight)."""
     lib = load_library()
+    M, K = _matrix(x, "x")
+    r = _matrix(l1, "l1")[0]
+    _shape(l1, "l1", (r, K))
     _dev(x, "x", (torch.bfloat16,))
     _dev(l1, "l1", (torch.bfloat16,))
-    M, K = x.shape
-    r = l1.shape[0]
-    if l1.dim() != 2 or l1.shape[1] != K:
-        raise ValueError("l1 has shape %s, expected [r, %d]" % (tuple(l1.shape), K))
     t = torch.empty((M, r), dtype=torch.float32, device=x.device)
     _check(lib.w4_lowrank_down(x.data_ptr(), l1.data_ptr(), M, K, r, t.data_ptr(), _stream(x.device)))
     return t
@@ -304,8 +359,16 @@ class RotationCache:
     stable-diffusion.cpp PR #2010, "Summary": the activation rotation / quantize is
     shared and cached per (input, group size).  The key is the tensor's identity
     (storage pointer, offset, shape, strides, dtype), torch's in-place version counter,
-    g and act_bits; the entry keeps a reference to the input, so its storage cannot be
-    freed and reused while cached.  Scope it to one block / forward and ``clear()`` it."""
+    the current stream, g and act_bits; the entry keeps a reference to the input, so its
+    storage cannot be freed and reused while cached.  Scope it to one block / forward and
+    ``clear()`` it.
+
+    The stream is part of the key because the cached codes are ordered only on the stream
+    that produced them: a lookup from another stream recomputes instead of reading codes
+    with no ordering against their producer.  The version counter sees torch's in-place
+    ops and the ``out=`` buffers of this package's linears (they bump it); a tensor written
+    through some other raw pointer must be bumped by its writer
+    (``torch.autograd.graph.increment_version``) or the cache cleared."""
 
     def __init__(self):
         self._d = {}
@@ -313,9 +376,13 @@ class RotationCache:
         self.misses = 0
 
     @staticmethod
-    def _key(X: torch.Tensor, g: int, act_bits: int):
+    def _stream_of(X: torch.Tensor) -> int:
+        return torch.cuda.current_stream(X.device).cuda_stream if X.is_cuda else 0
+
+    @classmethod
+    def _key(cls, X: torch.Tensor, g: int, act_bits: int):
         return (X.data_ptr(), X.storage_offset(), tuple(X.shape), tuple(X.stride()), X.dtype,
-                X._version, g, act_bits)
+                X._version, cls._stream_of(X), g, act_bits)
 
     def get(self, X: torch.Tensor, g: int, act_bits: int):
         k = self._key(X, g, act_bits)

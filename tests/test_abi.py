@@ -205,3 +205,92 @@ def test_linear_fused_query(lib):
     assert lib.w4_linear_fused(1, 4096, 4096, 256, 5, bf) == 0        # unsupported bits
     assert lib.w4_linear_fused(1, 4096, 4096, 256, 8, 7) == 0         # unknown dtype
     assert w4.w4_linear_fused(1, 4096, 12288, 256, 8) is True
+
+
+def _bf(*shape):
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_mis_shaped_tensors_before_launch():
+    """The C ABI cannot see sizes, so the binding checks every tensor against (M, N, K, r);
+    these CPU tensors never reach the device check or the library."""
+    M, N, K, r = 8, 64, 256, 4
+    i8 = lambda *s: torch.zeros(*s, dtype=torch.int8)
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)
+    good = dict(q=i8(M, K), tok_scale=f32(M), tok_rowsum=i32(M), act_bits=8, packed=u8(N, K // 2),
+                row_scale=f32(N))
+    bad_cases = [
+        dict(q=i8(M, K // 2)),                       # A8 codes must be [M, K]
+        dict(q=u8(M, K), act_bits=4),                # A4 codes must be [M, K/2]
+        dict(tok_scale=f32(M - 1)),
+        dict(tok_rowsum=i32(M + 1)),
+        dict(row_scale=f32(N - 1)),
+        dict(zp=u8(N - 1)),
+        dict(bias=_bf(N - 1)),
+        dict(bias=_bf(1, N)),
+        dict(q=i8(M * K)),                           # not 2-D
+        dict(lowrank=w4.LowRank(l2=_bf(r, N - 1), t=f32(M, r))),
+        dict(lowrank=w4.LowRank(l2=_bf(r, N), t=f32(M, r + 1))),
+        dict(lowrank=w4.LowRank(l2=_bf(r, N), x=_bf(M, K - 2), l1=_bf(r, K))),
+        dict(lowrank=w4.LowRank(l2=_bf(r, N), x=_bf(M, K), l1=_bf(r + 1, K))),
+        dict(lowrank=w4.LowRank(l2=_bf(r, N))),      # neither t nor (x, l1)
+        dict(out=torch.zeros(M, N + 1, dtype=torch.bfloat16)),
+    ]
+    for bad in bad_cases:
+        kw = dict(good)
+        kw.update(bad)
+        with pytest.raises(ValueError):
+            w4.w4_linear_cached_rot(**kw)
+    # the whole layer: X [M, K] against packed [N, K/2]
+    with pytest.raises(ValueError):
+        w4.w4_linear(_bf(M, K + 2), 64, 8, u8(N, K // 2), f32(N))
+    with pytest.raises(ValueError):
+        w4.w4_linear(_bf(M, K), 64, 8, u8(N, K // 2), f32(N), bias=f32(N + 3))
+    with pytest.raises(ValueError):
+        w4.w4_linear(_bf(M, K), 64, 8, u8(N, K // 2), f32(N),
+                     lowrank=w4.LowRank(l2=_bf(r, N), x=_bf(M + 1, K), l1=_bf(r, K)))
+    with pytest.raises(ValueError):
+        w4.w4_lowrank_down(_bf(M, K), _bf(r, K - 8))
+    with pytest.raises(ValueError):
+        w4.w4_rotate_quant_act(_bf(K), 64, 8)
+    with pytest.raises(ValueError):
+        w4.w4_pack_weights(_bf(N, K, 1), 64)
+    # well-shaped CPU tensors get past the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        w4.w4_linear_cached_rot(**good)
+
+
+def test_rotation_cache_key_includes_stream(monkeypatch):
+    calls = []
+    monkeypatch.setattr(w4, "w4_rotate_quant_act", lambda X, g, b: calls.append(1) or ("codes", len(calls)))
+    stream = [11]
+    monkeypatch.setattr(w4.RotationCache, "_stream_of", staticmethod(lambda X: stream[0]))
+    c = w4.RotationCache()
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    a = c.get(x, 256, 8)
+    assert c.get(x, 256, 8) is a and c.hits == 1
+    stream[0] = 12                                   # the same input looked up from another stream
+    b = c.get(x, 256, 8)
+    assert b is not a and c.misses == 2
+
+
+def test_out_buffer_writes_bump_the_version(monkeypatch):
+    """A linear writing into out= bumps its version, so a cache keyed on it recomputes."""
+    class FakeLib:
+        def __getattr__(self, name):
+            return lambda *a: 0 if name.startswith("w4_linear") else 0
+    monkeypatch.setattr(w4, "load_library", lambda: FakeLib())
+    monkeypatch.setattr(w4, "_dev", lambda t, name, dtypes: 0)
+    monkeypatch.setattr(w4, "_stream", lambda d: 0)
+    monkeypatch.setattr(w4, "w4_linear_workspace_bytes", lambda *a: 0)
+    monkeypatch.setattr(w4, "w4_workspace_bytes", lambda *a: 0)
+    M, N, K = 4, 16, 256
+    out = torch.zeros(M, N, dtype=torch.bfloat16)
+    v0 = out._version
+    w4.w4_linear(_bf(M, K), 64, 8, torch.zeros(N, K // 2, dtype=torch.uint8), torch.zeros(N), out=out)
+    assert out._version == v0 + 1
+    w4.w4_linear_cached_rot(torch.zeros(M, K, dtype=torch.int8), torch.zeros(M), torch.zeros(M, dtype=torch.int32),
+                            8, torch.zeros(N, K // 2, dtype=torch.uint8), torch.zeros(N), out=out)
+    assert out._version == v0 + 2
