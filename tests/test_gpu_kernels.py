@@ -393,3 +393,186 @@ def test_small_m_short_k_constants(M, N, K, g, bits, asym):
     err = rel_frob(ys[0], y64)
     say("  rel frob %.3e" % err)
     assert err <= FROB_TOL
+
+
+# --------------------------------------------------------------------------- K-split small-M path
+@pytest.mark.parametrize("M,N,K,g,bits,asym", [
+    (20, 4096, 12288, 256, 8, True),    # S = 8, text-encoder shape
+    (24, 2000, 12288, 256, 8, False),   # S = 8, ragged N
+    (40, 3072, 3072, 256, 4, False),    # S = 2, W4A4
+    (33, 1000, 4096, 64, 4, True),      # S = 2, ragged N and M, W4A4 asymmetric
+    (48, 1536, 3072, 256, 4, True),     # S = 2, three 16-token blocks
+])
+@pytest.mark.parametrize("lr_mode", ["none", "x", "t"])
+def test_small_m_ksplit_matches_oracle(M, N, K, g, bits, asym, lr_mode):
+    """17..48 tokens with a workspace: K is split over S > 1 workgroups whose int32 partial
+    tiles k_gemv_reduce sums in a fixed order before the epilogue (asymmetric correction,
+    low-rank term, bias).  Accumulators on the oracle's codes are exact; the layer output is
+    within the bar of the oracle's fp64 output, with the branch given as (x, L1) or as t."""
+    say("ksplit M=%d N=%d K=%d g=%d bits=%d asym=%s lr=%s" % (M, N, K, g, bits, asym, lr_mode))
+    S = w4.w4_workspace_bytes(M, N, K, bits, 0) // (M * N * 4)
+    assert S > 1, "shape must take the K-split path"
+    r = rng(M * 13 + N + K + bits)
+    X = act_input(M, K, seed=M + 7 * K)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    L1 = torch.from_numpy((r.standard_normal((K, 16)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    L2 = torch.from_numpy((r.standard_normal((16, N)) * 0.2).astype(np.float32)).to(torch.bfloat16)
+    lr = lr_mode != "none"
+    ref = oracle.linear(X, W, g, bits, asym, bias=bias, L1=L1 if lr else None, L2=L2 if lr else None)
+    pw = ref["w"]
+    args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
+    # exact accumulators on the oracle's own codes, through the split kernel
+    qa = ref["a"]["q"] if bits == 8 else ref["a"]["packed"]
+    acc = w4.w4_linear_cached_rot(to_dev(qa), to_dev(ref["a"]["scale"]),
+                                  to_dev(ref["a"]["rowsum"].astype(np.int32)), bits, *args, out_i32=True)
+    assert np.array_equal(np_(acc).astype(np.int64), ref["acc"])
+    # the layer output with the GPU's own rotation and codes
+    Xd = X.to(DEV)
+    low = None
+    if lr_mode == "x":
+        low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.t().contiguous().to(DEV))
+    elif lr_mode == "t":
+        low = w4.LowRank(l2=L2.to(DEV), t=w4.w4_lowrank_down(Xd, L1.t().contiguous().to(DEV)))
+    q, s, rs = w4.w4_rotate_quant_act(Xd, g, bits)
+    y = w4.w4_linear_cached_rot(q, s, rs, bits, *args, bias=bias.to(DEV), lowrank=low)
+    err = rel_frob(y, ref["y64"])
+    say("  rel frob %.3e" % err)
+    assert err <= FROB_TOL
+    if lr:
+        assert rel_frob(torch.from_numpy(ref["y64"] - ref["lr"]), ref["y64"]) > 4 * FROB_TOL
+    # w4_linear on the same shape takes the same split path (workspace sized for it)
+    y2 = w4.w4_linear(Xd, g, bits, *args, bias=bias.to(DEV), lowrank=low)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+# --------------------------------------------------------------------------- exact ties
+def _tie_rows_f32(M, K, g, bits, seed):
+    """Rotated rows X' whose quotients by the token scale are exact half-integers, and the
+    fp32 inputs X = X' . blockdiag(H_g / sqrt(g)) that produce them ((H_g / sqrt(g))^2 = I).
+    Each row holds +-qmax once, so its scale is exactly 1; the other entries are multiples of
+    1/2 inside (-qmax, qmax), most of them odd halves (ties)."""
+    qmax = oracle.QMAX[bits]
+    r = rng(seed)
+    Xr = (r.integers(-2 * qmax + 1, 2 * qmax, size=(M, K)) | 1).astype(np.float64) / 2.0   # odd halves
+    for m in range(M):
+        Xr[m, r.integers(0, K)] = qmax if m % 2 == 0 else -qmax
+    X = oracle.rotate(Xr, g)        # the rotation is its own inverse
+    assert np.array_equal(X.astype(np.float32).astype(np.float64), X), "inputs must be exact in fp32"
+    return torch.from_numpy(X.astype(np.float32)), Xr
+
+
+def _tie_rows_bf16(M, K, g, bits, seed):
+    """Like _tie_rows_f32, for bf16 inputs: a group of g holds either +-qmax alone or a few
+    small half-integers whose signed sums all fit bf16's 8 significant bits."""
+    qmax = oracle.QMAX[bits]
+    r = rng(seed)
+    Xr = np.zeros((M, K))
+    for m in range(M):
+        Xr[m, 0] = qmax if m % 2 == 0 else -qmax
+        for grp in range(1, K // g):
+            pos = r.choice(g, size=3, replace=False) + grp * g
+            Xr[m, pos] = r.choice([-2.5, -1.5, -0.5, 0.5, 1.5, 2.5], size=3)
+    X = oracle.rotate(Xr, g)
+    Xb = torch.from_numpy(X.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(oracle.to_f64(Xb), X), "inputs must be exact in bf16"
+    return Xb, Xr
+
+
+@pytest.mark.parametrize("M,K,g,bits,dtype", [
+    (16, 256, 64, 8, torch.float32), (9, 3072, 64, 4, torch.float32), (5, 4096, 64, 8, torch.float32),
+    (40, 1024, 64, 4, torch.float32), (300, 512, 64, 8, torch.float32),
+    (8, 3072, 256, 8, torch.bfloat16), (3, 12288, 256, 4, torch.bfloat16), (20, 1024, 64, 8, torch.bfloat16),
+])
+def test_rotate_quant_exact_ties_round_half_even(M, K, g, bits, dtype):
+    """Crafted tokens whose rotated values over the token scale (exactly 1) sit exactly on
+    half-integers: the GPU codes must equal the oracle's bit for bit, ties to even, with no
+    tie allowance (both sides compute these values exactly)."""
+    say("rotquant ties M=%d K=%d g=%d bits=%d %s" % (M, K, g, bits, dtype))
+    make = _tie_rows_f32 if dtype == torch.float32 else _tie_rows_bf16
+    X, Xr = make(M, K, g, bits, seed=M + K + bits)
+    ref = oracle.rotate_quant_act(X, g, bits)
+    assert np.array_equal(ref["rotated"], Xr) and np.all(ref["scale"] == 1.0)
+    frac = np.abs(ref["pre"] - np.floor(ref["pre"]))
+    n_ties = int((frac == 0.5).sum())
+    say("  %d exact ties" % n_ties)
+    assert n_ties >= M
+    q, s, rs = w4.w4_rotate_quant_act(X.to(DEV), g, bits)
+    assert np.all(np_(s) == 1.0)
+    qg = np_(q)
+    codes = oracle.unpack_nibbles(qg, signed=True) if bits == 4 else qg
+    assert np.array_equal(codes.astype(np.int64), ref["q"].astype(np.int64))
+    assert np.array_equal(np_(rs).astype(np.int64), ref["rowsum"])
+    # half-even, not half-away: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -2.5 -> -2
+    ties = frac == 0.5
+    assert np.all(codes[ties] % 2 == 0)
+
+
+def test_pack_weights_exact_ties():
+    """Weight rows whose rotated values over the row scale (exactly 1) are half-integers: the
+    packed bytes, scales and zero points equal the oracle's bit for bit.  Asymmetric rows with
+    an odd zero point tell round-then-add-z from rounding after adding z; one row's zero point
+    is itself a tie."""
+    g, K = 64, 256
+    say("pack ties K=%d g=%d" % (K, g))
+    r = rng(77)
+    sym = (r.integers(-13, 14, size=(6, K)) | 1).astype(np.float64) / 2.0   # odd halves in [-6.5, 6.5]
+    for i in range(6):
+        sym[i, r.integers(0, K)] = 7.0 if i % 2 else -7.0                   # scale exactly 1
+    asym = np.zeros((6, K))
+    for i, (lo, hi) in enumerate([(-5.0, 10.0), (-3.0, 12.0), (-7.0, 8.0), (-4.5, 10.5), (-1.0, 14.0),
+                                  (-9.0, 6.0)]):
+        row = (r.integers(int(2 * lo) + 1, int(2 * hi), size=K) | 1) / 2.0
+        row = np.clip(row, lo + 0.5, hi - 0.5)
+        row[0], row[1] = lo, hi                                             # (hi - lo) / 15 = 1
+        asym[i] = row
+    for rot, is_asym in ((sym, False), (asym, True)):
+        W = oracle.rotate(rot, g)
+        assert np.array_equal(W.astype(np.float32).astype(np.float64), W)
+        Wt = torch.from_numpy(W.astype(np.float32))
+        ref = oracle.pack_weights(Wt, g, is_asym)
+        assert np.array_equal(ref["rotated"], rot) and np.all(ref["scale"] == 1.0)
+        assert int((np.abs(ref["pre"] - np.floor(ref["pre"])) == 0.5).sum()) > K
+        packed, s, zp = w4.w4_pack_weights(Wt.to(DEV), g, is_asym)
+        assert np.array_equal(np_(packed), ref["packed"])
+        assert np.array_equal(np_(s), ref["scale"])
+        if is_asym:
+            assert np.array_equal(np_(zp), ref["zp"])
+            assert np.any(ref["zp"] % 2 == 1) and ref["zp"][3] == 4    # odd z; z = rint(4.5) = 4
+
+
+# --------------------------------------------------------------------------- fused path vs oracle
+@pytest.mark.parametrize("N,K,g,bits,asym,lr", [
+    (1000, 8192, 64, 4, True, False),     # W4A4, g = 64, ragged N
+    (520, 4096, 256, 4, False, True),     # W4A4 with the low-rank branch
+    (4096, 12288, 256, 8, True, False),   # the text-encoder shape
+    (300, 16384, 64, 8, False, False),
+])
+def test_fused_single_token_matches_oracle(N, K, g, bits, asym, lr):
+    """The one-launch path compared with the oracle directly: its int32 accumulators equal the
+    oracle's GEMM of the (oracle-checked) activation codes, and its bf16 output is within the
+    bar of the oracle's fp64 output."""
+    say("fused vs oracle N=%d K=%d g=%d bits=%d asym=%s lr=%s" % (N, K, g, bits, asym, lr))
+    assert w4.w4_linear_fused(1, N, K, g, bits)
+    r = rng(N + K + g + bits)
+    X = act_input(1, K, seed=N + 5 * K)
+    W = torch.from_numpy((r.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy((r.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16)
+    L1 = torch.from_numpy((r.standard_normal((K, 16)) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    L2 = torch.from_numpy((r.standard_normal((16, N)) * 0.2).astype(np.float32)).to(torch.bfloat16)
+    ref = oracle.linear(X, W, g, bits, asym, bias=bias, L1=L1 if lr else None, L2=L2 if lr else None)
+    pw = ref["w"]
+    args = (to_dev(pw["packed"]), to_dev(pw["scale"]), to_dev(pw["zp"]) if asym else None)
+    Xd = X.to(DEV)
+    low = w4.LowRank(l2=L2.to(DEV), x=Xd, l1=L1.t().contiguous().to(DEV)) if lr else None
+    y = w4.w4_linear(Xd, g, bits, *args, bias=bias.to(DEV), lowrank=low)
+    err = rel_frob(y, ref["y64"])
+    say("  rel frob %.3e" % err)
+    assert err <= FROB_TOL
+    acc = np_(w4.w4_linear(Xd, g, bits, *args, out_i32=True)).astype(np.int64)
+    q, _, _ = w4.w4_rotate_quant_act(Xd, g, bits)
+    qg = np_(q)
+    codes = oracle.unpack_nibbles(qg, signed=True) if bits == 4 else qg
+    check_codes(codes, ref["a"]["q"], ref["a"]["pre"], "act codes")
+    want = oracle.gemm_i64(codes.astype(np.int8), oracle.weight_operand(pw["packed"], pw["zp"], asym))
+    assert np.array_equal(acc, want)
