@@ -31,7 +31,8 @@
  *    for the calling thread's last error.  Faults during execution surface at
  *    the caller's next synchronization, as for any HIP work.
  *  - M == 0 is a valid no-op.  N >= 1 and K >= g are required.
- *  - Thread-safe: no global state besides the per-thread error message.
+ *  - Thread-safe: no global state besides the per-thread error message and the
+ *    per-device scratch array of w4_linear_noalloc (see there).
  */
 #ifndef W4_H
 #define W4_H
@@ -159,6 +160,27 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
               const uint8_t *packed, const float *row_scale, const uint8_t *zp, const void *bias,
               int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *ws,
               size_t ws_bytes, void *stream);
+
+/* w4_linear_noalloc - w4_linear for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.  Same arguments
+ * as w4_linear minus the workspace; same kernels and the same result (bit for bit, except
+ * that with a low-rank branch a shape whose K-split partials do not fit the scratch runs
+ * unsplit, within the usual bf16 bar of the split result).  Instead of a caller workspace it
+ * uses a file-scope device array of w4_noalloc_scratch_bytes() = 64 MiB that every GPU the
+ * library runs on holds until the process ends.  The codes, token scales and row sums (plus
+ * the low-rank t when computed here) must fit it: M * K (A8) or M * K / 2 (A4) bytes plus
+ * 8 * M plus 4 * M * r, each rounded up to 256 bytes; larger calls fail with
+ * W4_ERR_WORKSPACE before anything is launched.  K-split partial sums use whatever room is
+ * left.  The stream must belong to the current device.  Calls never allocate or free
+ * anything; calls that overlap on one GPU (concurrent streams or threads) share that GPU's
+ * array and race, so the caller orders them.  Nothing in the array has to start at zero. */
+int w4_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
+                      const uint8_t *packed, const float *row_scale, const uint8_t *zp,
+                      const void *bias, int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y,
+                      int y_kind, void *stream);
+
+/* Size in bytes of the per-device scratch array w4_linear_noalloc uses (host-only query). */
+size_t w4_noalloc_scratch_bytes(void);
 
 /* w4_lowrank_down - t = x . L1, f32 [M, r], from bf16 x [M, K] and bf16 l1 = L1 transposed,
  * [r, K] rank-major (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of

@@ -28,7 +28,7 @@ __all__ = [
     "w4_linear_cached_rot", "w4_linear", "w4_lowrank_down", "w4_workspace_bytes",
     "w4_linear_workspace_bytes", "w4_linear_fused", "LowRank", "RotationCache", "W4_OK", "W4_ERR_INVALID_ARG",
     "W4_ERR_SHAPE", "W4_ERR_UNSUPPORTED", "W4_ERR_ALIGN", "W4_ERR_HIP", "W4_ERR_WORKSPACE",
-    "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate",
+    "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate", "w4_linear_noalloc", "w4_noalloc_scratch_bytes",
 ]
 
 W4_OK, W4_ERR_INVALID_ARG, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_HIP, \
@@ -66,6 +66,9 @@ EXPORTS = {
                                   _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "w4_linear": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
                        _I64, _P, _I, _P, _SZ, _P]),
+    "w4_linear_noalloc": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
+                               _I64, _P, _I, _P]),
+    "w4_noalloc_scratch_bytes": (_SZ, []),
     "w4_lowrank_down": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
     "w4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "w4_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
@@ -323,6 +326,41 @@ def w4_linear(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,
         W4_OUT_I32 if out_i32 else W4_OUT_BF16,
         ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
         _stream(X.device)))
+    if out is not None:
+        increment_version(out)  # the library wrote it through a raw pointer
+    return Y
+
+
+def w4_noalloc_scratch_bytes() -> int:
+    return int(load_library().w4_noalloc_scratch_bytes())
+
+
+def w4_linear_noalloc(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,
+                      lowrank: Optional[LowRank] = None, out_i32: bool = False, out=None):
+    """w4_linear without a workspace: the library's per-device scratch array holds the codes.
+
+    For callers that cannot allocate device memory inside the call (graph capture, serving
+    loops): pass ``out`` to keep torch from allocating the output as well.  Calls that overlap
+    on one GPU share the scratch and must be ordered by the caller."""
+    lib = load_library()
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    _check_weights(packed, row_scale, zp, bias, N, K)
+    if lowrank is not None:
+        lowrank.check(M, N, K, need_t=not out_i32)
+    _dev(X, "X", (torch.float32, torch.bfloat16))
+    _dev(packed, "packed", (torch.uint8,))
+    _dev(row_scale, "row_scale", (torch.float32,))
+    _opt(zp, "zp", (torch.uint8,))
+    _opt(bias, "bias", (torch.float32, torch.bfloat16))
+    Y = _y(M, N, out_i32, X.device, out)
+    lrc = lowrank.as_c() if lowrank is not None else None
+    _check(lib.w4_linear_noalloc(
+        X.data_ptr(), _fdtype(X), M, K, g, act_bits, packed.data_ptr(), row_scale.data_ptr(),
+        zp.data_ptr() if zp is not None else None, bias.data_ptr() if bias is not None else None,
+        _fdtype(bias) if bias is not None else W4_BF16,
+        ctypes.byref(lrc) if lrc is not None else None, N, Y.data_ptr(),
+        W4_OUT_I32 if out_i32 else W4_OUT_BF16, _stream(X.device)))
     if out is not None:
         increment_version(out)  # the library wrote it through a raw pointer
     return Y

@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -63,6 +64,45 @@ int check_linear_shape(const char *fn, int64_t M, int64_t N, int64_t K, int act_
     if (K > W4_MAX_K) return fail(W4_ERR_SHAPE, "%s: K=%lld exceeds %d", fn, (long long)K, W4_MAX_K);
     if (act_bits != 4 && act_bits != 8) return fail(W4_ERR_UNSUPPORTED, "%s: act_bits=%d (supported: 4, 8)", fn, act_bits);
     if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31) return fail(W4_ERR_SHAPE, "%s: M or N too large", fn);
+    return W4_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Scratch for w4_linear_noalloc: the workspace of w4_linear (activation codes, token scales,
+// row sums, low-rank t, K-split partials) in a file-scope device array, so that callers who
+// cannot allocate need not pass one.  Every GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` is only a host-side stand-in for the symbol;
+// kernels get the device address from hipGetSymbolAddress, looked up once per device with
+// that device current.  Nothing in it has to start at zero: every byte a call reads was
+// written earlier in the same call.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The stream's device must be the current one (the symbol address is per device).
+int scratch_for_stream(const char *fn, hipStream_t st, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (st) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(st, &sdev);
+        if (e != hipSuccess) return hip_status(e, fn);
+        if ((int)sdev != dev)
+            return fail(W4_ERR_INVALID_ARG, "%s: stream is on device %d, current device is %d", fn, (int)sdev, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_INVALID_ARG, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return W4_OK;
 }
 
@@ -258,10 +298,15 @@ int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *t
                        Y, y_kind, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits, const uint8_t *packed,
-              const float *row_scale, const uint8_t *zp, const void *bias, int bias_dtype, const w4_lowrank *lr,
-              int64_t N, void *Y, int y_kind, void *ws, size_t ws_bytes, void *stream) {
-    const char *fn = "w4_linear";
+// The whole layer: rotate-quantize into the front of ws, then the GEMM half.  The codes,
+// token scales, row sums and (when computed here) the low-rank t must fit ws; the K-split
+// partial sums take whatever room is left (with less, the kernels do not split K).
+// noalloc == false: ws must also hold the partials, as w4_linear documents.  noalloc == true:
+// ws and ws_bytes are ignored; after every argument check the device's scratch array is used.
+static int linear_whole(const char *fn, const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
+                        const uint8_t *packed, const float *row_scale, const uint8_t *zp, const void *bias,
+                        int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *ws,
+                        size_t ws_bytes, hipStream_t st, bool noalloc) {
     if (x_dtype != W4_F32 && x_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: x_dtype=%d", fn, x_dtype);
     if (int e = check_linear_shape(fn, M, N, K, act_bits)) return e;
     if (int e = check_k(fn, K, g)) return e;
@@ -271,16 +316,20 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
     if (M == 0) return ok();
     W4_CHECK_PTR(X);
     const int r = (lr && !lr->t && y_kind == W4_OUT_BF16) ? lr->r : 0;
-    const size_t need = w4_linear_workspace_bytes(M, N, K, act_bits, r > 0 ? r : 0);
-    if (!ws || ws_bytes < need) return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    if (!aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
-    uint8_t *base = static_cast<uint8_t *>(ws);
     const size_t qb = align256(act_bits == 4 ? (size_t)M * (size_t)(K / 2) : (size_t)M * (size_t)K);
-    void *qbuf = base;
-    float *sx = reinterpret_cast<float *>(base + qb);
-    int32_t *rs = reinterpret_cast<int32_t *>(base + qb + align256((size_t)M * 4));
-    uint8_t *rest = base + qb + 2 * align256((size_t)M * 4);
-    const size_t rest_bytes = ws_bytes - (size_t)(rest - base);
+    const size_t front = qb + 2 * align256((size_t)M * 4);
+    if (noalloc) {
+        const size_t need = front + (r > 0 ? align256((size_t)M * (size_t)r * sizeof(float)) : 0);
+        if (need > kScratchBytes)
+            return fail(W4_ERR_WORKSPACE, "%s: needs %zu bytes of scratch (codes, token scales, row sums%s), the "
+                        "limit is %zu", fn, need, r > 0 ? ", low-rank t" : "", kScratchBytes);
+        ws = nullptr;  // looked up after every other check
+        ws_bytes = kScratchBytes;
+    } else {
+        const size_t need = w4_linear_workspace_bytes(M, N, K, act_bits, r > 0 ? r : 0);
+        if (!ws || ws_bytes < need) return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+        if (!aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
+    }
     // Check everything the GEMM half will check before launching the first kernel.
     {
         W4_CHECK_PTR(packed);
@@ -296,7 +345,14 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
             if (!lr->t && (!lr->x || !lr->l1)) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
         }
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (noalloc)
+        if (int e = scratch_for_stream(fn, st, &ws)) return e;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    void *qbuf = base;
+    float *sx = reinterpret_cast<float *>(base + qb);
+    int32_t *rs = reinterpret_cast<int32_t *>(base + qb + align256((size_t)M * 4));
+    uint8_t *rest = base + front;
+    const size_t rest_bytes = ws_bytes - front;
     // a few tokens: one launch rotates, quantizes and multiplies (same result, no codes written)
     if (w4::gemv_fusable(M, N, K, g, act_bits, x_dtype == W4_F32))
         return linear_impl(fn, qbuf, sx, rs, act_bits, packed, row_scale, zp, bias, bias_dtype, lr, M, N, K, Y, y_kind,
@@ -305,6 +361,22 @@ int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_b
     if (e != hipSuccess) return hip_status(e, fn);
     return linear_impl(fn, qbuf, sx, rs, act_bits, packed, row_scale, zp, bias, bias_dtype, lr, M, N, K, Y, y_kind,
                        rest, rest_bytes, st);
+}
+
+int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits, const uint8_t *packed,
+              const float *row_scale, const uint8_t *zp, const void *bias, int bias_dtype, const w4_lowrank *lr,
+              int64_t N, void *Y, int y_kind, void *ws, size_t ws_bytes, void *stream) {
+    return linear_whole("w4_linear", X, x_dtype, M, K, g, act_bits, packed, row_scale, zp, bias, bias_dtype, lr, N, Y,
+                        y_kind, ws, ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+size_t w4_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int w4_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits, const uint8_t *packed,
+                      const float *row_scale, const uint8_t *zp, const void *bias, int bias_dtype,
+                      const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *stream) {
+    return linear_whole("w4_linear_noalloc", X, x_dtype, M, K, g, act_bits, packed, row_scale, zp, bias, bias_dtype,
+                        lr, N, Y, y_kind, nullptr, 0, static_cast<hipStream_t>(stream), true);
 }
 
 }  // extern "C"

@@ -146,6 +146,26 @@ def test_linear_validation(lib):
     assert lin(M=0, ws=None) == w4.W4_OK
 
 
+def test_linear_noalloc_validation(lib):
+    """The no-workspace entry point checks everything before it looks up its scratch array
+    (so none of these calls touches a device)."""
+    def na(M=100, K=256, g=64, bits=8, Y=A, x_dtype=w4.W4_BF16, lr=None, N=64, X=A):
+        return lib.w4_linear_noalloc(X, x_dtype, M, K, g, bits, A, A, None, None, w4.W4_BF16, lr, N, Y,
+                                     w4.W4_OUT_BF16, None)
+    assert lib.w4_noalloc_scratch_bytes() == 64 << 20
+    assert na(M=8192, K=8192) == w4.W4_ERR_WORKSPACE                       # 64 MiB of int8 codes + scales
+    assert b"limit" in lib.w4_last_error()
+    lr = w4._LowRankC(A, A, None, A, 64)                                   # t of 64 ranks on top of the codes
+    assert na(M=8000, K=8192, lr=ctypes.byref(lr)) == w4.W4_ERR_WORKSPACE
+    assert na(Y=None) == w4.W4_ERR_INVALID_ARG
+    assert na(X=U) == w4.W4_ERR_ALIGN
+    assert na(g=16) == w4.W4_ERR_UNSUPPORTED
+    assert na(bits=3) == w4.W4_ERR_UNSUPPORTED
+    assert na(x_dtype=4) == w4.W4_ERR_INVALID_ARG
+    assert na(N=0) == w4.W4_ERR_SHAPE
+    assert na(M=0, X=None) == w4.W4_OK
+
+
 def test_probe_validation(lib):
     assert lib.w4_probe_mfma_rate(0, 10, 1, A, None) == w4.W4_ERR_INVALID_ARG
     assert lib.w4_probe_mfma_rate(8, 0, 1, A, None) == w4.W4_ERR_INVALID_ARG
