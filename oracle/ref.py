@@ -29,6 +29,8 @@ zero handling); each such reading is also listed with the design notes.
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 import torch
 
@@ -38,7 +40,8 @@ __all__ = [
     "QMAX", "to_f64", "hadamard", "rotate", "quant_weights_sym", "quant_weights_asym",
     "quant_act", "pack_nibbles", "unpack_nibbles", "gemm_i64", "epilogue", "bf16_rne",
     "bf16_bits_to_f64", "lowrank", "pack_weights", "rotate_quant_act", "weight_operand",
-    "linear_from_codes", "linear", "gelu_bf16", "num_threads",
+    "linear_from_codes", "linear", "gelu_bf16", "num_threads", "f16_rne", "quant_weights_grouped",
+    "gemm_i64_groups", "epilogue_grouped", "dequant_grouped", "pack_weights_grouped", "linear_grouped",
 ]
 
 # Largest code magnitude for per-token activation codes, by bit width.
@@ -77,17 +80,25 @@ def _popcount(a: np.ndarray) -> np.ndarray:
     return c
 
 
+@functools.lru_cache(maxsize=8)
+def _hadamard_cached(g: int) -> np.ndarray:
+    if g < 1 or g & (g - 1):
+        raise ValueError("g must be a power of two")
+    i = np.arange(g, dtype=np.int64)
+    H = np.where(_popcount(i[:, None] & i[None, :]) % 2 == 0, 1, -1).astype(np.int64)
+    H.setflags(write=False)
+    return H
+
+
 def hadamard(g: int) -> np.ndarray:
     """Unnormalised Sylvester-Hadamard matrix H_g[i, j] = (-1)^popcount(i & j).
 
     [CRUSH] "Inference / INT4" names a Hadamard rotation of the activations in
     blocks of rot_size; the pages never print the matrix.  Reading: the
     Sylvester (Walsh) ordering, no random sign flips, the same matrix for
-    activations and weights, so the rotation cancels in the product."""
-    if g < 1 or g & (g - 1):
-        raise ValueError("g must be a power of two")
-    i = np.arange(g, dtype=np.int64)
-    return np.where(_popcount(i[:, None] & i[None, :]) % 2 == 0, 1, -1).astype(np.int64)
+    activations and weights, so the rotation cancels in the product.  (Built once per g and
+    kept; the caller gets a fresh copy.)"""
+    return _hadamard_cached(int(g)).copy()
 
 
 def rotate(A: np.ndarray, g: int) -> np.ndarray:
@@ -95,11 +106,15 @@ def rotate(A: np.ndarray, g: int) -> np.ndarray:
     matrix multiply per contiguous group of g columns.
 
     [CRUSH] "Forward Pass" step 2 rotates the activations; [SDCPP] "Summary"
-    and "Backend notes" key the rotation by group size (64 and 256 verified).
+    and "Backend notes" key the rotation by group size (64 and 256 verified);
+    [CRUSH] "Nodes" lists the rotation sizes 0/16/64/256/1024/4096.
     Reading: contiguous groups [j*g, (j+1)*g) along K; K % g == 0 (padding to
     in_features is the caller's step 3); normalised by 1/sqrt(g), which is a
-    power of two for g = 4^n, so the scaling is exact."""
+    power of two for g = 4^n, so the scaling is exact.  g = 0 is "no rotation"
+    (the W4A16 path of [CRUSH] "Inference / INT4"): A is returned unchanged."""
     A = np.asarray(A, dtype=np.float64)
+    if g == 0:
+        return A.copy()
     R, K = A.shape
     if K % g:
         raise ValueError("K=%d is not a multiple of g=%d" % (K, g))
@@ -171,6 +186,38 @@ def quant_act(Xr: np.ndarray, bits: int):
     return q, s, q.astype(np.int64).sum(axis=1), pre
 
 
+def f16_rne(v: np.ndarray) -> np.ndarray:
+    """fp64 -> fp16, one round-to-nearest-even (NumPy's double -> half conversion rounds the
+    fp64 value directly, with no intermediate fp32 step; pinned against exact rationals)."""
+    return np.asarray(v, dtype=np.float64).astype(np.float16)
+
+
+def quant_weights_grouped(Wr: np.ndarray, gw: int):
+    """Symmetric int4 codes with one fp16 scale per output row and group of gw inputs.
+
+    [CRUSH] "Weight Format": INT4 weights are uint8 (two per byte) plus weight_scale fp16
+    [out, num_groups].  Reading: groups are contiguous runs of gw along K (num_groups =
+    K / gw); s = fp16(max|w'| / 7) over the group (fp64 division, one rounding to fp16);
+    c = clamp(rint(w' / s), -8, 7) with the division in fp64 by the stored fp16 scale.  A
+    group whose scale is 0 (all zero, or below fp16's smallest subnormal after rounding) gets
+    codes 0; a scale that overflows fp16 is rejected.  Returns (codes int8 [N, K],
+    scale f16 [N, K/gw], pre-round values)."""
+    N, K = Wr.shape
+    if gw < 1 or K % gw:
+        raise ValueError("K=%d is not a multiple of gw=%d" % (K, gw))
+    G = Wr.reshape(N, K // gw, gw)
+    amax = np.max(np.abs(G), axis=2)
+    s = f16_rne(amax / 7.0)
+    if not np.all(np.isfinite(s)):
+        raise OverflowError("group scale exceeds fp16")
+    s64 = s.astype(np.float64)
+    pre = np.zeros_like(G)
+    nz = s64 > 0
+    pre[nz] = G[nz] / s64[nz][:, None]
+    c = np.clip(np.rint(pre), -8, 7).astype(np.int8)
+    return c.reshape(N, K), s, pre.reshape(N, K)
+
+
 # --------------------------------------------------------------------------- nibble codec
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
     """Two 4-bit codes per byte along K, low nibble = even k.
@@ -239,6 +286,30 @@ def epilogue(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray, bias=None, lr=No
     return y
 
 
+def gemm_i64_groups(q: np.ndarray, w: np.ndarray, gw: int) -> np.ndarray:
+    """acc_j[m, n] = sum over k in group j of q[m, k] * w[n, k]: the int64 GEMM of each
+    contiguous group of gw inputs.  Returns int64 [K / gw, M, N]."""
+    K = q.shape[1]
+    if K % gw:
+        raise ValueError("K=%d is not a multiple of gw=%d" % (K, gw))
+    return np.stack([gemm_i64(np.ascontiguousarray(q[:, j:j + gw]), np.ascontiguousarray(w[:, j:j + gw]))
+                     for j in range(0, K, gw)])
+
+
+def epilogue_grouped(acc_g: np.ndarray, s_x: np.ndarray, s_wg: np.ndarray, bias=None, lr=None) -> np.ndarray:
+    """y[m, n] = s_x[m] * sum_j s_w[n, j] * acc_j[m, n] + lr[m, n] + bias[n], in fp64.
+
+    With one weight scale per group the group partial sums are scaled before they are added
+    ([CRUSH] "Weight Format" scales [out, num_groups]; "Inference / INT4" fused dequant)."""
+    sw = s_wg.astype(np.float64)                       # [N, G]
+    y = np.einsum("jmn,nj->mn", acc_g.astype(np.float64), sw) * s_x.astype(np.float64)[:, None]
+    if lr is not None:
+        y = y + lr
+    if bias is not None:
+        y = y + to_f64(bias)[None, :]
+    return y
+
+
 def bf16_rne(y: np.ndarray) -> torch.Tensor:
     """Round fp64 values once to bf16, nearest-even, by explicit quantum arithmetic.
 
@@ -279,6 +350,13 @@ def gelu_bf16(y: torch.Tensor) -> torch.Tensor:
     return bf16_rne(0.5 * x * (1.0 + scipy.special.erf(x / np.sqrt(2.0))))
 
 
+def dequant_grouped(packed: np.ndarray, s_wg: np.ndarray, gw: int) -> np.ndarray:
+    """W_hat[n, k] = s_w[n, k // gw] * c[n, k] in fp64 (exact: fp16 times a small integer)."""
+    c = unpack_nibbles(packed, signed=True).astype(np.float64)
+    N, K = c.shape
+    return (c.reshape(N, K // gw, gw) * s_wg.astype(np.float64)[:, :, None]).reshape(N, K)
+
+
 # --------------------------------------------------------------------------- pipeline
 def pack_weights(W, g: int, asym: bool) -> dict:
     """Offline weight step: rotate rows, quantize per row, pack two nibbles per byte."""
@@ -290,6 +368,15 @@ def pack_weights(W, g: int, asym: bool) -> dict:
     c, s, pre = quant_weights_sym(Wr)
     return {"packed": pack_nibbles(c), "scale": s, "zp": None, "codes": c.astype(np.int16),
             "pre": pre, "rotated": Wr}
+
+
+def pack_weights_grouped(W, g: int, gw: int) -> dict:
+    """Offline step of the grouped-scale format: rotate rows (g = 0: none), quantize per
+    (row, group of gw) with fp16 scales, pack two nibbles per byte."""
+    Wr = rotate(to_f64(W), g)
+    c, s, pre = quant_weights_grouped(Wr, gw)
+    return {"packed": pack_nibbles(c), "scale": s, "codes": c.astype(np.int16), "pre": pre, "rotated": Wr,
+            "gw": gw}
 
 
 def rotate_quant_act(X, g: int, bits: int) -> dict:
@@ -328,3 +415,33 @@ def linear(X, W, g: int, act_bits: int, asym: bool, bias=None, L1=None, L2=None)
                             bias, lr)
     out.update({"w": pw, "a": qa, "lr": lr})
     return out
+
+
+def linear_grouped(X, W, g: int, gw: int, act_bits: int, bias=None, L1=None, L2=None) -> dict:
+    """The layer with grouped fp16 weight scales.
+
+    act_bits 8 / 4: rotate + quantize X per token (g > 0), int64 GEMM per weight group,
+    grouped fp64 epilogue.  act_bits 16 (W4A16, [CRUSH] "Inference / INT4", Triton backend:
+    rot_size 0 unpacks INT4 to a float matrix for a plain GEMM): g must be 0; y = X . W_hat^T
+    in fp64 with W_hat the dequantized weights.  Then lr and bias, one bf16 rounding."""
+    pw = pack_weights_grouped(W, g, gw)
+    lr = lowrank(X, L1, L2) if L1 is not None else None
+    if act_bits == 16:
+        if g != 0:
+            raise ValueError("W4A16 takes unrotated weights (g = 0)")
+        y64 = to_f64(X) @ dequant_grouped(pw["packed"], pw["scale"], gw).T
+        if lr is not None:
+            y64 = y64 + lr
+        if bias is not None:
+            y64 = y64 + to_f64(bias)[None, :]
+        return {"y64": y64, "y": bf16_rne(y64), "w": pw, "lr": lr}
+    if g == 0:
+        raise ValueError("integer activations are rotated (g > 0)")
+    qa = rotate_quant_act(X, g, act_bits)
+    w = weight_operand(pw["packed"], None, False)
+    acc_g = gemm_i64_groups(qa["q"], w, gw)
+    acc = acc_g.sum(axis=0)
+    if acc.size and np.max(np.abs(acc)) >= 2 ** 31:
+        raise OverflowError("accumulator exceeds int32")
+    y64 = epilogue_grouped(acc_g, qa["scale"], pw["scale"], bias, lr)
+    return {"acc": acc, "acc_groups": acc_g, "y64": y64, "y": bf16_rne(y64), "w": pw, "a": qa, "lr": lr}

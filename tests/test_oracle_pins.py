@@ -497,3 +497,209 @@ def test_rotation_helps_with_outlier_channels():
             q, s, _, _ = oracle.quant_act(Xr, bits)
             errs[g] = np.linalg.norm(Xr - s[:, None] * q) / np.linalg.norm(Xr)
         assert errs[256] < errs[64] < errs[1] / 2
+
+
+# --------------------------------------------------------------------------- rotation sizes 16 .. 4096, none
+@pytest.mark.parametrize("g", [1024])
+def test_hadamard_1024_matches_sylvester_recursion(g):
+    assert np.array_equal(oracle.hadamard(g), np.array(sylvester(g)))
+
+
+def test_hadamard_4096_has_the_sylvester_block_structure():
+    """H_4096 = [[H, H], [H, -H]] with H = H_2048, and H_2048 likewise from H_1024 (pinned
+    against the recursion above): the closed form obeys the recursion at these sizes too."""
+    for g in (2048, 4096):
+        H, h = oracle.hadamard(g), oracle.hadamard(g // 2)
+        n = g // 2
+        assert np.array_equal(H[:n, :n], h) and np.array_equal(H[:n, n:], h)
+        assert np.array_equal(H[n:, :n], h) and np.array_equal(H[n:, n:], -h)
+
+
+@pytest.mark.parametrize("g", [16, 1024, 4096])
+def test_rotation_sizes_preserve_products_and_are_involutions(g):
+    r = rng(40 + g)
+    X = r.standard_normal((3, 2 * g))
+    W = r.standard_normal((4, 2 * g))
+    d = oracle.rotate(X, g) @ oracle.rotate(W, g).T - X @ W.T
+    assert np.abs(d).max() < 1e-10
+    assert np.abs(oracle.rotate(oracle.rotate(X, g), g) - X).max() < 1e-12       # (H/sqrt(g))^2 = I
+    e = np.zeros((1, 2 * g))
+    e[0, g + 3] = 1.0                       # a basis vector of the second group
+    col = oracle.rotate(e, g)
+    assert np.all(col[0, :g] == 0)
+    assert np.array_equal(col[0, g:] * np.sqrt(g), oracle.hadamard(g)[3].astype(np.float64))
+
+
+def test_rotation_size_zero_is_identity():
+    X = rng(41).standard_normal((3, 96))
+    assert np.array_equal(oracle.rotate(X, 0), X)
+
+
+# --------------------------------------------------------------------------- grouped fp16 scales
+def f16_exact(v: Fraction) -> float:
+    """Nearest fp16 (ties to even) of an exact rational: 11 significant bits, exponent >= -14
+    (subnormal quantum 2^-24), values rounding to 2^16 or more overflow to inf."""
+    if v == 0:
+        return 0.0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -14)
+    quantum = Fraction(2) ** (e - 10)
+    r = rhe(v / quantum) * quantum
+    if abs(r) >= 65520 - 16:             # max fp16 is 65504; 65520 is the midpoint to 2^16
+        if abs(r) >= 65536:
+            return math.copysign(math.inf, float(v))
+    return float(r)
+
+
+def test_f16_rounding_is_one_rne_step_from_f64():
+    r = rng(50)
+    v = r.standard_normal(4000) * np.exp(r.uniform(-20, 12, 4000))
+    ties = [1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -24 * 2.5, 65504.0 + 8.0,
+            -(2.0 ** -15 + 2.0 ** -25)]
+    # 1 + 2^-11 + 2^-40 is just above a tie: one rounding goes up, rounding through fp32 first
+    # would drop the 2^-40 and land on the tie (down to even)
+    above = [1.0 + 2.0 ** -11 + 2.0 ** -40]
+    v = np.concatenate([v, ties, above, [65519.9, 65520.0, 1e-9, 0.0]])
+    got = oracle.f16_rne(v).astype(np.float64)
+    want = np.array([f16_exact(Fraction(float(x))) for x in v])
+    assert np.array_equal(got, want)
+    assert oracle.f16_rne(np.array(above)).astype(np.float64)[0] == 1.0 + 2.0 ** -10
+
+
+def test_grouped_weight_codes_match_bruteforce():
+    r = rng(51)
+    N, K, gw = 5, 64, 16
+    Wr = r.standard_normal((N, K)) * np.exp(r.uniform(-3, 1, (N, K // gw))).repeat(gw, axis=1)
+    Wr[2, 16:32] = 0.0                                     # an all-zero group
+    c, s, pre = oracle.quant_weights_grouped(Wr, gw)
+    assert c.shape == (N, K) and s.shape == (N, K // gw) and s.dtype == np.float16
+    for n in range(N):
+        for j in range(K // gw):
+            grp = [Fraction(float(x)) for x in Wr[n, j * gw:(j + 1) * gw]]
+            sj = f16_exact(max(abs(x) for x in grp) / 7)
+            assert float(s[n, j]) == sj
+            for i, x in enumerate(grp):
+                want = argmin_code(x / Fraction(sj), -8, 7) if sj else 0
+                assert c[n, j * gw + i] == want
+    assert np.all(s[2, 1] == 0) and np.all(c[2, 16:32] == 0)
+
+
+def test_grouped_weight_ties_and_rejects():
+    # scale exactly 1 (max 7): half-integers round to even
+    Wr = np.array([[7.0, 2.5, -2.5, 0.5, -0.5, 1.5, -6.5, 3.5]])
+    c, s, _ = oracle.quant_weights_grouped(Wr, 8)
+    assert float(s[0, 0]) == 1.0
+    assert c[0].tolist() == [7, 2, -2, 0, 0, 2, -6, 4]
+    with pytest.raises(ValueError):
+        oracle.quant_weights_grouped(np.zeros((2, 96)), 64)
+    with pytest.raises(OverflowError):
+        oracle.quant_weights_grouped(np.full((1, 8), 1e6), 8)
+
+
+def test_group_gemm_sums_to_the_whole_gemm_and_matches_python_ints():
+    r = rng(52)
+    M, N, K, gw = 3, 5, 48, 16
+    q = r.integers(-128, 128, (M, K)).astype(np.int8)
+    w = r.integers(-8, 8, (N, K)).astype(np.int8)
+    acc_g = oracle.gemm_i64_groups(q, w, gw)
+    assert acc_g.shape == (K // gw, M, N)
+    assert np.array_equal(acc_g.sum(0), oracle.gemm_i64(q, w))
+    for j in range(K // gw):
+        for m in range(M):
+            for n in range(N):
+                assert acc_g[j, m, n] == sum(int(q[m, k]) * int(w[n, k]) for k in range(j * gw, (j + 1) * gw))
+
+
+def exact_grouped_pipeline(X, W, bias, g, gw, bits):
+    """The grouped-scale layer in exact rationals: Sylvester rotation, fp16 group scales,
+    codes by round-half-even, per-group integer sums scaled before they are added."""
+    H = sylvester(g) if g else None
+    norm = Fraction(1, int(round(math.sqrt(g)))) if g else 1
+
+    def rot(A):
+        out = []
+        for row in A:
+            r = [Fraction(float(v)) for v in row]
+            if not g:
+                out.append(r)
+                continue
+            o = []
+            for b in range(0, len(r), g):
+                o += [sum(r[b + l] * H[l][i] for l in range(g)) * norm for i in range(g)]
+            out.append(o)
+        return out
+
+    Wr = rot(W)
+    K = len(Wr[0])
+    sw, c = [], []
+    for row in Wr:
+        srow, crow = [], []
+        for j in range(0, K, gw):
+            sj = Fraction(f16_exact(max(abs(v) for v in row[j:j + gw]) / 7))
+            srow.append(sj)
+            crow += [max(-8, min(7, rhe(v / sj))) if sj else 0 for v in row[j:j + gw]]
+        sw.append(srow)
+        c.append(crow)
+    M, N = len(X), len(W)
+    if bits == 16:
+        Xf = [[Fraction(float(v)) for v in row] for row in X]
+        y = [[sum(Xf[m][k] * sw[n][k // gw] * c[n][k] for k in range(K)) + Fraction(float(bias[n]))
+              for n in range(N)] for m in range(M)]
+        return None, y
+    qmax = oracle.QMAX[bits]
+    Xr = rot(X)
+    y, accs = [], []
+    for m in range(M):
+        s = f32_of(max(abs(v) for v in Xr[m]) / qmax)
+        q = [max(-qmax - 1, min(qmax, rhe(v / s))) if s else 0 for v in Xr[m]]
+        row, arow = [], []
+        for n in range(N):
+            parts = [sum(q[k] * c[n][k] for k in range(j, j + gw)) for j in range(0, K, gw)]
+            arow.append(sum(parts))
+            row.append(s * sum(p * sw[n][j] for j, p in enumerate(parts)) + Fraction(float(bias[n])))
+        y.append(row)
+        accs.append(arow)
+    return accs, y
+
+
+@pytest.mark.parametrize("g,gw,bits", [(4, 4, 8), (4, 8, 4), (16, 16, 8), (0, 8, 16), (0, 4, 16)])
+def test_grouped_pipeline_equals_exact_rational_recomputation(g, gw, bits):
+    r = rng(200 + g + gw + bits)
+    M, N, K = 3, 6, 16
+    X = r.standard_normal((M, K)).astype(np.float32)
+    X[:, 2] *= 20.0
+    W = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, 8:] *= 8.0                          # groups of very different magnitude
+    bias = (r.standard_normal(N) * 0.01).astype(np.float32)
+    out = oracle.linear_grouped(X, W, g, gw, bits, bias=bias)
+    accs, y = exact_grouped_pipeline(X, W, bias, g, gw, bits)
+    if accs is not None:
+        assert out["acc"].tolist() == accs
+    yf = np.array([[float(v) for v in row] for row in y])
+    assert np.allclose(out["y64"], yf, rtol=1e-13, atol=1e-300)
+    yb = np.array([[bf16_exact(v) for v in row] for row in y])
+    assert np.array_equal(out["y"].float().numpy().astype(np.float64), yb)
+
+
+def test_w4a16_equals_dequantized_float_product():
+    """W4A16 with no rotation is X times the dequantized weights (the pages' unpack-to-float
+    then GEMM): the fp64 product of bf16 X and fp16-scale-times-code weights is exact enough
+    that a float32 torch matmul of the same operands agrees to 1e-5."""
+    r = rng(53)
+    X = torch.from_numpy(r.standard_normal((16, 256)).astype(np.float32)).to(torch.bfloat16)
+    W = torch.from_numpy((r.standard_normal((32, 256)) * 0.02).astype(np.float32))
+    out = oracle.linear_grouped(X, W, 0, 64, 16)
+    pw = out["w"]
+    codes = oracle.unpack_nibbles(pw["packed"], signed=True).astype(np.float32)
+    Wh = torch.from_numpy(codes.reshape(32, 4, 64) * pw["scale"].astype(np.float32)[:, :, None]).reshape(32, 256)
+    ref = (X.float() @ Wh.T).double().numpy()
+    assert np.abs(out["y64"] - ref).max() <= 1e-5 * np.abs(ref).max()
+    with pytest.raises(ValueError):
+        oracle.linear_grouped(X, W, 64, 64, 16)
+    with pytest.raises(ValueError):
+        oracle.linear_grouped(X, W, 0, 64, 8)
