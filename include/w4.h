@@ -10,8 +10,8 @@
  *   acc[m, n] = sum_k q[m, k] * (c[n, k] - z[n])                     int32, exact
  *   Y  = bf16( acc * s_x[m] * s_w[n] + (X . L1) . L2 + bias[n] )
  *
- * H_g is the Sylvester-ordered Hadamard matrix, g in {64, 256}, groups are
- * contiguous blocks of g along K.  rint is round-half-to-even.  Two 4-bit codes
+ * H_g is the Sylvester-ordered Hadamard matrix, g in {16, 64, 256, 1024, 4096}, groups
+ * are contiguous blocks of g along K.  rint is round-half-to-even.  Two 4-bit codes
  * per byte along K, low nibble = even k.  Symmetric weights: signed codes in
  * [-8, 7] (two's complement nibbles), z = 0, s_w = fp32(max|W'| / 7).
  * Asymmetric weights: unsigned codes in [0, 15] with a zero point z[n] in [0, 15],
@@ -48,7 +48,7 @@ extern "C" {
 #define W4_OK 0
 #define W4_ERR_INVALID_ARG 1 /* null pointer, unknown enum value */
 #define W4_ERR_SHAPE 2       /* negative or zero size, K % g != 0, K out of range */
-#define W4_ERR_UNSUPPORTED 3 /* g not in {64, 256}, act_bits not in {4, 8}, K not tileable */
+#define W4_ERR_UNSUPPORTED 3 /* g, gw or act_bits not supported, K not tileable */
 #define W4_ERR_ALIGN 4       /* a device pointer is not 16-byte aligned */
 #define W4_ERR_HIP 5         /* a HIP launch failed (message from hipGetErrorString) */
 #define W4_ERR_WORKSPACE 6   /* workspace missing or smaller than w4_workspace_bytes() */
@@ -98,8 +98,8 @@ typedef struct w4_lowrank {
  *  packed   : out uint8 [N, K/2]
  *  row_scale: out f32 [N]
  *  zp       : out uint8 [N] zero points; required for W4_ASYM, must be NULL for W4_SYM
- * Requires K % g == 0, g in {64, 256}, K <= W4_MAX_K.  Rotation, scales and quotients are
- * computed in fp64 with IEEE division, exactly as in the definition above. */
+ * Requires K % g == 0, g in {16, 64, 256, 1024, 4096}, K <= W4_MAX_K.  Rotation, scales and
+ * quotients are computed in fp64 with IEEE division, exactly as in the definition above. */
 int w4_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int g, int wmode,
                     uint8_t *packed, float *row_scale, uint8_t *zp, void *stream);
 
@@ -115,10 +115,11 @@ int w4_pack_weights(const void *W, int w_dtype, int64_t N, int64_t K, int g, int
  *  tok_scale : out f32 [M]
  *  tok_rowsum: out int32 [M] = sum_k q[m, k] (used by the asymmetric-weight correction)
  * The rotation runs in fp64 (exact for bf16 inputs); codes equal rint(X'/s_x) up to the
- * last fp64 bit of the quotient.  Requires K % g == 0 and one of: K % 256 == 0 with
- * K <= 32768 (K % 1024 == 0 takes the row-team kernel), or K/16 = C * T for some C in 1..4
- * and T a multiple of g/16 with T <= 512 (every K used by DiT / text-encoder linears
- * qualifies); else W4_ERR_UNSUPPORTED. */
+ * last fp64 bit of the quotient.  Requires K % g == 0; for g = 64 or 256 also one of:
+ * K % 256 == 0 with K <= 32768 (K % 1024 == 0 takes the row-team kernel), or K/16 = C * T for
+ * some C in 1..4 and T a multiple of g/16 with T <= 512 (every K used by DiT / text-encoder
+ * linears qualifies); else W4_ERR_UNSUPPORTED.  g = 16, 1024 and 4096 run a general kernel
+ * (one workgroup per token, two passes over the row) that takes any K % g == 0. */
 int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
                         void *q, float *tok_scale, int32_t *tok_rowsum, void *stream);
 
@@ -181,6 +182,53 @@ int w4_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int g, i
 
 /* Size in bytes of the per-device scratch array w4_linear_noalloc uses (host-only query). */
 size_t w4_noalloc_scratch_bytes(void);
+
+/* ---- Grouped-scale weight format ----------------------------------------------------------
+ * (ComfyUI-INT-Crush README, "Weight Format": INT4 weights are uint8, two values per byte, with
+ *  weight_scale fp16 [out, num_groups]; "Nodes": rot_size 0/16/64/256/1024/4096;
+ *  "Inference / INT4", Triton backend: W4A8 for rot_size > 0, W4A16 for rot_size 0.)
+ * Symmetric signed codes packed as above, [N, K/2], and one fp16 scale per output row and run
+ * of gw consecutive inputs: group_scale [N, K/gw] (row-major, raw fp16 bits),
+ *   s[n, j] = fp16(max over the group of |W'| / 7)   (one rounding from fp64)
+ *   c[n, k] = clamp(rint(W'[n, k] / s[n, k / gw]), -8, 7)      (a zero scale gives codes 0)
+ * gw in {32, 64, 128, 256}; K a multiple of 64 and of gw.  The layer:
+ *   W4A8 / W4A4 (act_bits 8 / 4, g > 0): y = s_x[m] * sum_j s[n, j] * acc_j[m, n] + lr + bias,
+ *     acc_j the exact integer sum of q * c over group j;
+ *   W4A16 (act_bits 16, g = 0, bf16 X): y = sum_k X[m, k] * s[n, k / gw] * c[n, k] + lr + bias,
+ *     group partial sums exact in fp32 (bf16 times small integers), scaled per group.
+ * Y is bf16; W4_OUT_I32 (integer activations only) gives sum_k q * c with no scales. */
+
+/* w4_pack_weights_grouped - offline: rotate each row of W along K in groups of g (g = 0: no
+ * rotation; else g in {16, 64, 256, 1024, 4096}), quantize per (row, run of gw inputs) and pack.
+ *  W           : [N, K] of w_dtype
+ *  packed      : out uint8 [N, K/2]
+ *  group_scale : out fp16 bits [N, K/gw]
+ * A group scale that overflows fp16 (max |W'| > 7 * 65504) is not detected. */
+int w4_pack_weights_grouped(const void *W, int w_dtype, int64_t N, int64_t K, int g, int gw,
+                            uint8_t *packed, uint16_t *group_scale, void *stream);
+
+/* w4_linear_cached_rot_grouped - the GEMM half on codes from w4_rotate_quant_act (act_bits 8 or
+ * 4; tok_rowsum is not needed with symmetric codes).  bias, lr, Y, y_kind as for
+ * w4_linear_cached_rot.  ws: w4_grouped_workspace_bytes(M, N, K, act_bits, gw, r_needed) bytes
+ * (the low-rank t when computed here, then, for M <= 64, optional partial sums of a split of K
+ * over several workgroups; with less room K is not split). */
+int w4_linear_cached_rot_grouped(const void *q, const float *tok_scale, int act_bits,
+                                 const uint8_t *packed, const uint16_t *group_scale, int gw,
+                                 const void *bias, int bias_dtype, const w4_lowrank *lr, int64_t M,
+                                 int64_t N, int64_t K, void *Y, int y_kind, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* w4_linear_grouped - the whole layer on the grouped format.  act_bits 8 / 4: rotate and quantize
+ * X (g in {16, 64, 256, 1024, 4096}) into the workspace, then as above.  act_bits 16: g must be
+ * 0 and X bf16; X feeds the bf16 matrix cores directly.  ws: at least
+ * w4_linear_grouped_workspace_bytes(M, N, K, act_bits, gw, r_needed). */
+int w4_linear_grouped(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,
+                      const uint8_t *packed, const uint16_t *group_scale, int gw, const void *bias,
+                      int bias_dtype, const w4_lowrank *lr, int64_t N, void *Y, int y_kind,
+                      void *ws, size_t ws_bytes, void *stream);
+
+size_t w4_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r);
+size_t w4_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r);
 
 /* w4_lowrank_down - t = x . L1, f32 [M, r], from bf16 x [M, K] and bf16 l1 = L1 transposed,
  * [r, K] rank-major (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of

@@ -29,6 +29,8 @@ __all__ = [
     "w4_linear_workspace_bytes", "w4_linear_fused", "LowRank", "RotationCache", "W4_OK", "W4_ERR_INVALID_ARG",
     "W4_ERR_SHAPE", "W4_ERR_UNSUPPORTED", "W4_ERR_ALIGN", "W4_ERR_HIP", "W4_ERR_WORKSPACE",
     "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate", "w4_linear_noalloc", "w4_noalloc_scratch_bytes",
+    "w4_pack_weights_grouped", "w4_linear_cached_rot_grouped", "w4_linear_grouped",
+    "w4_grouped_workspace_bytes", "w4_linear_grouped_workspace_bytes",
 ]
 
 W4_OK, W4_ERR_INVALID_ARG, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_HIP, \
@@ -69,6 +71,13 @@ EXPORTS = {
     "w4_linear_noalloc": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
                                _I64, _P, _I, _P]),
     "w4_noalloc_scratch_bytes": (_SZ, []),
+    "w4_pack_weights_grouped": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P]),
+    "w4_linear_cached_rot_grouped": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, ctypes.POINTER(_LowRankC),
+                                          _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "w4_linear_grouped": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _I, _P, _I, ctypes.POINTER(_LowRankC),
+                               _I64, _P, _I, _P, _SZ, _P]),
+    "w4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I, _I]),
+    "w4_linear_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I, _I]),
     "w4_lowrank_down": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
     "w4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "w4_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
@@ -363,6 +372,106 @@ def w4_linear_noalloc(X, g: int, act_bits: int, packed, row_scale, zp=None, bias
         W4_OUT_I32 if out_i32 else W4_OUT_BF16, _stream(X.device)))
     if out is not None:
         increment_version(out)  # the library wrote it through a raw pointer
+    return Y
+
+
+# ------------------------------------------------------------------ grouped-scale weight format
+def w4_grouped_workspace_bytes(M, N, K, act_bits, gw, r=0) -> int:
+    return int(load_library().w4_grouped_workspace_bytes(M, N, K, act_bits, gw, r))
+
+
+def w4_linear_grouped_workspace_bytes(M, N, K, act_bits, gw, r=0) -> int:
+    return int(load_library().w4_linear_grouped_workspace_bytes(M, N, K, act_bits, gw, r))
+
+
+def w4_pack_weights_grouped(W: torch.Tensor, g: int, gw: int):
+    """Rotate (g = 0: not at all), quantize per (row, run of gw inputs) and pack W [N, K].
+
+    Returns (packed uint8 [N, K/2], group_scale fp16 [N, K/gw])."""
+    lib = load_library()
+    N, K = _matrix(W, "W")
+    if gw <= 0 or K % gw:
+        raise ValueError("K=%d is not a multiple of gw=%r" % (K, gw))
+    _dev(W, "W", (torch.float32, torch.bfloat16))
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N, K // gw), dtype=torch.float16, device=W.device)
+    _check(lib.w4_pack_weights_grouped(W.data_ptr(), _fdtype(W), N, K, g, gw, packed.data_ptr(),
+                                       scale.data_ptr(), _stream(W.device)))
+    return packed, scale
+
+
+def _check_grouped(packed, group_scale, bias, N, K):
+    _shape(packed, "packed", (N, K // 2))
+    gw = K // int(_matrix(group_scale, "group_scale")[1]) if group_scale.shape[1] else 0
+    _shape(group_scale, "group_scale", (N, K // gw if gw else -1))
+    if gw * group_scale.shape[1] != K:
+        raise ValueError("group_scale width %d does not divide K=%d" % (group_scale.shape[1], K))
+    _shape(bias, "bias", (N,))
+    return gw
+
+
+def w4_linear_cached_rot_grouped(q, tok_scale, act_bits: int, packed, group_scale, bias=None,
+                                 lowrank: Optional[LowRank] = None, out_i32: bool = False, out=None, ws=None):
+    """Grouped-scale GEMM + dequant on codes from ``w4_rotate_quant_act``.  Returns Y [M, N]."""
+    lib = load_library()
+    if act_bits not in (4, 8):
+        raise ValueError("act_bits must be 4 or 8, got %r" % (act_bits,))
+    N, Kh = _matrix(packed, "packed")
+    K = 2 * Kh
+    M = _matrix(q, "q")[0]
+    _shape(q, "q", (M, K) if act_bits == 8 else (M, K // 2))
+    _shape(tok_scale, "tok_scale", (M,))
+    gw = _check_grouped(packed, group_scale, bias, N, K)
+    if lowrank is not None:
+        lowrank.check(M, N, K, need_t=not out_i32)
+    _dev(q, "q", (torch.int8,) if act_bits == 8 else (torch.uint8,))
+    _dev(tok_scale, "tok_scale", (torch.float32,))
+    _dev(packed, "packed", (torch.uint8,))
+    _dev(group_scale, "group_scale", (torch.float16,))
+    _opt(bias, "bias", (torch.float32, torch.bfloat16))
+    Y = _y(M, N, out_i32, packed.device, out)
+    lrc = lowrank.as_c() if lowrank is not None else None
+    r = lowrank.r if (lowrank is not None and lowrank.t is None and not out_i32) else 0
+    ws = _ws(w4_grouped_workspace_bytes(M, N, K, act_bits, gw, r), packed.device, ws)
+    _check(lib.w4_linear_cached_rot_grouped(
+        q.data_ptr(), tok_scale.data_ptr(), act_bits, packed.data_ptr(), group_scale.data_ptr(), gw,
+        bias.data_ptr() if bias is not None else None, _fdtype(bias) if bias is not None else W4_BF16,
+        ctypes.byref(lrc) if lrc is not None else None, M, N, K, Y.data_ptr(),
+        W4_OUT_I32 if out_i32 else W4_OUT_BF16,
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream(packed.device)))
+    if out is not None:
+        increment_version(out)
+    return Y
+
+
+def w4_linear_grouped(X, g: int, act_bits: int, packed, group_scale, bias=None,
+                      lowrank: Optional[LowRank] = None, out_i32: bool = False, out=None, ws=None):
+    """The layer on the grouped-scale format: W4A8 / W4A4 (rotation g > 0) or W4A16 (g = 0,
+    act_bits = 16, bf16 X).  Returns Y [M, N]."""
+    lib = load_library()
+    M, K = _matrix(X, "X")
+    N = _matrix(packed, "packed")[0]
+    gw = _check_grouped(packed, group_scale, bias, N, K)
+    if lowrank is not None:
+        lowrank.check(M, N, K, need_t=not out_i32)
+    _dev(X, "X", (torch.float32, torch.bfloat16))
+    _dev(packed, "packed", (torch.uint8,))
+    _dev(group_scale, "group_scale", (torch.float16,))
+    _opt(bias, "bias", (torch.float32, torch.bfloat16))
+    Y = _y(M, N, out_i32, X.device, out)
+    lrc = lowrank.as_c() if lowrank is not None else None
+    r = lowrank.r if (lowrank is not None and lowrank.t is None and not out_i32) else 0
+    ws = _ws(w4_linear_grouped_workspace_bytes(M, N, K, act_bits, gw, r), X.device, ws)
+    _check(lib.w4_linear_grouped(
+        X.data_ptr(), _fdtype(X), M, K, g, act_bits, packed.data_ptr(), group_scale.data_ptr(), gw,
+        bias.data_ptr() if bias is not None else None, _fdtype(bias) if bias is not None else W4_BF16,
+        ctypes.byref(lrc) if lrc is not None else None, N, Y.data_ptr(),
+        W4_OUT_I32 if out_i32 else W4_OUT_BF16,
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream(X.device)))
+    if out is not None:
+        increment_version(out)
     return Y
 
 

@@ -1,0 +1,519 @@
+// GEMM + dequant for the grouped-scale weight format on gfx950 (large and small M).
+//
+// ComfyUI-INT-Crush README, "Weight Format": INT4 weights are two nibbles per byte plus
+// weight_scale fp16 [out, num_groups]; "Inference / INT4": W4A8 = unpack INT4 to INT8,
+// dynamic activation quantization, INT8 GEMM with fused dequant; W4A16 (rot_size 0) =
+// unpack INT4 to a float matrix and a float GEMM.
+//
+//   W4A8 / W4A4:  y[m, n] = s_x[m] * sum_j s_w[n, j] * acc_j[m, n] + lr[m, n] + bias[n]
+//                 acc_j = sum over group j (gw consecutive k) of q[m, k] * c[n, k]   (int32)
+//   W4A16:        y[m, n] = sum_j s_w[n, j] * sum_{k in j} x[m, k] * c[n, k] + lr + bias
+//
+// Weight codes are signed (symmetric) nibbles.  Group partial sums are exact: int32 on the
+// int8 matrix cores, and on the bf16 ones every product of a bf16 activation and a small
+// integer code is exact with fp32 accumulation.  At the end of each group the lane's
+// accumulators are scaled by the group's fp16 scale into fp32 running sums and restarted.
+//
+// Operands.  Weights are the MFMA A operand (rows = output features), activations the B
+// operand (columns = tokens); a lane ends up holding 4 consecutive features of one token per
+// register group.  A signed nibble moved into the high half of a byte is the int8 value
+// 16 * c; the factor 16 (256 for int4 x int4) goes into the final scale, exactly.  For the
+// bf16 path the same int8 values are converted to bf16 (exact).  k order inside a step is
+// natural (int8 x int8, bf16) or even/odd on both sides (int4 x int4).
+//
+// Tiles.  4 waves, WM x WN of them, each FM x FN blocks of 32 x 32.  Large M: 2 x 2 waves of
+// 2 x 2 blocks (128 x 128 tile), a 3-deep LDS ring of 64-k stages.  Small M (<= 64): 1 x 4
+// waves of FM x 1 blocks (32 or 64 tokens x 128 features), a deeper ring, and K split over
+// several workgroups whose partial sums (fp32, or int32 for the raw output) go to the
+// caller's workspace and are added in a fixed order by k_grp_reduce, which applies the
+// epilogue.  Each stage (activations, weights, and the stage's weight scales, one dword per
+// feature) arrives by direct global -> LDS loads spread evenly over the waves.
+#include <algorithm>
+#include <type_traits>
+
+#include <hip/hip_fp16.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int BK = 64;
+
+enum { kOutBf16 = 0, kOutI32 = 1, kPartF32 = 2, kPartI32 = 3 };
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float fl16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+template <int AT, int FM, int FN, int WM, int WN, int STAGES>
+struct Cfg {
+    static_assert(WM * WN == 4, "four waves");
+    static constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+    static constexpr int AROW = AT == 8 ? BK : AT == 4 ? BK / 2 : 2 * BK;  // activation bytes per row
+    static constexpr int ACT = BM * AROW;
+    static constexpr int WROW = BK / 2;                                     // 32 packed weight bytes
+    static constexpr int WB = BN * WROW;
+    static constexpr int SC = BN * 4;                                       // one dword per feature
+    static constexpr int STAGE = ACT + WB + SC;
+    static constexpr int CA = ACT / 16 / 4;                                 // activation chunks per wave
+    static constexpr int CW = WB / 16 / 4;                                  // weight chunks per wave
+    static constexpr int AI = (CA + 63) / 64;                               // instructions
+    static constexpr int WI = (CW + 63) / 64;
+    static constexpr int LOADS = AI + WI + 1;                               // per wave and stage
+    static constexpr int LDS = STAGES * STAGE;
+    static_assert(BN / 4 <= 64, "one scale instruction per wave");
+    static_assert((STAGES - 1) * LOADS <= 63, "vmcnt range");
+};
+
+// physical 16-byte chunk of logical chunk c in row r (involutions)
+template <int ROWBYTES>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (ROWBYTES == 128) return c ^ (r & 7);
+    else if constexpr (ROWBYTES == 64) return c ^ ((r >> 1) & 3);
+    else return c ^ ((r >> 2) & 1);  // 32-byte rows
+}
+
+struct GrpArgs {
+    const uint8_t *A;        // int8 [M, K], packed int4 [M, K/2], or bf16 [M, K]
+    const float *sx;         // [M] (integer activations)
+    const uint8_t *B;        // packed weights [N, K/2]
+    const uint16_t *gs;      // fp16 [N, K / gw]
+    int gw;
+    const void *bias;
+    int bias_bf16;
+    const float *lr_t;       // [M, r] or null
+    const uint16_t *lr_l2;   // bf16 [r, N]
+    int lr_r;
+    void *Y;
+    int64_t M, N, K;
+    int S;                   // K ranges
+    void *part;              // [S, M, N] partial sums (split)
+};
+
+// Issue the loads of one stage (global k0 .. k0 + 63) into LDS slot `st`.
+template <int AT, int FM, int FN, int WM, int WN, int STAGES>
+__device__ __forceinline__ void issue_stage(const GrpArgs &p, uint8_t *smem, int slot, int64_t m0, int64_t n0,
+                                            int64_t k0, int wave, int lane) {
+    using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
+    const uint32_t base = lds_addr(smem) + slot * C::STAGE;
+    const int ebits = AT == 8 ? 8 : AT == 4 ? 4 : 16;
+    const int64_t krow = (p.K * ebits) / 8;  // activation row bytes
+    // activations
+    {
+        const uint64_t g0 = (uint64_t)(p.A + m0 * krow + (k0 * ebits) / 8);
+#pragma unroll
+        for (int i = 0; i < C::AI; ++i) {
+            const int ci = wave * C::CA + i * 64 + lane;
+            const int r = (ci * 16) / C::AROW, pc = ci % (C::AROW / 16);
+            const int c = swz<C::AROW>(r, pc);
+            const int64_t rr = min<int64_t>(m0 + r, p.M - 1) - m0;
+            if (i * 64 + lane < C::CA)
+                gl_lds16_so(g0, (uint32_t)(rr * krow + 16 * c), base + (wave * C::CA + i * 64) * 16);
+        }
+    }
+    // weights
+    {
+        const uint64_t g0 = (uint64_t)(p.B + n0 * (p.K / 2) + k0 / 2);
+#pragma unroll
+        for (int i = 0; i < C::WI; ++i) {
+            const int ci = wave * C::CW + i * 64 + lane;
+            const int n = ci / 2, pc = ci % 2;
+            const int c = swz<32>(n, pc);
+            const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
+            if (i * 64 + lane < C::CW)
+                gl_lds16_so(g0, (uint32_t)(nn * (p.K / 2) + 16 * c), base + C::ACT + (wave * C::CW + i * 64) * 16);
+        }
+    }
+    // scales of this stage: one dword per feature (gw = 32: the stage's two groups; else the
+    // group holding the stage, zero-extended)
+    {
+        const int64_t ng = p.K / p.gw;
+        const uint64_t g0 = (uint64_t)(p.gs + n0 * ng);
+        const int nf = C::BN / 4;
+        const int n = wave * nf + lane;
+        const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
+        const uint32_t lb = base + C::ACT + C::WB + wave * nf * 4;
+        if (lane < nf) {
+            if (p.gw == 32) gl_lds4_so(g0, (uint32_t)((nn * ng + k0 / 32) * 2), lb);
+            else gl_lds2_so(g0, (uint32_t)((nn * ng + k0 / p.gw) * 2), lb);
+        }
+    }
+}
+
+__device__ __forceinline__ v4i nat16(uint32_t d0, uint32_t d1) {
+    uint32_t a, b, c, d;
+    unpack_nat(d0, a, b);
+    unpack_nat(d1, c, d);
+    return v4i{(int)a, (int)b, (int)c, (int)d};
+}
+
+// 8 codes of one packed dword (k .. k+7) as bf16 values 16 * c in natural order
+__device__ __forceinline__ bf8 bf16_codes(uint32_t d) {
+    const uint32_t e = nib_evens16(d), o = nib_odds16(d);
+    bf8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = (__bf16)(float)(int)(int8_t)(e >> (8 * i));
+        r[2 * i + 1] = (__bf16)(float)(int)(int8_t)(o >> (8 * i));
+    }
+    return r;
+}
+
+template <int AT, int FM, int FN, int WM, int WN, int STAGES, int EPI>
+__global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int tiles_n) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
+    constexpr bool INT = AT != 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // tile and K range: XCD x (blocks dealt round-robin) takes a contiguous run of tiles,
+    // walking M inside each column of tiles so the weight panel stays in its L2
+    const int ntiles = tiles_m * tiles_n;
+    int b = (int)blockIdx.x;
+    const int kp = b / ntiles;
+    b -= kp * ntiles;
+    if (ntiles % 8 == 0) b = (b % 8) * (ntiles / 8) + b / 8;
+    const int tm = b % tiles_m, tn = b / tiles_m;
+    const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t KS = p.K / p.S;
+    const int64_t kbeg = kp * KS;
+    const int nk = (int)(KS / BK);
+
+    // groups end after this many 32-k (int) or 16-k (bf16) steps
+    constexpr int KSTEP = INT ? 32 : 16;
+    constexpr int NSTEP = BK / KSTEP;
+    const int steps_per_group = p.gw / KSTEP;
+
+    typedef typename std::conditional<INT, v16i, fl16>::type AccT;
+    AccT acc[FM][FN];
+    fl16 accf[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                acc[i][j][v] = 0;
+                accf[i][j][v] = 0.0f;
+            }
+        }
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue_stage<AT, FM, FN, WM, WN, STAGES>(p, smem, s, m0, n0, kbeg + s * BK, wave, lane);
+
+    int gstep = 0;  // steps into the current group
+    for (int kt = 0; kt < nk; ++kt) {
+        const int slot = kt % STAGES;
+        // stage kt has landed once at most (stages issued after it) * LOADS remain
+        const int after = min(nk - 1 - kt, STAGES - 2);
+        wait_rem<C::LOADS, STAGES - 2>(after);
+        // publish: every wave's share of stage kt is in LDS and every wave is done with stage
+        // kt - 1, whose slot the loads issued next overwrite (a bare s_barrier: the waits above
+        // are the only ones wanted, not a drain of every stage in flight)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + STAGES - 1 < nk)
+            issue_stage<AT, FM, FN, WM, WN, STAGES>(p, smem, (kt + STAGES - 1) % STAGES, m0, n0,
+                                                    kbeg + (int64_t)(kt + STAGES - 1) * BK, wave, lane);
+        const uint8_t *st = smem + slot * C::STAGE;
+        const uint8_t *wst = st + C::ACT;
+        const uint32_t *sct = reinterpret_cast<const uint32_t *>(st + C::ACT + C::WB);
+#pragma unroll
+        for (int ks = 0; ks < NSTEP; ++ks) {
+            if constexpr (INT) {
+                v4i wf[FN], xf[FM];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = wn * FN * 32 + j * 32 + l32;
+                    const uint2 d = *reinterpret_cast<const uint2 *>(wst + n * 32 + 16 * swz<32>(n, ks) + 8 * h);
+                    wf[j] = AT == 8 ? nat16(d.x, d.y) : evod(d.x, d.y);
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wm * FM * 32 + i * 32 + l32;
+                    if constexpr (AT == 8) {
+                        const uint4 x = *reinterpret_cast<const uint4 *>(st + r * C::AROW + 16 * swz<64>(r, 2 * ks + h));
+                        xf[i] = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+                    } else {
+                        const uint2 x = *reinterpret_cast<const uint2 *>(st + r * C::AROW + 16 * swz<32>(r, ks) + 8 * h);
+                        xf[i] = evod(x.x, x.y);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], xf[i], acc[i][j], 0, 0, 0);
+            } else {
+                bf8 wf[FN], xf[FM];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = wn * FN * 32 + j * 32 + l32;
+                    // codes k = 16 ks + 8 h .. + 7: byte 8 ks + 4 h of the 32-byte stage row
+                    const uint32_t d = *reinterpret_cast<const uint32_t *>(
+                        wst + n * 32 + 16 * swz<32>(n, ks >> 1) + 8 * (ks & 1) + 4 * h);
+                    wf[j] = bf16_codes(d);
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int r = wm * FM * 32 + i * 32 + l32;
+                    xf[i] = *reinterpret_cast<const bf8 *>(st + r * C::AROW + 16 * swz<128>(r, 2 * ks + h));
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+            }
+            if constexpr (EPI == kOutBf16 || EPI == kPartF32) {
+                if (++gstep == steps_per_group) {
+                    gstep = 0;
+                    // group scale of the lane's features: for gw = 32 the stage holds two
+                    // groups, the first in the low half of the feature's dword
+                    const int sh = (p.gw == 32 && (ks * KSTEP) / 32 == 1) ? 16 : 0;
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        float sv[16];
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int nl = wn * FN * 32 + j * 32 + 8 * g + 4 * h;
+                            const uint4 s4 = *reinterpret_cast<const uint4 *>(sct + nl);
+                            const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                sv[4 * g + u] = __half2float(__ushort_as_half((uint16_t)(sw[u] >> sh)));
+                        }
+#pragma unroll
+                        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) {
+                                accf[i][j][v] = fmaf((float)acc[i][j][v], sv[v], accf[i][j][v]);
+                                acc[i][j][v] = 0;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- output.  Block (i, j), lane l, register v: feature n = 8 (v / 4) + 4 h + v % 4 of the
+    // block, token m = l % 32 of the block.
+    constexpr float UNSCALE = AT == 4 ? 1.0f / 256 : 1.0f / 16;
+    constexpr int SHIFT = AT == 4 ? 8 : 4;
+    if constexpr (EPI == kPartF32 || EPI == kPartI32) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * FM * 32 + i * 32 + l32;
+            if (m >= p.M) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t n = n0 + wn * FN * 32 + j * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                    if (n >= p.N) continue;
+                    const int64_t o = ((int64_t)kp * p.M + m) * p.N + n;
+                    if constexpr (EPI == kPartF32) reinterpret_cast<float *>(p.part)[o] = accf[i][j][v];
+                    else reinterpret_cast<int32_t *>(p.part)[o] = acc[i][j][v];
+                }
+        }
+        return;
+    }
+    if constexpr (EPI == kOutI32) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * FM * 32 + i * 32 + l32;
+            if (m >= p.M) continue;
+            int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t n = n0 + wn * FN * 32 + j * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                    if (n < p.N) Y[n] = acc[i][j][v] >> SHIFT;
+                }
+        }
+        return;
+    }
+    // bf16 output: stage the tile's l2 rows in LDS (the ring is free once every wave is past it)
+    const int r = p.lr_t ? p.lr_r : 0;
+    uint16_t *l2s = reinterpret_cast<uint16_t *>(smem);
+    if (r) {
+        __syncthreads();
+        for (int e = tid; e < r * C::BN; e += 256) {
+            const int q = e / C::BN, nl = e % C::BN;
+            const int64_t n = min<int64_t>(n0 + nl, p.N - 1);
+            l2s[e] = p.lr_l2[(int64_t)q * p.N + n];
+        }
+        __syncthreads();
+    }
+    uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * FM * 32 + i * 32 + l32;
+        if (m >= p.M) continue;
+        const float xs = INT ? p.sx[m] * UNSCALE : UNSCALE;
+        const float *tr = r ? p.lr_t + m * r : nullptr;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * FN * 32 + j * 32 + 8 * g + 4 * h;
+                const int64_t n = n0 + nl;
+                float y[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) y[u] = accf[i][j][4 * g + u] * xs;
+                if (r) {
+                    for (int q = 0; q < r; ++q) {
+                        const float t = tr[q];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) y[u] = fmaf(t, bf16_to_f32(l2s[q * C::BN + nl + u]), y[u]);
+                    }
+                }
+                if (p.bias) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t nb = min<int64_t>(n + u, p.N - 1);
+                        y[u] += p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[nb])
+                                            : reinterpret_cast<const float *>(p.bias)[nb];
+                    }
+                }
+                uint16_t *yr = Y + m * p.N;
+                if (n + 3 < p.N && (p.N & 3) == 0) {
+                    *reinterpret_cast<uint2 *>(yr + n) =
+                        make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16), f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (n + u < p.N) yr[n + u] = (uint16_t)f32_to_bf16(y[u]);
+                }
+            }
+    }
+}
+
+// Fixed-order sum of the S partial sums and the epilogue (one thread per output).
+template <int AT, bool I32>
+__global__ void __launch_bounds__(256) k_grp_reduce(GrpArgs p) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.M * p.N) return;
+    const int64_t m = e / p.N, n = e % p.N;
+    const int64_t MN = p.M * p.N;
+    if constexpr (I32) {
+        constexpr int SHIFT = AT == 4 ? 8 : 4;
+        const int32_t *part = reinterpret_cast<const int32_t *>(p.part);
+        int32_t s = 0;
+        for (int k = 0; k < p.S; ++k) s += part[k * MN + e];
+        reinterpret_cast<int32_t *>(p.Y)[e] = s >> SHIFT;
+    } else {
+        constexpr float UNSCALE = AT == 4 ? 1.0f / 256 : 1.0f / 16;
+        const float *part = reinterpret_cast<const float *>(p.part);
+        float s = 0.0f;
+        for (int k = 0; k < p.S; ++k) s += part[k * MN + e];
+        float y = s * (AT != 16 ? p.sx[m] * UNSCALE : UNSCALE);
+        if (p.lr_t)
+            for (int q = 0; q < p.lr_r; ++q) y = fmaf(p.lr_t[m * p.lr_r + q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), y);
+        if (p.bias)
+            y += p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
+                             : reinterpret_cast<const float *>(p.bias)[n];
+        reinterpret_cast<uint16_t *>(p.Y)[e] = (uint16_t)f32_to_bf16(y);
+    }
+}
+
+template <int AT, int FM, int FN, int WM, int WN, int STAGES, int EPI>
+hipError_t launch_cfg(const GrpArgs &a, hipStream_t st) {
+    using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
+    const size_t lds = std::max<size_t>(C::LDS, (size_t)2 * a.lr_r * C::BN);
+    auto kern = k_gemm_grp<AT, FM, FN, WM, WN, STAGES, EPI>;
+    if (lds > 65536) {
+        static const hipError_t attr =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024);
+        if (attr != hipSuccess) return attr;
+    }
+    const int tiles_m = (int)((a.M + C::BM - 1) / C::BM), tiles_n = (int)((a.N + C::BN - 1) / C::BN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n * a.S)), dim3(256), lds, st, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+// K ranges for a small-M grid: about two workgroups per compute unit, each range a whole
+// number of stages and of groups.
+int plan_s(int64_t M, int64_t N, int64_t K, int gw) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t tiles = (N + 127) / 128;
+    int S = 1;
+    while (S < 16 && tiles * S * 2 <= 2 * ncu && K % (2 * S * std::max(gw, BK)) == 0 && K / (2 * S) >= 4 * BK)
+        S *= 2;
+    return S;
+}
+
+template <int AT, int EPI>
+hipError_t launch_at(const GrpArgs &a, hipStream_t st) {
+    if (a.M > 64) return launch_cfg<AT, 2, 2, 2, 2, 3, EPI>(a, st);
+    if (a.M > 32) return launch_cfg<AT, 2, 1, 1, 4, 6, EPI>(a, st);
+    return launch_cfg<AT, 1, 1, 1, 4, 6, EPI>(a, st);
+}
+
+template <int AT, bool I32>
+hipError_t launch_grp(GrpArgs a, void *ws, size_t ws_bytes, hipStream_t st) {
+    a.S = 1;
+    a.part = nullptr;
+    if (a.M <= 64) {
+        const int S = plan_s(a.M, a.N, a.K, a.gw);
+        const size_t need = (size_t)S * a.M * a.N * 4;
+        if (S > 1 && ws && ws_bytes >= need) {
+            a.S = S;
+            a.part = ws;
+            hipError_t e = launch_at<AT, I32 ? kPartI32 : kPartF32>(a, st);
+            if (e != hipSuccess) return e;
+            const int64_t n = a.M * a.N;
+            hipLaunchKernelGGL((k_grp_reduce<AT, I32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    return launch_at<AT, I32 ? kOutI32 : kOutBf16>(a, st);
+}
+
+}  // namespace
+
+size_t grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int gw) {
+    if (M <= 0 || M > 64) return 0;
+    const int S = plan_s(M, N, K, gw);
+    return S > 1 ? (size_t)S * M * N * 4 : 0;
+}
+
+hipError_t launch_gemm_grouped(const GroupedArgs &g, int act_bits, void *ws, size_t ws_bytes, hipStream_t st) {
+    if (g.M == 0) return hipSuccess;
+    GrpArgs a{};
+    a.A = static_cast<const uint8_t *>(g.A);
+    a.sx = g.sx;
+    a.B = g.B;
+    a.gs = g.gs;
+    a.gw = g.gw;
+    a.bias = g.bias;
+    a.bias_bf16 = g.bias_bf16;
+    a.lr_t = g.lr_t;
+    a.lr_l2 = g.lr_l2;
+    a.lr_r = g.lr_t ? g.lr_r : 0;
+    a.Y = g.Y;
+    a.M = g.M;
+    a.N = g.N;
+    a.K = g.K;
+    if (act_bits == 16 && g.y_i32) return hipErrorInvalidValue;
+    switch (act_bits) {
+        case 8: return g.y_i32 ? launch_grp<8, true>(a, ws, ws_bytes, st) : launch_grp<8, false>(a, ws, ws_bytes, st);
+        case 4: return g.y_i32 ? launch_grp<4, true>(a, ws, ws_bytes, st) : launch_grp<4, false>(a, ws, ws_bytes, st);
+        case 16: return launch_grp<16, false>(a, ws, ws_bytes, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4

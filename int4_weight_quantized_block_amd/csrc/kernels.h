@@ -12,9 +12,14 @@ bool rotquant_supported(int64_t K, int g);
 hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st);
 
-// Offline weight rotate + per-row quantize + nibble pack.
+// Offline weight rotate + per-row quantize + nibble pack (g in {0 = none, 16, 64, 256, 1024,
+// 4096}).
 hipError_t launch_pack(const void *W, bool f32in, int64_t N, int64_t K, int g, bool asym,
                        uint8_t *packed, float *row_scale, uint8_t *zp, hipStream_t st);
+// The same with symmetric codes and fp16 scales per (row, run of gw inputs) [N, K/gw];
+// gw divides 4096 and K.
+hipError_t launch_pack_grouped(const void *W, bool f32in, int64_t N, int64_t K, int g, int gw, uint8_t *packed,
+                               uint16_t *group_scale, hipStream_t st);
 
 struct LinearArgs {
     const uint8_t *A;      // activation codes: int8 [M, K] or packed int4 [M, K/2]
@@ -46,6 +51,28 @@ hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_by
 // launch_gemv bit for bit.
 bool gemv_fusable(int64_t M, int64_t N, int64_t K, int g, int act_bits, bool f32in);
 hipError_t launch_gemv_fused(const LinearArgs &a, const void *X, int g, int act_bits, hipStream_t st);
+
+// Grouped-scale format: signed codes [N, K/2] with fp16 scales [N, K/gw] (gw in 32, 64, 128,
+// 256), against int8 / packed int4 activation codes with token scales (act_bits 8 / 4) or
+// bf16 activations (act_bits 16).  K % 64 == 0 and K % gw == 0.  For M <= 64, a workspace of
+// grouped_workspace_bytes() bytes splits K over several workgroups.
+struct GroupedArgs {
+    const void *A;            // int8 [M, K], packed int4 [M, K/2] or bf16 [M, K]
+    const float *sx;          // [M] (act_bits 8 / 4)
+    const uint8_t *B;         // [N, K/2]
+    const uint16_t *gs;       // fp16 [N, K / gw]
+    int gw;
+    const void *bias;         // [N] or null
+    int bias_bf16;
+    const float *lr_t;        // [M, lr_r] or null
+    const uint16_t *lr_l2;    // bf16 [lr_r, N]
+    int lr_r;
+    void *Y;                  // bf16 [M, N], or int32 (act_bits 8 / 4: sum_k q c, no scales)
+    int y_i32;
+    int64_t M, N, K;
+};
+size_t grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int gw);
+hipError_t launch_gemm_grouped(const GroupedArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
 
 // Measurement probe: blocks workgroups of 4 waves, each wave iters rounds of 4 int8 MFMAs.
 hipError_t launch_mfma_rate(int64_t blocks, int iters, bool random_operands, int32_t *sink, hipStream_t st);

@@ -651,9 +651,117 @@ hipError_t launch_stream(const void *X, int64_t M, int64_t K, void *q, float *s,
 
 bool stream_ok(int64_t K) { return K % 256 == 0 && K / 64 <= 512; }
 
+// ---------------------------------------------------------------------------------------------
+// Any rotation size (ComfyUI-INT-Crush README, "Nodes": rot_size 16 / 64 / 256 / 1024 / 4096):
+// one workgroup per token row, the row in slabs of 4096 elements staged in LDS as fp64.
+// Pass 1 transforms each slab with in-place butterflies and reduces max|x'|; pass 2 reads
+// and transforms it again (from L2) and quantizes with the IEEE quotient x' / s.  It serves
+// the sizes the register kernels above do not (16, 1024, 4096); every size divides the slab,
+// so no group straddles two slabs.
+constexpr int kGenSlab = 4096;
+constexpr int kGenThreads = 256;
+
+template <int G, bool F32IN>
+__device__ void gen_load_rotate(const void *X, int64_t row, int K, int k0, int len, double *buf) {
+    const int tid = threadIdx.x;
+    for (int k = tid; k < len; k += kGenThreads) {
+        const int64_t idx = row * K + k0 + k;
+        buf[k] = F32IN ? (double)reinterpret_cast<const float *>(X)[idx]
+                       : (double)bf16_to_f32(reinterpret_cast<const uint16_t *>(X)[idx]);
+    }
+    __syncthreads();
+    for (int h = 1; h < G; h <<= 1) {
+        for (int p = tid; p < len / 2; p += kGenThreads) {
+            const int i = ((p & ~(h - 1)) << 1) | (p & (h - 1));
+            const double a = buf[i], b = buf[i + h];
+            buf[i] = a + b;
+            buf[i + h] = a - b;
+        }
+        __syncthreads();
+    }
+}
+
+template <int G, int BITS, bool F32IN>
+__global__ void __launch_bounds__(kGenThreads)
+k_rotquant_gen(const void *__restrict__ Xv, int K, void *__restrict__ qv, float *__restrict__ tok_scale,
+               int32_t *__restrict__ tok_rowsum) {
+    __shared__ double buf[kGenSlab];
+    __shared__ double red_d[kGenThreads / 64];
+    __shared__ int red_i[kGenThreads / 64];
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 16 ? 0.25 : G == 64 ? 0.125 : G == 256 ? 0.0625 : G == 1024 ? 0.03125
+                                                                                                  : 0.015625;
+    static_assert(G == 16 || G == 64 || G == 256 || G == 1024 || G == 4096, "rotation size");
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+    double am = 0.0;
+    for (int k0 = 0; k0 < K; k0 += kGenSlab) {
+        const int len = min(kGenSlab, K - k0);
+        gen_load_rotate<G, F32IN>(Xv, row, K, k0, len, buf);
+        for (int k = tid; k < len; k += kGenThreads) am = fmax(am, fabs(buf[k]));
+        __syncthreads();
+    }
+    for (int off = 32; off >= 1; off >>= 1) am = fmax(am, __shfl_xor(am, off));
+    if (lane == 0) red_d[w] = am;
+    __syncthreads();
+    am = red_d[0];
+    for (int i = 1; i < kGenThreads / 64; ++i) am = fmax(am, red_d[i]);
+    const float scale = (float)((am * INV_SQRT_G) / (double)QMAX);  // amax / sqrt(g): exact scaling
+    const double sd = (double)scale;
+    if (tid == 0) tok_scale[row] = scale;
+
+    int rowsum = 0;
+    for (int k0 = 0; k0 < K; k0 += kGenSlab) {
+        const int len = min(kGenSlab, K - k0);
+        gen_load_rotate<G, F32IN>(Xv, row, K, k0, len, buf);
+        for (int p = tid; p < len / 2; p += kGenThreads) {
+            int c[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                c[h] = sd > 0.0 ? min(max((int)rint((buf[2 * p + h] * INV_SQRT_G) / sd), -QMAX - 1), QMAX) : 0;
+                rowsum += c[h];
+            }
+            if constexpr (BITS == 8) {
+                int8_t *q = reinterpret_cast<int8_t *>(qv) + row * K + k0 + 2 * p;
+                q[0] = (int8_t)c[0];
+                q[1] = (int8_t)c[1];
+            } else {
+                reinterpret_cast<uint8_t *>(qv)[row * (K / 2) + k0 / 2 + p] =
+                    (uint8_t)((c[0] & 15) | ((c[1] & 15) << 4));
+            }
+        }
+        __syncthreads();
+    }
+    for (int off = 32; off >= 1; off >>= 1) rowsum += __shfl_xor(rowsum, off);
+    if (lane == 0) red_i[w] = rowsum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+        for (int i = 0; i < kGenThreads / 64; ++i) total += red_i[i];
+        tok_rowsum[row] = total;
+    }
+}
+
+template <int G, int BITS, bool F32IN>
+hipError_t launch_gen_t(const void *X, int64_t M, int64_t K, void *q, float *s, int32_t *rs, hipStream_t st) {
+    hipLaunchKernelGGL((k_rotquant_gen<G, BITS, F32IN>), dim3((unsigned)M), dim3(kGenThreads), 0, st, X, (int)K, q,
+                       s, rs);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_gen(const void *X, bool f32in, int64_t M, int64_t K, int bits, void *q, float *s, int32_t *rs,
+                      hipStream_t st) {
+    if (bits == 8) return f32in ? launch_gen_t<G, 8, true>(X, M, K, q, s, rs, st)
+                                : launch_gen_t<G, 8, false>(X, M, K, q, s, rs, st);
+    return f32in ? launch_gen_t<G, 4, true>(X, M, K, q, s, rs, st) : launch_gen_t<G, 4, false>(X, M, K, q, s, rs, st);
+}
+
 }  // namespace
 
 bool rotquant_supported(int64_t K, int g) {
+    if (g == 16 || g == 1024 || g == 4096) return K > 0 && K % g == 0;
     Split sp;
     return stream_ok(K) || choose_split(K, g, sp);
 }
@@ -661,6 +769,10 @@ bool rotquant_supported(int64_t K, int g) {
 hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st) {
     if (M == 0) return hipSuccess;
+    if (g == 16) return launch_gen<16>(X, f32in, M, K, bits, q, tok_scale, tok_rowsum, st);
+    if (g == 1024) return launch_gen<1024>(X, f32in, M, K, bits, q, tok_scale, tok_rowsum, st);
+    if (g == 4096) return launch_gen<4096>(X, f32in, M, K, bits, q, tok_scale, tok_rowsum, st);
+    if (g != 64 && g != 256) return hipErrorInvalidValue;
     int C = 0, W = 0;
     if (row_team_split(M, K, C, W)) {
 #define W4_RT(G, B, F) return launch_row<G, B, F>(X, M, K, C, W, q, tok_scale, tok_rowsum, st)

@@ -50,8 +50,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
         if ((p) && !aligned16(p)) return fail(W4_ERR_ALIGN, "%s: %s not 16-byte aligned", fn, #p); \
     } while (0)
 
+bool rot_size_ok(int g) { return g == 16 || g == 64 || g == 256 || g == 1024 || g == 4096; }
+
 int check_k(const char *fn, int64_t K, int g) {
-    if (g != 64 && g != 256) return fail(W4_ERR_UNSUPPORTED, "%s: g=%d (supported: 64, 256)", fn, g);
+    if (!rot_size_ok(g)) return fail(W4_ERR_UNSUPPORTED, "%s: g=%d (supported: 16, 64, 256, 1024, 4096)", fn, g);
     if (K < g || K % g) return fail(W4_ERR_SHAPE, "%s: K=%lld must be a positive multiple of g=%d", fn, (long long)K, g);
     if (K > W4_MAX_K) return fail(W4_ERR_SHAPE, "%s: K=%lld exceeds %d", fn, (long long)K, W4_MAX_K);
     return W4_OK;
@@ -377,6 +379,183 @@ int w4_linear_noalloc(const void *X, int x_dtype, int64_t M, int64_t K, int g, i
                       const w4_lowrank *lr, int64_t N, void *Y, int y_kind, void *stream) {
     return linear_whole("w4_linear_noalloc", X, x_dtype, M, K, g, act_bits, packed, row_scale, zp, bias, bias_dtype,
                         lr, N, Y, y_kind, nullptr, 0, static_cast<hipStream_t>(stream), true);
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped-scale weight format
+
+static int check_gw(const char *fn, int64_t K, int gw) {
+    if (gw != 32 && gw != 64 && gw != 128 && gw != 256)
+        return fail(W4_ERR_UNSUPPORTED, "%s: gw=%d (supported: 32, 64, 128, 256)", fn, gw);
+    if (K < 64 || K % 64 || K % gw)
+        return fail(W4_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 64 and of gw=%d", fn, (long long)K, gw);
+    if (K > W4_MAX_K) return fail(W4_ERR_SHAPE, "%s: K=%lld exceeds %d", fn, (long long)K, W4_MAX_K);
+    return W4_OK;
+}
+
+size_t w4_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r) {
+    (void)act_bits;
+    if (M <= 0) return 0;
+    const size_t t = r > 0 ? align256((size_t)M * (size_t)r * sizeof(float)) : 0;
+    const size_t part = N <= 0 || K <= 0 || gw <= 0 ? 0 : align256(w4::grouped_workspace_bytes(M, N, K, gw));
+    return t + part;
+}
+
+size_t w4_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r) {
+    if (M <= 0) return 0;
+    const size_t codes = act_bits == 16 ? 0
+                         : align256(act_bits == 4 ? (size_t)M * (size_t)(K / 2) : (size_t)M * (size_t)K) +
+                               2 * align256((size_t)M * 4);
+    return codes + w4_grouped_workspace_bytes(M, N, K, act_bits, gw, r);
+}
+
+int w4_pack_weights_grouped(const void *W, int w_dtype, int64_t N, int64_t K, int g, int gw, uint8_t *packed,
+                            uint16_t *group_scale, void *stream) {
+    const char *fn = "w4_pack_weights_grouped";
+    if (w_dtype != W4_F32 && w_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: w_dtype=%d", fn, w_dtype);
+    if (N < 1) return fail(W4_ERR_SHAPE, "%s: N=%lld < 1", fn, (long long)N);
+    if (N > (int64_t)1 << 31) return fail(W4_ERR_SHAPE, "%s: N too large", fn);
+    if (int e = check_gw(fn, K, gw)) return e;
+    if (g != 0) {
+        if (int e = check_k(fn, K, g)) return e;
+    }
+    W4_CHECK_PTR(W);
+    W4_CHECK_PTR(packed);
+    W4_CHECK_PTR(group_scale);
+    return hip_status(w4::launch_pack_grouped(W, w_dtype == W4_F32, N, K, g, gw, packed, group_scale,
+                                              static_cast<hipStream_t>(stream)),
+                      fn);
+}
+
+// act: int8 / packed int4 codes (act_bits 8 / 4, with tok_scale) or bf16 X (act_bits 16).
+static int grouped_impl(const char *fn, const void *act, const float *tok_scale, int act_bits, const uint8_t *packed,
+                        const uint16_t *group_scale, int gw, const void *bias, int bias_dtype, const w4_lowrank *lr,
+                        int64_t M, int64_t N, int64_t K, void *Y, int y_kind, void *ws, size_t ws_bytes,
+                        hipStream_t st) {
+    if (y_kind != W4_OUT_BF16 && y_kind != W4_OUT_I32) return fail(W4_ERR_INVALID_ARG, "%s: y_kind=%d", fn, y_kind);
+    if (act_bits == 16 && y_kind == W4_OUT_I32)
+        return fail(W4_ERR_INVALID_ARG, "%s: W4_OUT_I32 needs integer activations", fn);
+    if (bias && bias_dtype != W4_F32 && bias_dtype != W4_BF16)
+        return fail(W4_ERR_INVALID_ARG, "%s: bias_dtype=%d", fn, bias_dtype);
+    W4_CHECK_PTR(act);
+    if (act_bits != 16) W4_CHECK_PTR(tok_scale);
+    W4_CHECK_PTR(packed);
+    W4_CHECK_PTR(group_scale);
+    W4_CHECK_OPT_PTR(bias);
+    W4_CHECK_PTR(Y);
+    const float *t = nullptr;
+    const uint16_t *l2 = nullptr;
+    int r = 0;
+    size_t tbytes = 0;
+    if (lr && y_kind == W4_OUT_BF16) {
+        r = lr->r;
+        if (r < 1 || r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: lowrank r=%d (supported 1..64)", fn, r);
+        if (!lr->l2) return fail(W4_ERR_INVALID_ARG, "%s: lowrank l2 is NULL", fn);
+        if (!aligned16(lr->l2)) return fail(W4_ERR_ALIGN, "%s: lowrank l2 not 16-byte aligned", fn);
+        l2 = static_cast<const uint16_t *>(lr->l2);
+        if (lr->t) {
+            if (!aligned16(lr->t)) return fail(W4_ERR_ALIGN, "%s: lowrank t not 16-byte aligned", fn);
+            t = lr->t;
+        } else {
+            if (!lr->x || !lr->l1) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
+            if (!aligned16(lr->x) || !aligned16(lr->l1))
+                return fail(W4_ERR_ALIGN, "%s: lowrank x / l1 not 16-byte aligned", fn);
+            tbytes = align256((size_t)M * (size_t)r * sizeof(float));
+            if (!ws || ws_bytes < tbytes)
+                return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, tbytes);
+        }
+    }
+    if (ws && !aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
+    if (M == 0) return ok();
+    if (r && !t) {
+        float *tw = static_cast<float *>(ws);
+        hipError_t e = w4::launch_lowrank_down(lr->x, lr->l1, M, K, r, tw, st);
+        if (e != hipSuccess) return hip_status(e, fn);
+        t = tw;
+    }
+    w4::GroupedArgs a{};
+    a.A = act;
+    a.sx = tok_scale;
+    a.B = packed;
+    a.gs = group_scale;
+    a.gw = gw;
+    a.bias = y_kind == W4_OUT_BF16 ? bias : nullptr;
+    a.bias_bf16 = bias_dtype == W4_BF16;
+    a.lr_t = t;
+    a.lr_l2 = l2;
+    a.lr_r = r;
+    a.Y = Y;
+    a.y_i32 = y_kind == W4_OUT_I32;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    void *gws = ws ? static_cast<uint8_t *>(ws) + tbytes : nullptr;
+    const size_t gbytes = ws ? ws_bytes - tbytes : 0;
+    return hip_status(w4::launch_gemm_grouped(a, act_bits, gws, gbytes, st), fn);
+}
+
+int w4_linear_cached_rot_grouped(const void *q, const float *tok_scale, int act_bits, const uint8_t *packed,
+                                 const uint16_t *group_scale, int gw, const void *bias, int bias_dtype,
+                                 const w4_lowrank *lr, int64_t M, int64_t N, int64_t K, void *Y, int y_kind, void *ws,
+                                 size_t ws_bytes, void *stream) {
+    const char *fn = "w4_linear_cached_rot_grouped";
+    if (act_bits != 4 && act_bits != 8)
+        return fail(W4_ERR_UNSUPPORTED, "%s: act_bits=%d (supported: 4, 8)", fn, act_bits);
+    if (int e = check_linear_shape(fn, M, N, K, act_bits)) return e;
+    if (int e = check_gw(fn, K, gw)) return e;
+    return grouped_impl(fn, q, tok_scale, act_bits, packed, group_scale, gw, bias, bias_dtype, lr, M, N, K, Y, y_kind,
+                        ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int w4_linear_grouped(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits, const uint8_t *packed,
+                      const uint16_t *group_scale, int gw, const void *bias, int bias_dtype, const w4_lowrank *lr,
+                      int64_t N, void *Y, int y_kind, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "w4_linear_grouped";
+    if (x_dtype != W4_F32 && x_dtype != W4_BF16) return fail(W4_ERR_INVALID_ARG, "%s: x_dtype=%d", fn, x_dtype);
+    if (act_bits != 4 && act_bits != 8 && act_bits != 16)
+        return fail(W4_ERR_UNSUPPORTED, "%s: act_bits=%d (supported: 4, 8, 16)", fn, act_bits);
+    if (int e = check_linear_shape(fn, M, N, K, act_bits == 16 ? 8 : act_bits)) return e;
+    if (int e = check_gw(fn, K, gw)) return e;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (act_bits == 16) {
+        // W4A16: the unrotated bf16 activations go straight into the bf16 GEMM
+        if (g != 0) return fail(W4_ERR_UNSUPPORTED, "%s: W4A16 takes unrotated weights (g = 0), got g=%d", fn, g);
+        if (x_dtype != W4_BF16) return fail(W4_ERR_UNSUPPORTED, "%s: W4A16 takes bf16 activations", fn);
+        return grouped_impl(fn, X, nullptr, 16, packed, group_scale, gw, bias, bias_dtype, lr, M, N, K, Y, y_kind, ws,
+                            ws_bytes, st);
+    }
+    if (int e = check_k(fn, K, g)) return e;
+    if (!w4::rotquant_supported(K, g))
+        return fail(W4_ERR_UNSUPPORTED, "%s: K=%lld has no supported split for g=%d", fn, (long long)K, g);
+    if (y_kind != W4_OUT_BF16 && y_kind != W4_OUT_I32) return fail(W4_ERR_INVALID_ARG, "%s: y_kind=%d", fn, y_kind);
+    if (M == 0) return ok();
+    W4_CHECK_PTR(X);
+    const int r = (lr && !lr->t && y_kind == W4_OUT_BF16) ? lr->r : 0;
+    const size_t need = w4_linear_grouped_workspace_bytes(M, N, K, act_bits, gw, r > 0 ? r : 0);
+    if (!ws || ws_bytes < need) return fail(W4_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    if (!aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
+    {
+        W4_CHECK_PTR(packed);
+        W4_CHECK_PTR(group_scale);
+        W4_CHECK_OPT_PTR(bias);
+        W4_CHECK_PTR(Y);
+        if (bias && bias_dtype != W4_F32 && bias_dtype != W4_BF16)
+            return fail(W4_ERR_INVALID_ARG, "%s: bias_dtype=%d", fn, bias_dtype);
+        if (lr && y_kind == W4_OUT_BF16) {
+            if (lr->r < 1 || lr->r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: lowrank r=%d", fn, lr->r);
+            if (!lr->l2) return fail(W4_ERR_INVALID_ARG, "%s: lowrank l2 is NULL", fn);
+            if (!lr->t && (!lr->x || !lr->l1)) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
+        }
+    }
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    const size_t qb = align256(act_bits == 4 ? (size_t)M * (size_t)(K / 2) : (size_t)M * (size_t)K);
+    float *sx = reinterpret_cast<float *>(base + qb);
+    int32_t *rs = reinterpret_cast<int32_t *>(base + qb + align256((size_t)M * 4));
+    uint8_t *rest = base + qb + 2 * align256((size_t)M * 4);
+    hipError_t e = w4::launch_rotquant(X, x_dtype == W4_F32, M, K, g, act_bits, base, sx, rs, st);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return grouped_impl(fn, base, sx, act_bits, packed, group_scale, gw, bias, bias_dtype, lr, M, N, K, Y, y_kind, rest,
+                        ws_bytes - (size_t)(rest - base), st);
 }
 
 }  // extern "C"

@@ -141,7 +141,7 @@ def test_linear_validation(lib):
     assert lin(ws=None, ws_bytes=need) == w4.W4_ERR_WORKSPACE
     assert lin(ws=U, ws_bytes=need) == w4.W4_ERR_ALIGN
     assert lin(Y=None, ws_bytes=need) == w4.W4_ERR_INVALID_ARG              # caught before any launch
-    assert lin(g=16) == w4.W4_ERR_UNSUPPORTED
+    assert lin(g=32) == w4.W4_ERR_UNSUPPORTED                               # not a rotation size
     assert lin(x_dtype=4) == w4.W4_ERR_INVALID_ARG
     assert lin(M=0, ws=None) == w4.W4_OK
 
@@ -159,11 +159,50 @@ def test_linear_noalloc_validation(lib):
     assert na(M=8000, K=8192, lr=ctypes.byref(lr)) == w4.W4_ERR_WORKSPACE
     assert na(Y=None) == w4.W4_ERR_INVALID_ARG
     assert na(X=U) == w4.W4_ERR_ALIGN
-    assert na(g=16) == w4.W4_ERR_UNSUPPORTED
+    assert na(g=32) == w4.W4_ERR_UNSUPPORTED
     assert na(bits=3) == w4.W4_ERR_UNSUPPORTED
     assert na(x_dtype=4) == w4.W4_ERR_INVALID_ARG
     assert na(N=0) == w4.W4_ERR_SHAPE
     assert na(M=0, X=None) == w4.W4_OK
+
+
+def test_grouped_validation(lib):
+    """The grouped-scale calls check rotation size, group width, bit width and shapes before
+    anything is launched."""
+    def pg(N=8, K=256, g=64, gw=64, W=A, packed=A, gs=A):
+        return lib.w4_pack_weights_grouped(W, w4.W4_BF16, N, K, g, gw, packed, gs, None)
+    assert pg(gw=48) == w4.W4_ERR_UNSUPPORTED
+    assert pg(gw=16) == w4.W4_ERR_UNSUPPORTED
+    assert pg(K=288, gw=32) == w4.W4_ERR_SHAPE                             # K not a multiple of 64
+    assert pg(g=128) == w4.W4_ERR_UNSUPPORTED
+    assert pg(K=1024, g=4096) == w4.W4_ERR_SHAPE                           # K < g
+    assert pg(gs=None) == w4.W4_ERR_INVALID_ARG
+    assert pg(packed=U) == w4.W4_ERR_ALIGN
+
+    def lg(M=100, K=256, g=64, bits=8, gw=64, Y=A, ws=A, ws_bytes=1 << 20, x_dtype=w4.W4_BF16, y_kind=w4.W4_OUT_BF16):
+        return lib.w4_linear_grouped(A, x_dtype, M, K, g, bits, A, A, gw, None, w4.W4_BF16, None, 64, Y, y_kind,
+                                     ws, ws_bytes, None)
+    assert lg(bits=16) == w4.W4_ERR_UNSUPPORTED                             # W4A16 with a rotation
+    assert lg(bits=16, g=0, x_dtype=w4.W4_F32) == w4.W4_ERR_UNSUPPORTED
+    assert lg(bits=16, g=0, y_kind=w4.W4_OUT_I32) == w4.W4_ERR_INVALID_ARG
+    assert lg(g=0) == w4.W4_ERR_UNSUPPORTED                                 # integer codes need a rotation
+    assert lg(bits=2) == w4.W4_ERR_UNSUPPORTED
+    assert lg(gw=512) == w4.W4_ERR_UNSUPPORTED
+    assert lg(ws_bytes=10) == w4.W4_ERR_WORKSPACE
+    assert lg(Y=None) == w4.W4_ERR_INVALID_ARG
+    assert lg(M=0, ws=None, ws_bytes=0) == w4.W4_OK
+    need = lib.w4_linear_grouped_workspace_bytes(100, 64, 256, 8, 64, 0)
+    assert need == 100 * 256 + 2 * 512                                      # codes, token scales, row sums
+    assert lib.w4_linear_grouped_workspace_bytes(100, 64, 256, 16, 64, 0) == 0
+    assert lib.w4_grouped_workspace_bytes(100, 64, 256, 8, 64, 32) == 100 * 32 * 4
+
+    def cg(M=100, K=256, bits=8, gw=64, q=A, s=A):
+        return lib.w4_linear_cached_rot_grouped(q, s, bits, A, A, gw, None, w4.W4_BF16, None, M, 64, K, A,
+                                                w4.W4_OUT_BF16, None, 0, None)
+    assert cg(bits=16) == w4.W4_ERR_UNSUPPORTED
+    assert cg(s=None) == w4.W4_ERR_INVALID_ARG
+    assert cg(K=320, gw=128) == w4.W4_ERR_SHAPE
+    assert cg(M=0) == w4.W4_OK
 
 
 def test_probe_validation(lib):
