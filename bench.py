@@ -26,6 +26,11 @@ Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
   small_m      asym W4A8 g=256, M in {1,4,16,64}, K/N 4096/12288     metric: weight GB/s
   double_block 20 blocks x {QKV, out, up, down} at M=4608, cached    metric: TOPS
   tiny         W4A8 g=64, 16 x 256 -> 256                            metric: TOPS
+  attn_proj_grouped  attn_proj shape, fp16 weight scales per row and --gw inputs (W4A8)
+  attn_proj_w4a16    attn_proj shape, W4A16 (no rotation, bf16 activations, grouped scales)
+  small_m_w4a16      small_m shapes (symmetric codes) as W4A16                metric: weight GB/s
+The default run also times the small-M text-encoder linear at M = 1 and 16 (K = 12288) and
+reports them under "detail" (--no-small-m-detail skips that).
   mfma_peak    the library's int8 MFMA rate probe (not a layer): the chip's sustained
                dense int8 rate with random and with constant operands
 """
@@ -43,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A8/W4A4 linear TOPS at M=4096; weight GB/s at M≤16; % of roofline"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, 5.0 POPS
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 MALL_BYTES = 256 << 20
 
 
@@ -56,7 +62,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="attn_proj",
-                    choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny", "mfma_peak"])
+                    choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny", "mfma_peak",
+                             "attn_proj_grouped", "attn_proj_w4a16", "small_m_w4a16"])
+    ap.add_argument("--gw", type=int, default=128, help="grouped-scale workloads: inputs per weight scale")
+    ap.add_argument("--no-small-m-detail", action="store_true",
+                    help="attn_proj: skip timing the two small-M text-encoder shapes reported in detail")
+    ap.add_argument("--summarize-trace", metavar="TRACE", default=None,
+                    help="no GPU: per-kernel statistics of a rocprofv3 kernel trace (kernel_trace.csv or the "
+                         "results .db), plus each kernel's mean duration over its timed back-to-back launches")
     ap.add_argument("--M", type=int, default=None, help="tokens (small_m: 1, 4, 16 or 64)")
     ap.add_argument("--K", type=int, default=12288, help="small_m: input features (4096 or 12288)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,29 +85,37 @@ def parse():
 
 # --------------------------------------------------------------------------- workloads
 class Linear:
-    """One quantized linear with its inputs on the GPU (weights packed once, untimed)."""
+    """One quantized linear with its inputs on the GPU (weights packed once, untimed).
 
-    def __init__(self, X, W, bias, g, bits, asym, lowrank=None):
+    gw > 0: the grouped-scale format (fp16 scales [N, K/gw], symmetric codes); bits 16 with
+    g = 0 is W4A16."""
+
+    def __init__(self, X, W, bias, g, bits, asym, lowrank=None, gw=0):
         import int4_weight_quantized_block_amd as w4
-        self.g, self.bits, self.asym = g, bits, asym
+        self.g, self.bits, self.asym, self.gw = g, bits, asym, gw
         self.M, self.K = X.shape
         self.N = W.shape[0]
         self.X = X
         self.bias = bias
-        self.packed, self.s_w, self.zp = w4.w4_pack_weights(W, g, asym)
+        if gw:
+            self.packed, self.s_w = w4.w4_pack_weights_grouped(W, g, gw)
+            self.zp = None
+        else:
+            self.packed, self.s_w, self.zp = w4.w4_pack_weights(W, g, asym)
         self.lowrank = lowrank
 
     def ops(self):
         return 2.0 * self.M * self.N * self.K
 
     def gemm_bytes(self):
-        """Algorithmic HBM bytes of one GEMM launch (codes, weights, scales, bias, output)."""
+        """Algorithmic HBM bytes of one GEMM launch (codes or bf16 X, weights, scales, bias, output)."""
         M, N, K = self.M, self.N, self.K
-        a = M * K if self.bits == 8 else M * K // 2
-        w = N * K // 2 + 4 * N + (N if self.asym else 0)
-        return a + w + 8 * M + 2 * N + 2 * M * N
+        a = {8: M * K, 4: M * K // 2, 16: 2 * M * K}[self.bits]
+        return a + self.weight_bytes() + (0 if self.bits == 16 else 8 * M) + 2 * N + 2 * M * N
 
     def weight_bytes(self):
+        if self.gw:
+            return self.N * self.K // 2 + 2 * self.N * (self.K // self.gw)
         return self.N * self.K // 2 + 4 * self.N + (self.N if self.asym else 0)
 
     def fused_bytes(self):
@@ -138,6 +159,25 @@ def build_workload(args, dev):
         return [[("small_m", d["X"], d["W"], d["bias"], 256, 8, True)]], {
             "workload": "small_m", "M": M, "K": K, "N": N, "g": 256, "act_bits": 8,
             "weights": "asym int4 per-row + zero point"}
+    if name in ("attn_proj_grouped", "attn_proj_w4a16"):
+        M = args.M or 4096
+        d = synth.attn_proj(M=M)
+        gw = args.gw
+        if name == "attn_proj_grouped":
+            return [[("attn_proj", d["X"], d["W"], d["bias"], 256, 8, False, gw)]], {
+                "workload": name, "M": M, "K": 3072, "N": 3072, "g": 256, "act_bits": 8,
+                "weights": "sym int4, fp16 scale per row and %d inputs" % gw}
+        return [[("attn_proj", d["X"], d["W"], d["bias"], 0, 16, False, gw)]], {
+            "workload": name, "M": M, "K": 3072, "N": 3072, "g": 0, "act_bits": 16,
+            "weights": "sym int4, fp16 scale per row and %d inputs (W4A16, no rotation)" % gw}
+    if name == "small_m_w4a16":
+        M = args.M or 16
+        K = args.K
+        N = 12288 if K == 4096 else 4096
+        d = synth.small_m(M, K, N)
+        return [[("small_m", d["X"], d["W"], d["bias"], 0, 16, False, args.gw)]], {
+            "workload": name, "M": M, "K": K, "N": N, "g": 0, "act_bits": 16,
+            "weights": "sym int4, fp16 scale per row and %d inputs (W4A16, no rotation)" % args.gw}
     if name == "tiny":
         d = synth.tiny()
         return [[("tiny", d["X"], d["W"], d["bias"], 64, 8, False)]], {
@@ -152,10 +192,27 @@ def cpu_baseline(layer, rows_wanted):
     of the layer: rotate + quantize, int64 GEMM, fp64 epilogue (weight packing not counted).
     Returns (dict, seconds, rows)."""
     import oracle
-    name, X, W, bias, g, bits, asym = layer
+    name, X, W, bias, g, bits, asym = layer[:7]
+    gw = layer[7] if len(layer) > 7 else 0
     M = X.shape[0]
     rows = min(M, rows_wanted)
     Xs = X[:rows].cpu()
+    if gw:
+        pw = oracle.pack_weights_grouped(W.cpu(), g, gw)
+        t1 = time.perf_counter()
+        if bits == 16:
+            oracle.bf16_rne(oracle.to_f64(Xs) @ oracle.dequant_grouped(pw["packed"], pw["scale"], gw).T
+                            + oracle.to_f64(bias.cpu())[None, :])
+        else:
+            qa = oracle.rotate_quant_act(Xs, g, bits)
+            accg = oracle.gemm_i64_groups(qa["q"], oracle.weight_operand(pw["packed"], None, False), gw)
+            oracle.bf16_rne(oracle.epilogue_grouped(accg, qa["scale"], pw["scale"], bias.cpu()))
+        sec = time.perf_counter() - t1
+        return {"cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "%s: %d of %d token rows, one pass (%s)" % (
+                    name, rows, M, "fp64 product with the dequantized weights" if bits == 16 else
+                    "rotate + quantize + int64 GEMM per weight group + grouped epilogue"),
+                "seconds": round(sec, 3)}, sec, rows
     pw = oracle.pack_weights(W.cpu(), g, asym)
     t1 = time.perf_counter()
     qa = oracle.rotate_quant_act(Xs, g, bits)
@@ -169,7 +226,7 @@ def cpu_baseline(layer, rows_wanted):
 COPY_BYTES = 512 << 20
 # kernel-name prefix -> (short name, source file)
 KERNEL_SOURCE = {"k_gemm<": ("k_gemm", "gemm.hip"), "k_gemv": ("k_gemv", "gemv.hip"),
-                 "k_rotquant": ("k_rotquant", "rotquant.hip")}
+                 "k_rotquant": ("k_rotquant", "rotquant.hip"), "k_gemm_grp": ("k_gemm_grp", "gemm_grp.hip")}
 
 
 def copy_calibration(dev):
@@ -238,6 +295,8 @@ def ingest_counters(fetch_dir, write_dir, workload):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.steps)
     if args.ingest_counters:
         return ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
                                traffic_workload(args.workload, args.M or 16, args.K))
@@ -260,17 +319,101 @@ def main():
         return bench_mfma_peak(args, dev)
 
     layer_specs, cfg = build_workload(args, dev)
-    name, X, W, bias, g, bits, asym = layer_specs[0][0]
-    lin = Linear(X.to(dev), W.to(dev), bias.to(dev), g, bits, asym)
+    spec = layer_specs[0][0]
+    r = time_layer(args, dev, spec)
+    lin, fused, t_rq, t_mm, wall = r["lin"], r["fused"], r["t_rq"], r["t_mm"], r["wall"]
+    M, bits = lin.M, lin.bits
+    ms_step = wall / args.steps * 1e3
+    log("bench: %.3f ms/step wall (%s)" % (ms_step, "eager" if args.eager else "graph replay"))
+    if args.copy_calibration:
+        copy_calibration(dev)
+
+    small = M <= 64
+    if small:
+        value = lin.weight_bytes() / (wall / args.steps) / 1e9
+        unit = "GB/s"
+        alg = lin.fused_bytes() if fused else lin.gemm_bytes()
+        roof = {"bound": "hbm", "achieved": alg / t_mm / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        value = lin.ops() / (wall / args.steps) / 1e12
+        unit = "TOPS"
+        peak = PEAK_BF16_TFLOPS if bits == 16 else PEAK_INT8_TOPS
+        roof = {"bound": "mfma", "achieved": lin.ops() / t_mm / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = r["kernel"]
+    roof["traffic"] = measured_traffic(r["kernel"], cfg)
+    roof["launch_us"] = round(t_mm * 1e6, 3)
+    extra = {
+        "fused": fused,
+        "rotquant_us": round(t_rq * 1e6, 3) if t_rq else None,
+        "rotquant_hbm_gbs": round(lin.rotquant_bytes() / t_rq / 1e9, 1) if t_rq else None,
+        "rotquant_hbm_frac": round(lin.rotquant_bytes() / t_rq / 1e9 / PEAK_HBM_GBS, 4) if t_rq else None,
+        "gemm_tops": round(lin.ops() / t_mm / 1e12, 2),
+        "gemm_weight_gbs": round(lin.weight_bytes() / t_mm / 1e9, 1),
+        "gemm_alg_bytes": lin.fused_bytes() if fused else lin.gemm_bytes(),
+        "timed_launch": "eager" if args.eager else "one hip graph of the K steps",
+        "input_copies": r["ncopy"],
+    }
+    if args.workload == "attn_proj" and not args.no_small_m_detail:
+        # the metric's second half: weight GB/s of the HBM-bound text-encoder linears at M <= 16
+        # (asymmetric W4A8, K = 12288 -> N = 4096), whole w4_linear step and dominant kernel
+        extra["small_m"] = {}
+        for Ms in (1, 16):
+            sub = argparse.Namespace(**vars(args))
+            sub.workload, sub.M, sub.K = "small_m", Ms, 12288
+            sspec = build_workload(sub, dev)[0][0][0]
+            rs = time_layer(sub, dev, sspec)
+            ls = rs["lin"]
+            step_s = rs["wall"] / args.steps
+            alg = ls.fused_bytes() if rs["fused"] else ls.gemm_bytes()
+            extra["small_m"]["M%d_K12288_N4096" % Ms] = {
+                "weight_gbs_per_step": round(ls.weight_bytes() / step_s / 1e9, 1),
+                "us_per_step": round(step_s * 1e6, 3),
+                "kernel": rs["kernel"], "kernel_us": round(rs["t_mm"] * 1e6, 3),
+                "kernel_hbm_gbs": round(alg / rs["t_mm"] / 1e9, 1),
+                "kernel_hbm_frac": round(alg / rs["t_mm"] / 1e9 / PEAK_HBM_GBS, 4),
+                "rotquant_us": round(rs["t_rq"] * 1e6, 3) if rs["t_rq"] else None}
+            log("bench: small-M M=%d: %s" % (Ms, extra["small_m"]["M%d_K12288_N4096" % Ms]))
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or M
+        log("bench: timing the CPU oracle on %d rows" % rows)
+        cpu, sec, rows = cpu_baseline(spec, rows)
+        if small:  # weight bytes streamed per full pass over the M tokens
+            cpu["value"] = round(lin.weight_bytes() / (sec * M / rows) / 1e9, 4)
+            cpu["unit"] = "GB/s"
+        else:
+            cpu["value"] = round(lin.ops() * rows / M / sec / 1e12, 6)
+            cpu["unit"] = "TOPS"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": {8: "int8", 4: "int4", 16: "bf16"}[bits],
+        "data": "synthetic", "config": dict(cfg, parallelism="single-gpu"),
+        "roofline": roof, "cpu_baseline": cpu, "detail": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def time_layer(args, dev, spec):
+    """Time one linear: per-launch durations of its kernels (HIP events around a graph of K
+    back-to-back launches of each) and the wall time of K whole steps (one graph replay).
+    Returns dict(lin, fused, t_rq, t_mm, wall, ncopy, kernel)."""
+    import torch
+    import int4_weight_quantized_block_amd as w4
+    name, X, W, bias, g, bits, asym = spec[:7]
+    gw = spec[7] if len(spec) > 7 else 0
+    lin = Linear(X.to(dev), W.to(dev), bias.to(dev), g, bits, asym, gw=gw)
     # distinct copies of the inputs so the timed loop streams from HBM
-    per_copy = lin.X.numel() * lin.X.element_size() + lin.packed.numel() + lin.s_w.numel() * 4
+    per_copy = lin.X.numel() * lin.X.element_size() + lin.packed.numel() + lin.s_w.numel() * lin.s_w.element_size()
     ncopy = max(1, min(64, math.ceil(2 * MALL_BYTES / per_copy)))
     Xs = [lin.X] + [lin.X.clone() for _ in range(ncopy - 1)]
     Ps = [(lin.packed, lin.s_w, lin.zp)] + [(lin.packed.clone(), lin.s_w.clone(),
                                             lin.zp.clone() if lin.zp is not None else None)
                                            for _ in range(ncopy - 1)]
     M, K, N = lin.M, lin.K, lin.N
-    qbuf = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+    abits = 8 if bits == 16 else bits
+    qbuf = torch.empty((M, K if abits == 8 else K // 2), dtype=torch.int8 if abits == 8 else torch.uint8, device=dev)
     sx = torch.empty((M,), dtype=torch.float32, device=dev)
     rs = torch.empty((M,), dtype=torch.int32, device=dev)
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -281,18 +424,42 @@ def main():
     # argument tuples built once, so the timed loop costs little host time per launch and the
     # GPU never waits for the host
     xdt = w4.W4_BF16 if lin.X.dtype == torch.bfloat16 else w4.W4_F32
-    rq_args = [(x.data_ptr(), xdt, M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr) for x in Xs]
-    mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
-                z.data_ptr() if z is not None else None, lin.bias.data_ptr(), w4.W4_BF16, None, M, N, K,
-                Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
-    # the step: the whole layer through w4_linear (rotate + quantize into its workspace, then
-    # the GEMM; one fused launch for a single token, see w4_linear_fused)
-    wsl = torch.empty((max(256, w4.w4_linear_workspace_bytes(M, N, K, bits)),), dtype=torch.uint8, device=dev)
-    lin_args = [(x.data_ptr(), xdt, M, K, g, bits, p.data_ptr(), s.data_ptr(), z.data_ptr() if z is not None else None,
-                 lin.bias.data_ptr(), w4.W4_BF16, None, N, Y.data_ptr(), w4.W4_OUT_BF16, wsl.data_ptr(), wsl.numel(),
-                 sptr) for x, (p, s, z) in zip(Xs, Ps)]
-    f_rq, f_mm, f_lin = L.w4_rotate_quant_act, L.w4_linear_cached_rot, L.w4_linear
-    fused = bool(L.w4_linear_fused(M, N, K, g, bits, xdt))
+    bptr = lin.bias.data_ptr()
+    if gw:
+        wsg = torch.empty((max(256, w4.w4_linear_grouped_workspace_bytes(M, N, K, bits, gw)),), dtype=torch.uint8,
+                          device=dev)
+        wsc = torch.empty((max(256, w4.w4_grouped_workspace_bytes(M, N, K, bits, gw)),), dtype=torch.uint8,
+                          device=dev)
+        rq_args = [(x.data_ptr(), xdt, M, K, g, abits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr)
+                   for x in Xs]
+        if bits == 16:   # W4A16: the GEMM reads X itself
+            mm_args = [(x.data_ptr(), xdt, M, K, 0, 16, p.data_ptr(), s.data_ptr(), gw, bptr, w4.W4_BF16, None, N,
+                        Y.data_ptr(), w4.W4_OUT_BF16, wsg.data_ptr(), wsg.numel(), sptr) for x, (p, s, _) in zip(Xs, Ps)]
+            f_mm = L.w4_linear_grouped
+        else:
+            mm_args = [(qbuf.data_ptr(), sx.data_ptr(), bits, p.data_ptr(), s.data_ptr(), gw, bptr, w4.W4_BF16, None,
+                        M, N, K, Y.data_ptr(), w4.W4_OUT_BF16, wsc.data_ptr(), wsc.numel(), sptr) for p, s, _ in Ps]
+            f_mm = L.w4_linear_cached_rot_grouped
+        lin_args = [(x.data_ptr(), xdt, M, K, g, bits, p.data_ptr(), s.data_ptr(), gw, bptr, w4.W4_BF16, None, N,
+                     Y.data_ptr(), w4.W4_OUT_BF16, wsg.data_ptr(), wsg.numel(), sptr) for x, (p, s, _) in zip(Xs, Ps)]
+        f_lin = L.w4_linear_grouped
+        fused = False
+        kernel = "k_gemm_grp"
+    else:
+        rq_args = [(x.data_ptr(), xdt, M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr) for x in Xs]
+        mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
+                    z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, None, M, N, K,
+                    Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
+        # the step: the whole layer through w4_linear (rotate + quantize into its workspace, then
+        # the GEMM; one fused launch for a single token, see w4_linear_fused)
+        wsl = torch.empty((max(256, w4.w4_linear_workspace_bytes(M, N, K, bits)),), dtype=torch.uint8, device=dev)
+        lin_args = [(x.data_ptr(), xdt, M, K, g, bits, p.data_ptr(), s.data_ptr(),
+                     z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, None, N, Y.data_ptr(),
+                     w4.W4_OUT_BF16, wsl.data_ptr(), wsl.numel(), sptr) for x, (p, s, z) in zip(Xs, Ps)]
+        f_mm, f_lin = L.w4_linear_cached_rot, L.w4_linear
+        fused = bool(L.w4_linear_fused(M, N, K, g, bits, xdt))
+        kernel = "k_gemv_fused" if fused else ("k_gemv" if M <= 64 else "k_gemm")
+    f_rq = L.w4_rotate_quant_act
 
     def step(i):
         rc = f_lin(*lin_args[i % ncopy])
@@ -302,8 +469,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log("bench: %d copies of the inputs (%.0f MB), %d warmup steps done" % (ncopy, ncopy * per_copy / 1e6,
-                                                                            args.warmup))
+    log("bench: %s: %d copies of the inputs (%.0f MB), %d warmup steps done" % (
+        name, ncopy, ncopy * per_copy / 1e6, args.warmup))
+
     # per-launch durations: each kernel launched K times back to back between two HIP events.
     # The K launches are captured once in a HIP graph and the replay is timed, so the events
     # see the kernels and the GPU's own launch gaps, not the host's per-call cost (a ctypes
@@ -326,6 +494,10 @@ def main():
                 w4._check(f(*(argl[i % ncopy][:-1] + (sk,))))
         gk.replay()
         torch.cuda.synchronize()
+        # two replays back to back; the events bracket the second, which the host has
+        # submitted while the first still runs, so they see K launches and not the graph's
+        # submission latency
+        gk.replay()
         e0.record(stream)
         gk.replay()
         e1.record(stream)
@@ -335,18 +507,20 @@ def main():
     if fused:  # one kernel per step
         t_rq, t_mm = None, per_launch(f_lin, lin_args)
         log("bench: fused rotate+quant+GEMM %.2f us per launch" % (t_mm * 1e6))
+    elif bits == 16:
+        t_rq, t_mm = None, per_launch(f_mm, mm_args)
+        log("bench: W4A16 GEMM %.2f us per launch" % (t_mm * 1e6))
     else:
         t_rq, t_mm = per_launch(f_rq, rq_args), per_launch(f_mm, mm_args)
         log("bench: rotate+quant %.2f us, GEMM %.2f us per launch" % (t_rq * 1e6, t_mm * 1e6))
-    # eager steps, timed as a whole
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log("bench: eager %.3f ms/step wall" % (wall / args.steps * 1e3))
-    if not args.eager:
+    if args.eager:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
         # the timed steps: one HIP graph holding the K steps' launches in order (step i on
         # input copy i % ncopy), captured once untimed and replayed once, so the GPU runs the
         # steps back to back without waiting for the host
@@ -362,55 +536,52 @@ def main():
         gph.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
-    log("bench: %.3f ms/step wall (%s)" % (ms_step, "eager" if args.eager else "graph replay"))
-    if args.copy_calibration:
-        copy_calibration(dev)
+    return {"lin": lin, "fused": fused, "t_rq": t_rq, "t_mm": t_mm, "wall": wall, "ncopy": ncopy, "kernel": kernel}
 
-    small = args.workload == "small_m"
-    if small:
-        value = lin.weight_bytes() / (wall / args.steps) / 1e9
-        unit = "GB/s"
-        alg = lin.fused_bytes() if fused else lin.gemm_bytes()
-        roof = {"bound": "hbm", "achieved": alg / t_mm / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+
+def summarize_trace(path, steps):
+    """Per-kernel statistics of a rocprofv3 kernel trace (CSV), and for each kernel the mean
+    duration over its longest run of back-to-back dispatches, last `steps` of them: the
+    graph replay that bench.py times with HIP events for the roofline."""
+    import csv
+    if path.endswith(".db"):   # rocprofv3's default (rocpd SQLite) output
+        import sqlite3
+        q = sqlite3.connect(path).execute("select name, start, end from kernels")
+        rows = [{"Kernel_Name": n, "Start_Timestamp": s, "End_Timestamp": e} for n, s, e in q]
     else:
-        value = lin.ops() / (wall / args.steps) / 1e12
-        unit = "TOPS"
-        roof = {"bound": "mfma", "achieved": lin.ops() / t_mm / 1e12, "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "k_gemv_fused" if fused else ("k_gemv" if M <= 64 else "k_gemm")
-    roof["traffic"] = measured_traffic("k_gemv" if M <= 64 else "k_gemm", cfg)
-    roof["launch_us"] = round(t_mm * 1e6, 3)
-    extra = {
-        "fused": fused,
-        "rotquant_us": round(t_rq * 1e6, 3) if t_rq else None,
-        "rotquant_hbm_gbs": round(lin.rotquant_bytes() / t_rq / 1e9, 1) if t_rq else None,
-        "rotquant_hbm_frac": round(lin.rotquant_bytes() / t_rq / 1e9 / PEAK_HBM_GBS, 4) if t_rq else None,
-        "gemm_tops": round(lin.ops() / t_mm / 1e12, 2),
-        "gemm_weight_gbs": round(lin.weight_bytes() / t_mm / 1e9, 1),
-        "gemm_alg_bytes": lin.fused_bytes() if fused else lin.gemm_bytes(),
-        "timed_launch": "eager" if args.eager else "one hip graph of the K steps",
-        "input_copies": ncopy,
-    }
-    cpu = None
-    if not args.no_cpu_baseline:
-        rows = args.cpu_rows or M
-        log("bench: timing the CPU oracle on %d rows" % rows)
-        cpu, sec, rows = cpu_baseline(layer_specs[0][0], rows)
-        if small:  # weight bytes streamed per full pass over the M tokens
-            cpu["value"] = round(lin.weight_bytes() / (sec * M / rows) / 1e9, 4)
-            cpu["unit"] = "GB/s"
+        rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| kernel | calls | mean us | min us | max us |")
+    print("|---|---|---|---|---|")
+    for k, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print("| %s | %d | %.3f | %.3f | %.3f |" % (k[:90], len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
+    # runs of consecutive dispatches of one kernel
+    runs = []
+    cur = None
+    for r in rows:
+        k = r["Kernel_Name"]
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if cur and cur[0] == k:
+            cur[1].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
         else:
-            cpu["value"] = round(lin.ops() * rows / M / sec / 1e12, 6)
-            cpu["unit"] = "TOPS"
-    out = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8" if bits == 8 else "int4",
-        "data": "synthetic", "config": dict(cfg, parallelism="single-gpu"),
-        "roofline": roof, "cpu_baseline": cpu, "detail": extra,
-    }
-    print(json.dumps(out), flush=True)
+            cur = [k, [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]))]]
+            runs.append(cur)
+        del dur
+    print()
+    print("| kernel | back-to-back launches (last of its longest run) | mean kernel us | mean start-to-start us |")
+    print("|---|---|---|---|")
+    best = {}
+    for k, seq in runs:
+        if len(seq) >= steps and len(seq) >= len(best.get(k, [])):
+            best[k] = seq
+    for k, seq in best.items():
+        seq = seq[-steps:]
+        mean = sum(e - s for s, e in seq) / len(seq) / 1e3
+        span = (seq[-1][1] - seq[0][0]) / len(seq) / 1e3
+        print("| %s | %d | %.3f | %.3f |" % (k[:90], len(seq), mean, span))
 
 
 def measured_traffic(kernel, cfg):
