@@ -664,6 +664,9 @@ def bench_double_block(args, dev):
             packed, s_w, _ = w4.w4_pack_weights(p["W"], 256, False)
             lins[name] = (packed, s_w, p["bias"], p["L1"], p["L2"])
             del p["W"]
+        # QKV and MLP-up read the block input: their L1 factors are stacked once (a load-time
+        # step) so one pass gives both low-rank inputs along with the shared codes
+        lins["x_l1"] = torch.cat([blk["qkv"]["L1"], blk["up"]["L1"]], dim=0).contiguous()
         blocks.append((blk["x"], blk["attn"], lins))
         log("bench: block %d packed" % b)
     torch.cuda.synchronize()
@@ -676,13 +679,16 @@ def bench_double_block(args, dev):
     stream = torch.cuda.current_stream(dev)
     gemm_times = []
 
+    r = synth.LOWRANK
+
     def step(record):
         for x, attn, lins in blocks:
             cache = w4.RotationCache()
-            for name, inp in (("qkv", x), ("up", x), ("out", attn)):
+            for name, inp, l1, cols in (("qkv", x, lins["x_l1"], slice(0, r)), ("up", x, lins["x_l1"], slice(r, 2 * r)),
+                                        ("out", attn, lins["out"][3], slice(0, r))):
                 packed, s_w, bias, L1, L2 = lins[name]
-                q, sx, rs = cache.get(inp, 256, 8)
-                t = w4.w4_lowrank_down(inp, L1)
+                q, sx, rs, tt = cache.get(inp, 256, 8, l1=l1)   # codes and x . L1 in one pass
+                t = tt[:, cols]
                 e0 = torch.cuda.Event(enable_timing=True) if record else None
                 if record:
                     e0.record(stream)
@@ -694,8 +700,7 @@ def bench_double_block(args, dev):
                     gemm_times.append((e0, e1))
             torch.nn.functional.gelu(outs["up"], out=h)  # host glue between the MLP linears
             packed, s_w, bias, L1, L2 = lins["down"]
-            q, sx, rs = w4.w4_rotate_quant_act(h, 256, 8)
-            t = w4.w4_lowrank_down(h, L1)
+            q, sx, rs, t = w4.w4_rotate_quant_act_lowrank(h, 256, 8, L1)
             w4.w4_linear_cached_rot(q, sx, rs, 8, packed, s_w, bias=bias, lowrank=w4.LowRank(l2=L2, t=t),
                                     out=outs["down"])
             cache.clear()

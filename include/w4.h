@@ -79,13 +79,18 @@ extern "C" {
  *       shared by linears that read the same input); NULL -> computed into the workspace
  *  l2 : bf16 [r, N], rank-major: row q holds the q-th up-projection vector over the N
  *       outputs
- *  r  : rank, 1 <= r <= 64 */
+ *  r  : rank, 1 <= r <= 64
+ *  ldt: row stride of a supplied t in floats (0 means r; otherwise >= r).  With a stride, t
+ *       can be a column range of a wider t computed once for several linears that read the
+ *       same input (w4_rotate_quant_act_lowrank with their L1 factors stacked); a multiple of
+ *       4 (and a 16-byte aligned t) keeps the kernels' vector loads. */
 typedef struct w4_lowrank {
     const void *x;
     const void *l1;
     const float *t;
     const void *l2;
     int r;
+    int ldt;
 } w4_lowrank;
 
 /* w4_pack_weights - offline weight step: rotate every row of W along K in groups of g,
@@ -229,6 +234,26 @@ int w4_linear_grouped(const void *X, int x_dtype, int64_t M, int64_t K, int g, i
 
 size_t w4_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r);
 size_t w4_linear_grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits, int gw, int r);
+
+/* w4_rotate_quant_act_lowrank - w4_rotate_quant_act plus the low-rank down-projection
+ * t = X . L1 of the same bf16 input in the same pass (ComfyUI-INT-Crush README, "Forward Pass"
+ * step 6 and "LoRA": the residual from L1 / L2 on the unrotated activations;
+ * stable-diffusion.cpp PR #2010, "Summary": the work on an input is shared by the linears that
+ * read it, so their L1 factors are stacked into one l1 and applied once).
+ *  X, x_dtype (W4_BF16 only), M, K, g, act_bits, q, tok_scale, tok_rowsum: as for
+ *              w4_rotate_quant_act; the outputs are the same bit for bit
+ *  l1        : bf16 [r, K], rank-major (stacked rows of every consumer's L1 transposed)
+ *  r         : 1 <= r <= 64
+ *  t         : out f32 [M, r] with rows ldt floats apart (ldt = 0 means r), X . L1 with exact
+ *              bf16 products and fp32 sums
+ * For g in {64, 256} and K in {1024, 2048, 3072, 4096} one kernel does both and reads X from
+ * HBM once (w4_rotate_quant_act_lowrank_fused reports it); other shapes run the two steps as
+ * two launches.  K % 8 == 0. */
+int w4_rotate_quant_act_lowrank(const void *X, int x_dtype, int64_t M, int64_t K, int g,
+                                int act_bits, void *q, float *tok_scale, int32_t *tok_rowsum,
+                                const void *l1, int r, float *t, int64_t ldt, void *stream);
+/* 1 when w4_rotate_quant_act_lowrank runs as one kernel for (K, g), else 0 (host-only query). */
+int w4_rotate_quant_act_lowrank_fused(int64_t K, int g);
 
 /* w4_lowrank_down - t = x . L1, f32 [M, r], from bf16 x [M, K] and bf16 l1 = L1 transposed,
  * [r, K] rank-major (ComfyUI-INT-Crush README, "Forward Pass" step 6: the first factor of

@@ -30,7 +30,8 @@ __all__ = [
     "W4_ERR_SHAPE", "W4_ERR_UNSUPPORTED", "W4_ERR_ALIGN", "W4_ERR_HIP", "W4_ERR_WORKSPACE",
     "W4_MAX_K", "EXPORTS", "w4_probe_mfma_rate", "w4_linear_noalloc", "w4_noalloc_scratch_bytes",
     "w4_pack_weights_grouped", "w4_linear_cached_rot_grouped", "w4_linear_grouped",
-    "w4_grouped_workspace_bytes", "w4_linear_grouped_workspace_bytes",
+    "w4_grouped_workspace_bytes", "w4_linear_grouped_workspace_bytes", "w4_rotate_quant_act_lowrank",
+    "w4_rotate_quant_act_lowrank_fused",
 ]
 
 W4_OK, W4_ERR_INVALID_ARG, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_HIP, \
@@ -55,7 +56,7 @@ class W4Error(RuntimeError):
 
 class _LowRankC(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("l1", ctypes.c_void_p), ("t", ctypes.c_void_p),
-                ("l2", ctypes.c_void_p), ("r", ctypes.c_int)]
+                ("l2", ctypes.c_void_p), ("r", ctypes.c_int), ("ldt", ctypes.c_int)]
 
 
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -79,6 +80,8 @@ EXPORTS = {
     "w4_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I, _I]),
     "w4_linear_grouped_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I, _I]),
     "w4_lowrank_down": (_I, [_P, _P, _I64, _I64, _I, _P, _P]),
+    "w4_rotate_quant_act_lowrank": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, _P, _I64, _P]),
+    "w4_rotate_quant_act_lowrank_fused": (_I, [_I64, _I]),
     "w4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "w4_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I, _I]),
     "w4_linear_fused": (_I, [_I64, _I64, _I64, _I, _I, _I]),
@@ -214,12 +217,46 @@ def w4_rotate_quant_act(X: torch.Tensor, g: int, act_bits: int):
     return q, s, rs
 
 
+def w4_rotate_quant_act_lowrank(X: torch.Tensor, g: int, act_bits: int, l1: torch.Tensor, t=None):
+    """w4_rotate_quant_act and t = X . L1 in one pass over bf16 X [M, K].
+
+    ``l1`` is bf16 [r, K] (L1 transposed; stack the factors of every linear that reads X).
+    Returns (q, tok_scale, tok_rowsum, t f32 [M, r]); ``t`` may be given (a [M, r] f32 GPU
+    tensor with unit column stride)."""
+    lib = load_library()
+    M, K = _matrix(X, "X")
+    r = _matrix(l1, "l1")[0]
+    _shape(l1, "l1", (r, K))
+    _dev(X, "X", (torch.bfloat16,))
+    _dev(l1, "l1", (torch.bfloat16,))
+    if act_bits == 8:
+        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    else:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=X.device)
+    s = torch.empty((M,), dtype=torch.float32, device=X.device)
+    rs = torch.empty((M,), dtype=torch.int32, device=X.device)
+    if t is None:
+        t = torch.empty((M, r), dtype=torch.float32, device=X.device)
+    _shape(t, "t", (M, r))
+    tp = _strided_t(t)
+    _check(lib.w4_rotate_quant_act_lowrank(X.data_ptr(), W4_BF16, M, K, g, act_bits, q.data_ptr(), s.data_ptr(),
+                                           rs.data_ptr(), l1.data_ptr(), r, tp, int(t.stride(0)), _stream(X.device)))
+    increment_version(t)
+    return q, s, rs, t
+
+
+def w4_rotate_quant_act_lowrank_fused(K: int, g: int) -> bool:
+    return bool(load_library().w4_rotate_quant_act_lowrank_fused(K, g))
+
+
 @dataclass
 class LowRank:
     """Low-rank side branch (x . L1) . L2 on the unrotated input, added before the bias.
 
     Both factors are rank-major: ``l1`` = L1 transposed, bf16 [r, K]; ``l2`` = L2, bf16 [r, N].
-    Give either ``t`` (f32 [M, r] = x . L1, e.g. from ``w4_lowrank_down``) or ``x`` and ``l1``."""
+    Give either ``t`` (f32 [M, r] = x . L1, e.g. from ``w4_lowrank_down``) or ``x`` and ``l1``.
+    ``t`` may be a column range of a wider f32 tensor (unit column stride, any row stride),
+    e.g. a slice of the t that ``w4_rotate_quant_act_lowrank`` computes for stacked factors."""
     l2: torch.Tensor
     x: Optional[torch.Tensor] = None
     l1: Optional[torch.Tensor] = None
@@ -246,10 +283,22 @@ class LowRank:
         c = _LowRankC()
         c.x = _opt(self.x, "lowrank.x", (torch.bfloat16,))
         c.l1 = _opt(self.l1, "lowrank.l1", (torch.bfloat16,))
-        c.t = _opt(self.t, "lowrank.t", (torch.float32,))
+        c.t = _strided_t(self.t) if self.t is not None else None
         c.l2 = _dev(self.l2, "lowrank.l2", (torch.bfloat16,))
         c.r = self.r
+        c.ldt = int(self.t.stride(0)) if self.t is not None else 0
         return c
+
+
+def _strided_t(t: torch.Tensor) -> int:
+    """Device pointer of a low-rank t: f32, on the GPU, unit column stride (any row stride)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("lowrank.t must be a GPU tensor")
+    if t.dtype != torch.float32:
+        raise TypeError("lowrank.t has dtype %s, expected torch.float32" % t.dtype)
+    if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError("lowrank.t must be [M, r] with unit column stride")
+    return t.data_ptr()
 
 
 def _y(M, N, out_i32, device, out):
@@ -531,15 +580,22 @@ class RotationCache:
         return (X.data_ptr(), X.storage_offset(), tuple(X.shape), tuple(X.stride()), X.dtype,
                 X._version, cls._stream_of(X), g, act_bits)
 
-    def get(self, X: torch.Tensor, g: int, act_bits: int):
-        k = self._key(X, g, act_bits)
+    def get(self, X: torch.Tensor, g: int, act_bits: int, l1: Optional[torch.Tensor] = None):
+        """(q, tok_scale, tok_rowsum) for X, computed on a miss.  With ``l1`` (bf16 [r, K], the
+        stacked L1 factors of every linear that reads X) the entry also holds t = X . L1 from
+        the same pass, returned as a fourth value; give the same l1 on every lookup of X."""
+        k = self._key(X, g, act_bits) + ((l1.data_ptr(), tuple(l1.shape), l1._version) if l1 is not None else ())
         hit = self._d.get(k)
         if hit is not None:
             self.hits += 1
             return hit[1]
         self.misses += 1
-        val = w4_rotate_quant_act(X, g, act_bits)
-        self._d[k] = (X, val)
+        if l1 is not None:
+            val = w4_rotate_quant_act_lowrank(X, g, act_bits, l1)
+            self._d[k] = ((X, l1), val)
+        else:
+            val = w4_rotate_quant_act(X, g, act_bits)
+            self._d[k] = (X, val)
         return val
 
     def clear(self):

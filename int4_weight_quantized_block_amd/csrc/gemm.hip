@@ -528,13 +528,13 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         // (keeps this block's t loads here rather than hoisted for all blocks at once)
         if constexpr (EPI == kEpiLowRank) asm volatile("" ::: "memory");
         if (nks) {
-            const float *tr = p.lr_t + min<int64_t>(mrow0 + lr, p.M - 1) * lrr;
+            const float *tr = p.lr_t + min<int64_t>(mrow0 + lr, p.M - 1) * p.lr_ldt;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 if (ks >= nks) break;
                 const int q0 = 16 * ks + 8 * kb;
                 fl8 v;
-                if ((lrr & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
+                if ((lrr & 3) == 0 && (p.lr_ldt & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
                     const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                     const float4 u = q0 < lrr ? *reinterpret_cast<const float4 *>(tr + q0) : z;
                     const float4 w = q0 + 4 < lrr ? *reinterpret_cast<const float4 *>(tr + q0 + 4) : z;
@@ -643,7 +643,7 @@ __global__ void __launch_bounds__(256) k_gemm_tail(LinearArgs p, int tiles_m, in
     // flight), 8-byte l2 reads when the rows allow it
     float lw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (p.lr_t) {
-        const float *tm_ = p.lr_t + m * p.lr_r;
+        const float *tm_ = p.lr_t + m * p.lr_ldt;
         const uint16_t *l2 = p.lr_l2 + n;
         if (nv == 4 && (p.N & 3) == 0) {
 #pragma unroll 8

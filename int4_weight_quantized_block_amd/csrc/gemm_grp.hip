@@ -84,9 +84,10 @@ struct GrpArgs {
     int gw;
     const void *bias;
     int bias_bf16;
-    const float *lr_t;       // [M, r] or null
+    const float *lr_t;       // [M, r] (row stride lr_ldt) or null
     const uint16_t *lr_l2;   // bf16 [r, N]
     int lr_r;
+    int64_t lr_ldt;
     void *Y;
     int64_t M, N, K;
     int S;                   // K ranges
@@ -360,7 +361,7 @@ __global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int ti
         const int64_t m = m0 + wm * FM * 32 + i * 32 + l32;
         if (m >= p.M) continue;
         const float xs = INT ? p.sx[m] * UNSCALE : UNSCALE;
-        const float *tr = r ? p.lr_t + m * r : nullptr;
+        const float *tr = r ? p.lr_t + m * p.lr_ldt : nullptr;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -418,7 +419,7 @@ __global__ void __launch_bounds__(256) k_grp_reduce(GrpArgs p) {
         for (int k = 0; k < p.S; ++k) s += part[k * MN + e];
         float y = s * (AT != 16 ? p.sx[m] * UNSCALE : UNSCALE);
         if (p.lr_t)
-            for (int q = 0; q < p.lr_r; ++q) y = fmaf(p.lr_t[m * p.lr_r + q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), y);
+            for (int q = 0; q < p.lr_r; ++q) y = fmaf(p.lr_t[m * p.lr_ldt + q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), y);
         if (p.bias)
             y += p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
                              : reinterpret_cast<const float *>(p.bias)[n];
@@ -503,6 +504,7 @@ hipError_t launch_gemm_grouped(const GroupedArgs &g, int act_bits, void *ws, siz
     a.lr_t = g.lr_t;
     a.lr_l2 = g.lr_l2;
     a.lr_r = g.lr_t ? g.lr_r : 0;
+    a.lr_ldt = g.lr_ldt;
     a.Y = g.Y;
     a.M = g.M;
     a.N = g.N;

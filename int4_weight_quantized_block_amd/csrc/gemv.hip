@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_ring(LinearArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
             if (p.lr_t) {
-                const float *tr = p.lr_t + m * p.lr_r;
+                const float *tr = p.lr_t + m * p.lr_ldt;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t nc = min<int64_t>(nb + r, p.N - 1);
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(kThreads) k_gemv_split(LinearArgs p, int S, in
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
             if (p.lr_t) {
-                const float *tr = p.lr_t + m * p.lr_r;
+                const float *tr = p.lr_t + m * p.lr_ldt;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t nc = min<int64_t>(nb + r, p.N - 1);
@@ -647,7 +647,7 @@ __global__ void __launch_bounds__(256) k_gemv_reduce(LinearArgs p, int S, const 
                                                : reinterpret_cast<const float *>(p.bias)[n];
         y[r] = fmaf((float)v, sxm * (p.sw[n] * kUnscale), bs);
         if (p.lr_t) {
-            const float *tr = p.lr_t + m * p.lr_r;
+            const float *tr = p.lr_t + m * p.lr_ldt;
             float l = 0.0f;
             for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + n]), l);
             y[r] += l;
@@ -808,7 +808,7 @@ __device__ __forceinline__ void stream_epilogue(const LinearArgs &p, uint8_t *sm
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[r] = fmaf((float)a[r], sxm * sw[r], bs[r]);
         if (p.lr_t) {
-            const float *tr = p.lr_t + m * p.lr_r;
+            const float *tr = p.lr_t + m * p.lr_ldt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t nc = min<int64_t>(nb + r, p.N - 1);

@@ -12,6 +12,12 @@ bool rotquant_supported(int64_t K, int g);
 hipError_t launch_rotquant(const void *X, bool f32in, int64_t M, int64_t K, int g, int bits,
                            void *q, float *tok_scale, int32_t *tok_rowsum, hipStream_t st);
 
+// Rotate + quantize bf16 X and t = X . l1^T (l1 bf16 [r, K], r <= 64; t rows ldt floats apart)
+// in one pass; for g in {64, 256} and K in {1024, 2048, 3072, 4096} (rotquant_lr_fusable).
+bool rotquant_lr_fusable(int64_t K, int g);
+hipError_t launch_rotquant_lr(const void *X, int64_t M, int64_t K, int g, int bits, void *q, float *tok_scale,
+                              int32_t *tok_rowsum, const void *l1, int r, float *t, int64_t ldt, hipStream_t st);
+
 // Offline weight rotate + per-row quantize + nibble pack (g in {0 = none, 16, 64, 256, 1024,
 // 4096}).
 hipError_t launch_pack(const void *W, bool f32in, int64_t N, int64_t K, int g, bool asym,
@@ -30,9 +36,10 @@ struct LinearArgs {
     const uint8_t *zp;     // [N] or null (symmetric)
     const void *bias;      // [N] or null
     int bias_bf16;
-    const float *lr_t;        // [M, lr_r] or null
+    const float *lr_t;        // [M, lr_r] (row stride lr_ldt floats) or null
     const uint16_t *lr_l2;    // bf16 [lr_r, N]
     int lr_r;
+    int64_t lr_ldt;
     void *Y;               // bf16 or int32 [M, N]
     int y_i32;
     int64_t M, N, K;
@@ -64,9 +71,10 @@ struct GroupedArgs {
     int gw;
     const void *bias;         // [N] or null
     int bias_bf16;
-    const float *lr_t;        // [M, lr_r] or null
+    const float *lr_t;        // [M, lr_r] (row stride lr_ldt floats) or null
     const uint16_t *lr_l2;    // bf16 [lr_r, N]
     int lr_r;
+    int64_t lr_ldt;
     void *Y;                  // bf16 [M, N], or int32 (act_bits 8 / 4: sum_k q c, no scales)
     int y_i32;
     int64_t M, N, K;
@@ -78,6 +86,6 @@ hipError_t launch_gemm_grouped(const GroupedArgs &a, int act_bits, void *ws, siz
 hipError_t launch_mfma_rate(int64_t blocks, int iters, bool random_operands, int32_t *sink, hipStream_t st);
 
 hipError_t launch_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r,
-                               float *t, hipStream_t st);
+                               float *t, hipStream_t st, int64_t ldt = 0);
 
 }  // namespace w4

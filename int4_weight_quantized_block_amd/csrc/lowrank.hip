@@ -36,7 +36,7 @@ struct LrL {
 
 template <int RQ>
 __global__ void __launch_bounds__(256) k_lowrank_down(const uint16_t *__restrict__ x, const uint16_t *__restrict__ l1,
-                                                      int64_t M, int K, int r, float *__restrict__ t) {
+                                                      int64_t M, int K, int r, float *__restrict__ t, int64_t ldt) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = LrL<RQ>;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -100,31 +100,33 @@ __global__ void __launch_bounds__(256) k_lowrank_down(const uint16_t *__restrict
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int64_t mm = m0 + 16 * rb + 4 * kg + v;
-            if (mm < M && q < r) t[mm * r + q] = s[v];
+            if (mm < M && q < r) t[mm * ldt + q] = s[v];
         }
     }
 }
 
 template <int RQ>
-hipError_t launch_rq(const uint16_t *x, const uint16_t *l1, int64_t M, int64_t K, int r, float *t, hipStream_t st) {
+hipError_t launch_rq(const uint16_t *x, const uint16_t *l1, int64_t M, int64_t K, int r, float *t, int64_t ldt,
+                     hipStream_t st) {
     using L = LrL<RQ>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_lowrank_down<RQ>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
     if (attr != hipSuccess) return attr;
     const unsigned grid = (unsigned)((M + 31) / 32);
-    hipLaunchKernelGGL(k_lowrank_down<RQ>, dim3(grid), dim3(256), L::LDS, st, x, l1, M, (int)K, r, t);
+    hipLaunchKernelGGL(k_lowrank_down<RQ>, dim3(grid), dim3(256), L::LDS, st, x, l1, M, (int)K, r, t, ldt);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t,
-                               hipStream_t st) {
+                               hipStream_t st, int64_t ldt) {
     if (M == 0) return hipSuccess;
+    if (ldt == 0) ldt = r;
     const uint16_t *xp = reinterpret_cast<const uint16_t *>(x), *lp = reinterpret_cast<const uint16_t *>(l1);
-    if (r <= 16) return launch_rq<1>(xp, lp, M, K, r, t, st);
-    if (r <= 32) return launch_rq<2>(xp, lp, M, K, r, t, st);
-    return launch_rq<4>(xp, lp, M, K, r, t, st);  // r <= 64
+    if (r <= 16) return launch_rq<1>(xp, lp, M, K, r, t, ldt, st);
+    if (r <= 32) return launch_rq<2>(xp, lp, M, K, r, t, ldt, st);
+    return launch_rq<4>(xp, lp, M, K, r, t, ldt, st);  // r <= 64
 }
 
 }  // namespace w4

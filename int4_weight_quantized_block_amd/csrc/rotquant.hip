@@ -392,6 +392,118 @@ k_rotquant_stream(const void *__restrict__ Xv, int64_t M, int K, int T, int R, i
 // only the fma to the VALU's load (measured: faster than swizzling all four stages, and than
 // DPP moves for these two).
 
+// Steps of the row-team layout shared by the kernels below: a lane holds, for each of C
+// 256-element blocks, the 16 elements 16 * cl .. 16 * cl + 15 (cl = lane & 15).
+
+// Widen the raw words of C chunks (bf16: 2 x 16 bytes, fp32: 4 x 16 bytes per chunk) to fp64.
+template <bool F32IN, int C>
+__device__ __forceinline__ void rt_widen(const uint4 (&x)[C][F32IN ? 4 : 2], double (&v)[C][16]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if constexpr (F32IN) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[c][4 * j + 0] = (double)__uint_as_float(x[c][j].x);
+                v[c][4 * j + 1] = (double)__uint_as_float(x[c][j].y);
+                v[c][4 * j + 2] = (double)__uint_as_float(x[c][j].z);
+                v[c][4 * j + 3] = (double)__uint_as_float(x[c][j].w);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                v[c][8 * j + 0] = (double)bf16_lo(x[c][j].x);
+                v[c][8 * j + 1] = (double)bf16_hi(x[c][j].x);
+                v[c][8 * j + 2] = (double)bf16_lo(x[c][j].y);
+                v[c][8 * j + 3] = (double)bf16_hi(x[c][j].y);
+                v[c][8 * j + 4] = (double)bf16_lo(x[c][j].z);
+                v[c][8 * j + 5] = (double)bf16_hi(x[c][j].z);
+                v[c][8 * j + 6] = (double)bf16_lo(x[c][j].w);
+                v[c][8 * j + 7] = (double)bf16_hi(x[c][j].w);
+            }
+        }
+    }
+}
+
+// Walsh-Hadamard butterflies (unnormalised) of every group of G: bits 0-3 in registers, bits
+// 4-5 quad DPP exchanges, and (G = 256) bits 6-7 exchanges with the lanes 4 and 8 apart
+// through ds_swizzle.
+template <int G, int C>
+__device__ __forceinline__ void rt_fwht(double (&v)[C][16], int cl) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) fwht16(v[c]);
+    {
+        const double s1 = (cl & 1) ? -1.0 : 1.0, s2 = (cl & 2) ? -1.0 : 1.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s1, dpp_f64<kQuadXor1>(v[c][i]));
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s2, dpp_f64<kQuadXor2>(v[c][i]));
+    }
+    if constexpr (G == 256) {
+        const double s4 = (cl & 4) ? -1.0 : 1.0, s8 = (cl & 8) ? -1.0 : 1.0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s4, swz_f64<kSwzXor4>(v[c][i]));
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s8, swz_f64<kSwzXor8>(v[c][i]));
+    }
+}
+
+template <int C>
+__device__ __forceinline__ double rt_absmax(const double (&v)[C][16]) {
+    double am = 0.0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = fmax(am, fabs(v[c][i]));
+    return am;
+}
+
+// Codes rint(v * rr) (fp64, the low word of v * rr + 1.5 * 2^52), stored as int8 or packed
+// int4 (each lane's 16 codes of a block are contiguous); returns the lane's code sum.
+template <int BITS, int C>
+__device__ __forceinline__ int rt_quant_store(const double (&v)[C][16], double rr, void *qv, int64_t row, int K,
+                                              int blk0, int cl) {
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    int rowsum = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int q4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int qi = __double2loint(fma(v[c][4 * j + r], rr, kRoundMagic));
+                q4[r] = min(max(qi, -QMAX - 1), QMAX);
+            }
+            d[j] = (uint32_t)(q4[0] & 0xff) | ((uint32_t)(q4[1] & 0xff) << 8) | ((uint32_t)(q4[2] & 0xff) << 16) |
+                   ((uint32_t)(q4[3] & 0xff) << 24);
+            rowsum = __builtin_amdgcn_sdot4((int)d[j], 0x01010101, rowsum, false);
+        }
+        const int64_t e0 = (int64_t)(blk0 + c) * 256 + 16 * cl;
+        if constexpr (BITS == 8) {
+            *reinterpret_cast<uint4 *>(reinterpret_cast<int8_t *>(qv) + row * K + e0) = make_uint4(d[0], d[1], d[2], d[3]);
+        } else {
+            uint32_t x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t lo = d[j] & 0x0F0F0F0Fu;
+                x[j] = lo | (lo >> 4);
+            }
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(qv) + row * (K / 2) + e0 / 2) =
+                make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u));
+        }
+    }
+    return rowsum;
+}
+
 template <int G, int BITS, bool F32IN, int C>
 __global__ void __launch_bounds__(C == 1 ? 1024 : 512) __attribute__((amdgpu_waves_per_eu(2)))
 k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nteams, void *__restrict__ qv,
@@ -423,64 +535,12 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
     int par = 0;
     for (; row < M; row += nteams, par ^= 1) {
         double v[C][16];
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            if constexpr (F32IN) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[c][4 * j + 0] = (double)__uint_as_float(nxt[c][j].x);
-                    v[c][4 * j + 1] = (double)__uint_as_float(nxt[c][j].y);
-                    v[c][4 * j + 2] = (double)__uint_as_float(nxt[c][j].z);
-                    v[c][4 * j + 3] = (double)__uint_as_float(nxt[c][j].w);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    v[c][8 * j + 0] = (double)bf16_lo(nxt[c][j].x);
-                    v[c][8 * j + 1] = (double)bf16_hi(nxt[c][j].x);
-                    v[c][8 * j + 2] = (double)bf16_lo(nxt[c][j].y);
-                    v[c][8 * j + 3] = (double)bf16_hi(nxt[c][j].y);
-                    v[c][8 * j + 4] = (double)bf16_lo(nxt[c][j].z);
-                    v[c][8 * j + 5] = (double)bf16_hi(nxt[c][j].z);
-                    v[c][8 * j + 6] = (double)bf16_lo(nxt[c][j].w);
-                    v[c][8 * j + 7] = (double)bf16_hi(nxt[c][j].w);
-                }
-            }
-        }
+        rt_widen<F32IN, C>(nxt, v);
         if (row + nteams < M) load(row + nteams, nxt);  // in flight during the transform
-
-        // ---- Walsh-Hadamard butterflies (unnormalised)
-#pragma unroll
-        for (int c = 0; c < C; ++c) fwht16(v[c]);
-        {
-            const double s1 = (cl & 1) ? -1.0 : 1.0, s2 = (cl & 2) ? -1.0 : 1.0;
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s1, dpp_f64<kQuadXor1>(v[c][i]));
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s2, dpp_f64<kQuadXor2>(v[c][i]));
-        }
-        if constexpr (G == 256) {
-            const double s4 = (cl & 4) ? -1.0 : 1.0, s8 = (cl & 8) ? -1.0 : 1.0;
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s4, swz_f64<kSwzXor4>(v[c][i]));
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[c][i] = fma(v[c][i], s8, swz_f64<kSwzXor8>(v[c][i]));
-        }
+        rt_fwht<G, C>(v, cl);
 
         // ---- per-token absmax: the wave, then (W > 1) the team through LDS
-        double am = 0.0;
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) am = fmax(am, fabs(v[c][i]));
+        double am = rt_absmax<C>(v);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) am = fmax(am, __shfl_xor(am, off));
         if (W > 1) {
@@ -493,37 +553,8 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
         const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
         if (w == 0 && lane == 0) tok_scale[row] = scale;
 
-        // ---- quantize, pack, store (each lane's 16 codes of a block are contiguous)
-        int rowsum = 0;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            uint32_t d[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int q4[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qi = __double2loint(fma(v[c][4 * j + r], rr, kRoundMagic));
-                    q4[r] = min(max(qi, -QMAX - 1), QMAX);
-                }
-                d[j] = (uint32_t)(q4[0] & 0xff) | ((uint32_t)(q4[1] & 0xff) << 8) | ((uint32_t)(q4[2] & 0xff) << 16) |
-                       ((uint32_t)(q4[3] & 0xff) << 24);
-                rowsum = __builtin_amdgcn_sdot4((int)d[j], 0x01010101, rowsum, false);
-            }
-            const int64_t e0 = (int64_t)(blk0 + c) * 256 + 16 * cl;
-            if constexpr (BITS == 8) {
-                *reinterpret_cast<uint4 *>(reinterpret_cast<int8_t *>(qv) + row * K + e0) = make_uint4(d[0], d[1], d[2], d[3]);
-            } else {
-                uint32_t x[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = d[j] & 0x0F0F0F0Fu;
-                    x[j] = lo | (lo >> 4);
-                }
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint8_t *>(qv) + row * (K / 2) + e0 / 2) =
-                    make_uint2(__builtin_amdgcn_perm(x[1], x[0], 0x06040200u), __builtin_amdgcn_perm(x[3], x[2], 0x06040200u));
-            }
-        }
+        // ---- quantize, pack, store
+        int rowsum = rt_quant_store<BITS, C>(v, rr, qv, row, K, blk0, cl);
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) rowsum += __shfl_xor(rowsum, off);
         if (W > 1) {
@@ -534,6 +565,218 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
         }
         if (w == 0 && lane == 0) tok_rowsum[row] = rowsum;
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Rotate + quantize with the low-rank down-projection in the same pass (ComfyUI-INT-Crush
+// README, "Forward Pass" step 6: the SVD residual from the L1 / L2 factors, on the unrotated
+// activations per "LoRA"; stable-diffusion.cpp PR #2010, "Summary": the activation work is
+// shared per input, so the L1 factors of every linear reading the input are stacked and
+// applied once).  bf16 X, K = 1024 C W as for the row-team kernel (C chunks per lane, W waves
+// per row).
+//
+// Workgroup b of 8 waves owns R consecutive token rows (R = ceil(M / grid) <= 16 NB, the grid
+// at most one workgroup per compute unit, so there is no tail round).  Its 8 / W teams of W
+// waves rotate and quantize rows team, team + 8 / W, ... of them exactly as the row-team kernel
+// does (the next row's loads in flight during a row's transform; a team's absmax and code sum
+// meet in LDS, and the teams step together).  Then the rows, as NB MFMA blocks of 16 tokens,
+// are multiplied by l1 on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16: exact products,
+// fp32 sums): wave w takes one eighth of K for every rank block, so each l1 fragment is
+// loaded once per workgroup and serves all its rows; x fragments come from L2, where the
+// rotation's loads of the same rows have just put them, so X is read from HBM once.  Loads
+// run one 4-step batch ahead of the MFMAs (two batches per loop turn, so every buffer index
+// is a constant and the buffers stay in registers).  The eight K-range partial tiles are
+// added through LDS in a fixed order.
+template <int G, int BITS, int C, int W, int RQ, int NB>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_rotquant_lr(const uint16_t *__restrict__ X, int64_t M, int K, int R, void *__restrict__ qv,
+              float *__restrict__ tok_scale, int32_t *__restrict__ tok_rowsum, const uint16_t *__restrict__ l1, int r,
+              float *__restrict__ t, int64_t ldt) {
+    constexpr int QMAX = BITS == 8 ? 127 : 7;
+    constexpr double INV_SQRT_G = G == 64 ? 0.125 : 0.0625;
+    constexpr int NT = 8 / W;  // teams
+    __shared__ v4f part[8][NB * RQ][64];
+    __shared__ double red_d[2][8];
+    __shared__ int red_i[2][8];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int team = w / W, wt = w % W;
+    const int cl = lane & 15;
+    const int blk0 = (wt * 4 + (lane >> 4)) * C;
+    const int64_t m0 = (int64_t)blockIdx.x * R;
+    const int64_t m1 = min<int64_t>(m0 + R, M);
+
+    // ---- rotate + quantize rows m0 + team, m0 + team + NT, ...  (every team steps R / NT times,
+    // rounded up, so the teams meet at the same barriers; rows past m1 skip loads and stores)
+    auto load = [&](int64_t row, uint4 (&x)[C][2]) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(X + row * K + (int64_t)(blk0 + c) * 256 + 16 * cl);
+            x[c][0] = src[0];
+            x[c][1] = src[1];
+        }
+    };
+    uint4 nxt[C][2];
+    const int iters = (R + NT - 1) / NT;
+    int64_t row = m0 + team;
+    if (row < m1) load(row, nxt);
+    int par = 0;
+#pragma unroll 1
+    for (int it = 0; it < iters; ++it, row += NT, par ^= 1) {
+        const bool valid = row < m1;
+        double v[C][16];
+        rt_widen<false, C>(nxt, v);
+        if (row + NT < m1) load(row + NT, nxt);
+        rt_fwht<G, C>(v, cl);
+        double am = rt_absmax<C>(v);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) am = fmax(am, __shfl_xor(am, off));
+        if constexpr (W > 1) {
+            if (lane == 0) red_d[par][w] = am;
+            __syncthreads();
+            am = red_d[par][team * W];
+            for (int u = 1; u < W; ++u) am = fmax(am, red_d[par][team * W + u]);
+        }
+        const float scale = (float)((am * INV_SQRT_G) / (double)QMAX);
+        const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
+        int rowsum = valid ? rt_quant_store<BITS, C>(v, rr, qv, row, K, blk0, cl) : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) rowsum += __shfl_xor(rowsum, off);
+        if constexpr (W > 1) {
+            if (lane == 0) red_i[par][w] = rowsum;
+            __syncthreads();
+            rowsum = 0;
+            for (int u = 0; u < W; ++u) rowsum += red_i[par][team * W + u];
+        }
+        if (valid && wt == 0 && lane == 0) {
+            tok_scale[row] = scale;
+            tok_rowsum[row] = rowsum;
+        }
+    }
+
+    // ---- t = x . l1^T: A = 16 tokens x 32 k, B = 32 k x 16 ranks; lane l holds token (or rank)
+    // l % 16 of its block and k 8 (l / 16) .. + 7 of the step.  Wave w's eighth of K is
+    // 4 C W steps, taken as C W batches of 4.
+    constexpr int NBAT = C * W;
+    const int s0 = w * 4 * NBAT;
+    const uint16_t *xa[NB];
+    const uint16_t *lb[RQ];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t tok = min<int64_t>(m0 + 16 * nb + cl, m1 - 1);  // rows past the block: clamped, not stored
+        xa[nb] = X + tok * K + 8 * (lane >> 4) + 32 * s0;
+    }
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) lb[q] = l1 + (int64_t)min(16 * q + cl, r - 1) * K + 8 * (lane >> 4) + 32 * s0;
+    v4f acc[NB][RQ];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) acc[nb][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 xb0[4][NB], bb0[4][RQ], xb1[4][NB], bb1[4][RQ];
+    auto fetch = [&](uint4 (&xb)[4][NB], uint4 (&bb)[4][RQ], int bi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) xb[u][nb] = *reinterpret_cast<const uint4 *>(xa[nb] + 32 * (4 * bi + u));
+#pragma unroll
+            for (int q = 0; q < RQ; ++q) bb[u][q] = *reinterpret_cast<const uint4 *>(lb[q] + 32 * (4 * bi + u));
+        }
+    };
+    auto mul = [&](const uint4 (&xb)[4][NB], const uint4 (&bb)[4][RQ]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < RQ; ++q)
+                    acc[nb][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, xb[u][nb]),
+                                                                         __builtin_bit_cast(v8bf, bb[u][q]), acc[nb][q],
+                                                                         0, 0, 0);
+    };
+    fetch(xb0, bb0, 0);
+#pragma unroll 1
+    for (int bi = 0; bi + 1 < NBAT; bi += 2) {
+        fetch(xb1, bb1, bi + 1);
+        mul(xb0, bb0);
+        if (bi + 2 < NBAT) fetch(xb0, bb0, bi + 2);
+        mul(xb1, bb1);
+    }
+    if (NBAT & 1) mul(xb0, bb0);
+
+    // 16x16 layout: lane l, register v holds token 4 (l / 16) + v of the block, rank l % 16
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < RQ; ++q) part[w][nb * RQ + q][lane] = acc[nb][q];
+    __syncthreads();
+    for (int u = w; u < NB * RQ; u += 8) {
+        v4f sum = part[0][u][lane];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) sum += part[k][u][lane];
+        const int nb = u / RQ, q = 16 * (u % RQ) + cl;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t mm = m0 + 16 * nb + 4 * (lane >> 4) + v;
+            if (mm < m1 && q < r) t[mm * ldt + q] = sum[v];
+        }
+    }
+}
+
+template <int G, int BITS, int C, int W, int NB>
+hipError_t launch_lr_nb(const uint16_t *X, int64_t M, int64_t K, int R, void *q, float *s, int32_t *rs,
+                        const uint16_t *l1, int r, float *t, int64_t ldt, hipStream_t st) {
+    const unsigned grid = (unsigned)((M + R - 1) / R);
+    if (r <= 16)
+        hipLaunchKernelGGL((k_rotquant_lr<G, BITS, C, W, 1, NB>), dim3(grid), dim3(512), 0, st, X, M, (int)K, R, q, s,
+                           rs, l1, r, t, ldt);
+    else if (r <= 32)
+        hipLaunchKernelGGL((k_rotquant_lr<G, BITS, C, W, 2, NB>), dim3(grid), dim3(512), 0, st, X, M, (int)K, R, q, s,
+                           rs, l1, r, t, ldt);
+    else
+        hipLaunchKernelGGL((k_rotquant_lr<G, BITS, C, W, 4, NB>), dim3(grid), dim3(512), 0, st, X, M, (int)K, R, q, s,
+                           rs, l1, r, t, ldt);
+    return hipGetLastError();
+}
+
+// Rows per workgroup: at most one workgroup per compute unit while that keeps R <= 32 (two
+// MFMA token blocks), else 32.
+template <int G, int BITS, int C, int W>
+hipError_t launch_lr_cw(const uint16_t *X, int64_t M, int64_t K, void *q, float *s, int32_t *rs, const uint16_t *l1,
+                        int r, float *t, int64_t ldt, hipStream_t st) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    const int R = (int)std::min<int64_t>(32, (M + ncu - 1) / ncu);
+    if (R <= 16) return launch_lr_nb<G, BITS, C, W, 1>(X, M, K, R, q, s, rs, l1, r, t, ldt, st);
+    return launch_lr_nb<G, BITS, C, W, 2>(X, M, K, R, q, s, rs, l1, r, t, ldt, st);
+}
+
+// (C, W) with K = 1024 C W: 3 or 4 chunks per lane and 1, 2, 4 or 8 waves per row
+bool lr_split(int64_t K, int &C, int &W) {
+    if (K <= 0 || K % 1024) return false;
+    const int64_t n = K / 1024;
+    for (int c : {3, 4, 2, 1}) {
+        if (n % c) continue;
+        const int64_t w = n / c;
+        if (w == 1 || w == 2 || w == 4 || w == 8) {
+            C = c;
+            W = (int)w;
+            return true;
+        }
+    }
+    return false;
+}
+
+template <int G, int BITS>
+hipError_t launch_lr_gb(const uint16_t *X, int64_t M, int64_t K, void *q, float *s, int32_t *rs, const uint16_t *l1,
+                        int r, float *t, int64_t ldt, hipStream_t st) {
+    int C = 0, W = 0;
+    if (!lr_split(K, C, W)) return hipErrorInvalidValue;
+#define W4_LR(CC, WW) \
+    if (C == CC && W == WW) return launch_lr_cw<G, BITS, CC, WW>(X, M, K, q, s, rs, l1, r, t, ldt, st)
+    W4_LR(1, 1); W4_LR(2, 1); W4_LR(3, 1); W4_LR(4, 1);
+    W4_LR(3, 2); W4_LR(4, 2); W4_LR(3, 4); W4_LR(4, 4); W4_LR(3, 8); W4_LR(4, 8);
+#undef W4_LR
+    return hipErrorInvalidValue;
 }
 
 // (C, W) for the row-team kernel, or false.  A few rows (M <= 64) take one chunk per lane and
@@ -759,6 +1002,23 @@ hipError_t launch_gen(const void *X, bool f32in, int64_t M, int64_t K, int bits,
 }
 
 }  // namespace
+
+bool rotquant_lr_fusable(int64_t K, int g) {
+    int C = 0, W = 0;
+    return (g == 64 || g == 256) && lr_split(K, C, W);
+}
+
+hipError_t launch_rotquant_lr(const void *X, int64_t M, int64_t K, int g, int bits, void *q, float *tok_scale,
+                              int32_t *tok_rowsum, const void *l1, int r, float *t, int64_t ldt, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (!rotquant_lr_fusable(K, g) || r < 1 || r > 64) return hipErrorInvalidValue;
+    const uint16_t *x = static_cast<const uint16_t *>(X), *l = static_cast<const uint16_t *>(l1);
+    if (g == 64)
+        return bits == 8 ? launch_lr_gb<64, 8>(x, M, K, q, tok_scale, tok_rowsum, l, r, t, ldt, st)
+                         : launch_lr_gb<64, 4>(x, M, K, q, tok_scale, tok_rowsum, l, r, t, ldt, st);
+    return bits == 8 ? launch_lr_gb<256, 8>(x, M, K, q, tok_scale, tok_rowsum, l, r, t, ldt, st)
+                     : launch_lr_gb<256, 4>(x, M, K, q, tok_scale, tok_rowsum, l, r, t, ldt, st);
+}
 
 bool rotquant_supported(int64_t K, int g) {
     if (g == 16 || g == 1024 || g == 4096) return K > 0 && K % g == 0;

@@ -112,7 +112,7 @@ int scratch_for_stream(const char *fn, hipStream_t st, void **out) {
 
 extern "C" {
 
-const char *w4_version(void) { return "w4 0.1 (gfx950)"; }
+const char *w4_version(void) { return "w4 0.2 (gfx950)"; }
 
 const char *w4_last_error(void) { return g_last_error.c_str(); }
 
@@ -191,6 +191,38 @@ int w4_rotate_quant_act(const void *X, int x_dtype, int64_t M, int64_t K, int g,
                       fn);
 }
 
+int w4_rotate_quant_act_lowrank(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits, void *q,
+                                float *tok_scale, int32_t *tok_rowsum, const void *l1, int r, float *t, int64_t ldt,
+                                void *stream) {
+    const char *fn = "w4_rotate_quant_act_lowrank";
+    if (x_dtype != W4_BF16) return fail(W4_ERR_UNSUPPORTED, "%s: the low-rank branch takes bf16 X", fn);
+    if (act_bits != 4 && act_bits != 8) return fail(W4_ERR_UNSUPPORTED, "%s: act_bits=%d", fn, act_bits);
+    if (M < 0) return fail(W4_ERR_SHAPE, "%s: M=%lld < 0", fn, (long long)M);
+    if (M > (int64_t)1 << 31) return fail(W4_ERR_SHAPE, "%s: M too large", fn);
+    if (int e = check_k(fn, K, g)) return e;
+    if (!w4::rotquant_supported(K, g))
+        return fail(W4_ERR_UNSUPPORTED, "%s: K=%lld has no supported split for g=%d", fn, (long long)K, g);
+    if (K % 8) return fail(W4_ERR_SHAPE, "%s: K=%lld must be a multiple of 8", fn, (long long)K);
+    if (r < 1 || r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: r=%d (supported 1..64)", fn, r);
+    if (ldt != 0 && ldt < r) return fail(W4_ERR_INVALID_ARG, "%s: ldt=%lld < r=%d", fn, (long long)ldt, r);
+    if (M == 0) return ok();
+    W4_CHECK_PTR(X);
+    W4_CHECK_PTR(q);
+    W4_CHECK_PTR(tok_scale);
+    W4_CHECK_PTR(tok_rowsum);
+    W4_CHECK_PTR(l1);
+    W4_CHECK_PTR(t);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t ld = ldt ? ldt : r;
+    if (w4::rotquant_lr_fusable(K, g))
+        return hip_status(w4::launch_rotquant_lr(X, M, K, g, act_bits, q, tok_scale, tok_rowsum, l1, r, t, ld, st), fn);
+    hipError_t e = w4::launch_rotquant(X, false, M, K, g, act_bits, q, tok_scale, tok_rowsum, st);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(w4::launch_lowrank_down(X, l1, M, K, r, t, st, ld), fn);
+}
+
+int w4_rotate_quant_act_lowrank_fused(int64_t K, int g) { return w4::rotquant_lr_fusable(K, g) ? 1 : 0; }
+
 int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, float *t, void *stream) {
     const char *fn = "w4_lowrank_down";
     if (M < 0 || K < 8 || K % 8 || K > W4_MAX_K)
@@ -234,6 +266,7 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     const float *t = nullptr;
     const uint16_t *l2 = nullptr;
     int r = 0;
+    int ldt = 0;
     size_t tbytes = 0;  // workspace bytes taken by the low-rank t
     if (lr && y_kind == W4_OUT_BF16) {
         r = lr->r;
@@ -243,7 +276,9 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
         l2 = static_cast<const uint16_t *>(lr->l2);
         if (lr->t) {
             if (!aligned16(lr->t)) return fail(W4_ERR_ALIGN, "%s: lowrank t not 16-byte aligned", fn);
+            if (lr->ldt != 0 && lr->ldt < r) return fail(W4_ERR_INVALID_ARG, "%s: lowrank ldt=%d < r=%d", fn, lr->ldt, r);
             t = lr->t;
+            ldt = lr->ldt ? lr->ldt : r;
         } else {
             if (!lr->x || !lr->l1) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
             if (!aligned16(lr->x) || !aligned16(lr->l1))
@@ -260,6 +295,7 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
         hipError_t e = w4::launch_lowrank_down(lr->x, lr->l1, M, K, r, tw, st);
         if (e != hipSuccess) return hip_status(e, fn);
         t = tw;
+        ldt = r;
     }
     w4::LinearArgs a;
     a.A = static_cast<const uint8_t *>(q);
@@ -273,6 +309,7 @@ static int linear_impl(const char *fn, const void *q, const float *tok_scale, co
     a.lr_t = t;
     a.lr_l2 = l2;
     a.lr_r = r;
+    a.lr_ldt = ldt;
     a.Y = Y;
     a.y_i32 = y_kind == W4_OUT_I32;
     a.M = M;
@@ -446,6 +483,7 @@ static int grouped_impl(const char *fn, const void *act, const float *tok_scale,
     const float *t = nullptr;
     const uint16_t *l2 = nullptr;
     int r = 0;
+    int ldt = 0;
     size_t tbytes = 0;
     if (lr && y_kind == W4_OUT_BF16) {
         r = lr->r;
@@ -455,7 +493,9 @@ static int grouped_impl(const char *fn, const void *act, const float *tok_scale,
         l2 = static_cast<const uint16_t *>(lr->l2);
         if (lr->t) {
             if (!aligned16(lr->t)) return fail(W4_ERR_ALIGN, "%s: lowrank t not 16-byte aligned", fn);
+            if (lr->ldt != 0 && lr->ldt < r) return fail(W4_ERR_INVALID_ARG, "%s: lowrank ldt=%d < r=%d", fn, lr->ldt, r);
             t = lr->t;
+            ldt = lr->ldt ? lr->ldt : r;
         } else {
             if (!lr->x || !lr->l1) return fail(W4_ERR_INVALID_ARG, "%s: lowrank needs t or (x, l1)", fn);
             if (!aligned16(lr->x) || !aligned16(lr->l1))
@@ -472,6 +512,7 @@ static int grouped_impl(const char *fn, const void *act, const float *tok_scale,
         hipError_t e = w4::launch_lowrank_down(lr->x, lr->l1, M, K, r, tw, st);
         if (e != hipSuccess) return hip_status(e, fn);
         t = tw;
+        ldt = r;
     }
     w4::GroupedArgs a{};
     a.A = act;
@@ -484,6 +525,7 @@ static int grouped_impl(const char *fn, const void *act, const float *tok_scale,
     a.lr_t = t;
     a.lr_l2 = l2;
     a.lr_r = r;
+    a.lr_ldt = ldt;
     a.Y = Y;
     a.y_i32 = y_kind == W4_OUT_I32;
     a.M = M;

@@ -576,3 +576,43 @@ def test_fused_single_token_matches_oracle(N, K, g, bits, asym, lr):
     check_codes(codes, ref["a"]["q"], ref["a"]["pre"], "act codes")
     want = oracle.gemm_i64(codes.astype(np.int8), oracle.weight_operand(pw["packed"], pw["zp"], asym))
     assert np.array_equal(acc, want)
+
+
+# --------------------------------------------------------------------------- rotate-quantize + low-rank
+@pytest.mark.parametrize("M,K,g,bits,r", [
+    (4608, 3072, 256, 8, 64),    # the DiT block input, QKV and MLP-up factors stacked
+    (300, 3072, 256, 4, 32),
+    (37, 4096, 64, 8, 20),       # ragged M and r
+    (5, 1024, 256, 8, 16),       # fewer tokens than a block
+    (129, 2048, 64, 4, 48),
+    (40, 12288, 256, 8, 32),     # four waves per row
+    (4608, 12288, 256, 8, 32),   # the DiT down-projection input
+    (77, 8192, 64, 4, 64),       # two waves per row
+    (3, 5120, 256, 8, 16),       # K = 5 x 1024 has no row-team split: two launches
+])
+def test_rotate_quant_lowrank_matches_oracle(M, K, g, bits, r):
+    """One pass gives the same codes, scales and row sums as w4_rotate_quant_act (bit for bit)
+    and t = X . L1 within fp32 rounding of the oracle's fp64 product; t can be a column range
+    of a wider tensor (row stride)."""
+    say("rotquant+lowrank M=%d K=%d g=%d bits=%d r=%d fused=%s" % (M, K, g, bits, r,
+                                                                    w4.w4_rotate_quant_act_lowrank_fused(K, g)))
+    X = act_input(M, K, seed=M + K + r)
+    rg = rng(M + r)
+    L1 = torch.from_numpy((rg.standard_normal((K, r)) * 0.05).astype(np.float32)).to(torch.bfloat16)
+    Xd = X.to(DEV)
+    l1 = L1.t().contiguous().to(DEV)
+    q, s, rs, t = w4.w4_rotate_quant_act_lowrank(Xd, g, bits, l1)
+    q0, s0, rs0 = w4.w4_rotate_quant_act(Xd, g, bits)
+    assert torch.equal(q, q0) and torch.equal(s.view(torch.int32), s0.view(torch.int32)) and torch.equal(rs, rs0)
+    tref = oracle.to_f64(X) @ oracle.to_f64(L1)
+    assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
+    # into columns [8, 8 + r) of a [M, r + 12] tensor
+    wide = torch.full((M, r + 12), 7.0, dtype=torch.float32, device=DEV)
+    w4.w4_rotate_quant_act_lowrank(Xd, g, bits, l1, t=wide[:, 8:8 + r])
+    assert torch.equal(wide[:, 8:8 + r], t)
+    assert bool((wide[:, :8] == 7.0).all()) and bool((wide[:, 8 + r:] == 7.0).all())
+    if M >= 300:   # the codes against the oracle too
+        ref = oracle.rotate_quant_act(X[:64], g, bits)
+        qg = np_(q)[:64]
+        codes = oracle.unpack_nibbles(qg, signed=True) if bits == 4 else qg
+        check_codes(codes, ref["q"], ref["pre"], "act codes")

@@ -43,7 +43,7 @@ def weights_on_gpu(W, g, asym):
     return (packed, s, zp), ref
 
 
-def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag=""):
+def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag="", codes=None):
     """Run one linear on the GPU at full size and check it against the oracle on every row.
 
     Checked: the GPU's packed weights and scales; its token scales and activation codes; the
@@ -56,7 +56,9 @@ def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag=""):
     (packed, s_w, zp), pw = weights_on_gpu(W, g, asym)
     Xd = X if X.is_cuda else X.to(DEV)
     Xc = X.cpu() if X.is_cuda else X
-    if cache is not None:
+    if codes is not None:
+        q, sx, rs = codes
+    elif cache is not None:
         q, sx, rs = cache.get(Xd, g, bits)
     else:
         q, sx, rs = w4.w4_rotate_quant_act(Xd, g, bits)
@@ -92,7 +94,7 @@ def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag=""):
     say("  %s rel frob %.3e (worst 32-row block %.3e)" % (tag, err, worst))
     assert err <= FROB_TOL, (tag, err)
     assert worst <= 2 * FROB_TOL, (tag, worst)
-    if cache is None:  # the uncached entry point gives the same bits
+    if cache is None and codes is None:  # the uncached entry point gives the same bits
         y2 = w4.w4_linear(Xd, g, bits, packed, s_w, zp, bias=bias.to(DEV), lowrank=low if lowrank else None)
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), tag + " w4_linear vs cached"
     return y, y64
@@ -127,26 +129,30 @@ def test_small_m_asym_w4a8(M, K, N):
 
 @pytest.mark.parametrize("b", [0, 19])
 def test_double_block_cached_lowrank(b):
-    """One DiT double block: QKV and MLP-up share the rotated block input through the cache;
-    every linear carries a rank-32 low-rank branch on its unrotated input."""
+    """One DiT double block: QKV and MLP-up share the rotated block input through the cache,
+    and their stacked L1 factors give both low-rank inputs t in the same pass; every linear
+    carries a rank-32 low-rank branch on its unrotated input."""
     say("double block %d: drawing inputs on the GPU" % b)
     blk = synth.double_block(b, DEV)
-    M = blk["x"].shape[0]
     cache = w4.RotationCache()
+    l1_x = torch.cat([blk["qkv"]["L1"], blk["up"]["L1"]], dim=0)   # stacked [64, K]
+    r = blk["qkv"]["L1"].shape[0]
     outs = {}
-    for name, inp in (("qkv", blk["x"]), ("up", blk["x"]), ("out", blk["attn"])):
+    for name, inp, l1, cols in (("qkv", blk["x"], l1_x, slice(0, r)), ("up", blk["x"], l1_x, slice(r, 2 * r)),
+                                ("out", blk["attn"], blk["out"]["L1"], slice(0, r))):
         p = blk[name]
-        t = w4.w4_lowrank_down(inp, p["L1"])
-        low = w4.LowRank(l2=p["L2"], t=t)
+        q, sx, rs, t = cache.get(inp, 256, 8, l1=l1)
+        low = w4.LowRank(l2=p["L2"], t=t[:, cols])
         outs[name], y64 = check_layer(inp, p["W"].cpu(), p["bias"], 256, 8, False,
-                                      lowrank=(p["L1"], p["L2"], low), cache=cache, tag="block%d.%s" % (b, name))
+                                      lowrank=(p["L1"], p["L2"], low), codes=(q, sx, rs), tag="block%d.%s" % (b, name))
         if name == "up":
             h = oracle.gelu_bf16(oracle.bf16_rne(y64)).to(DEV)   # the down-proj input, all rows
         del y64
     assert cache.hits == 1 and cache.misses == 2
-    # down-proj input: GELU of the oracle's up-projection output (computed above, all rows)
+    # down-proj input: GELU of the oracle's up-projection output (computed above, all rows);
     p = blk["down"]
-    low = w4.LowRank(l2=p["L2"], x=h, l1=p["L1"])
-    check_layer(h, p["W"].cpu(), p["bias"], 256, 8, False, lowrank=(p["L1"], p["L2"], low),
+    q, sx, rs, t = w4.w4_rotate_quant_act_lowrank(h, 256, 8, p["L1"])
+    low = w4.LowRank(l2=p["L2"], t=t)
+    check_layer(h, p["W"].cpu(), p["bias"], 256, 8, False, lowrank=(p["L1"], p["L2"], low), codes=(q, sx, rs),
                 tag="block%d.down" % b)
     cache.clear()
