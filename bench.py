@@ -35,6 +35,7 @@ reports them under "detail" (--no-small-m-detail skips that).
                dense int8 rate with random and with constant operands
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -65,6 +66,9 @@ def parse():
                     choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny", "mfma_peak",
                              "attn_proj_grouped", "attn_proj_w4a16", "small_m_w4a16"])
     ap.add_argument("--gw", type=int, default=128, help="grouped-scale workloads: inputs per weight scale")
+    ap.add_argument("--lowrank", type=int, default=0, metavar="R",
+                    help="single-linear workloads: add a rank-R low-rank branch (x . L1 computed once, untimed, "
+                         "and added in the GEMM epilogue)")
     ap.add_argument("--no-small-m-detail", action="store_true",
                     help="attn_proj: skip timing the two small-M text-encoder shapes reported in detail")
     ap.add_argument("--summarize-trace", metavar="TRACE", default=None,
@@ -319,6 +323,8 @@ def main():
         return bench_mfma_peak(args, dev)
 
     layer_specs, cfg = build_workload(args, dev)
+    if args.lowrank:
+        cfg = dict(cfg, lowrank=args.lowrank)
     spec = layer_specs[0][0]
     r = time_layer(args, dev, spec)
     lin, fused, t_rq, t_mm, wall = r["lin"], r["fused"], r["t_rq"], r["t_mm"], r["wall"]
@@ -446,15 +452,25 @@ def time_layer(args, dev, spec):
         fused = False
         kernel = "k_gemm_grp"
     else:
+        lrp = None
+        if getattr(args, "lowrank", 0):
+            # the branch's t = x . L1 precomputed (untimed); the GEMM adds t . L2 in its epilogue
+            gen = torch.Generator(device=dev).manual_seed(2011)
+            R = args.lowrank
+            t_lr = (torch.randn(M, R, generator=gen, device=dev) * 0.5).contiguous()
+            l2_lr = (torch.randn(R, N, generator=gen, device=dev) * 0.01).to(torch.bfloat16).contiguous()
+            lr_c = w4.LowRank(l2=l2_lr, t=t_lr).as_c()
+            lr_keep = (t_lr, l2_lr, lr_c)
+            lrp = ctypes.byref(lr_c)
         rq_args = [(x.data_ptr(), xdt, M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr) for x in Xs]
         mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
-                    z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, None, M, N, K,
+                    z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, lrp, M, N, K,
                     Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
         # the step: the whole layer through w4_linear (rotate + quantize into its workspace, then
         # the GEMM; one fused launch for a single token, see w4_linear_fused)
         wsl = torch.empty((max(256, w4.w4_linear_workspace_bytes(M, N, K, bits)),), dtype=torch.uint8, device=dev)
         lin_args = [(x.data_ptr(), xdt, M, K, g, bits, p.data_ptr(), s.data_ptr(),
-                     z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, None, N, Y.data_ptr(),
+                     z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, lrp, N, Y.data_ptr(),
                      w4.W4_OUT_BF16, wsl.data_ptr(), wsl.numel(), sptr) for x, (p, s, z) in zip(Xs, Ps)]
         f_mm, f_lin = L.w4_linear_cached_rot, L.w4_linear
         fused = bool(L.w4_linear_fused(M, N, K, g, bits, xdt))

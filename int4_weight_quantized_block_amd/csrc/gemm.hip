@@ -216,7 +216,11 @@ __device__ __forceinline__ void half_stage(const Frags<ABITS> &fc, const Ops &oc
 // Output forms, one kernel each (the epilogue is straight-line code run once per tile, so
 // leaving out what a launch does not need keeps it short)
 // kEpiPartial: raw int32 partial tiles of one K range (the split tail, summed by k_gemm_tail)
-enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2, kEpiPartial = 3 };
+enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2, kEpiPartial = 3, kEpiLowRank16 = 4, kEpiLowRank32 = 5 };
+// bf16 output with the low-rank branch, by rank: r <= 16, r <= 32 or r <= 64 (1, 2, 4 k-steps
+// of 16 ranks on the bf16 MFMA)
+constexpr bool epi_lr(int e) { return e == kEpiLowRank || e == kEpiLowRank16 || e == kEpiLowRank32; }
+constexpr int epi_lrk(int e) { return e == kEpiLowRank16 ? 1 : e == kEpiLowRank32 ? 2 : 4; }
 
 // The tiles one launch covers: ids [base, base + count); with kEpiPartial each tile is split
 // into kparts equal K ranges (one workgroup each) whose partial tiles go to part.
@@ -288,7 +292,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // over the waves, when its rows are 16-byte aligned (N % 8 == 0), else element by element
     // through registers (a one-off wait, ragged N only).  The prologue's wait and barrier
     // make it visible to every wave.
-    if constexpr (EPI == kEpiLowRank) {
+    if constexpr (epi_lr(EPI)) {
         if (l2_dma) {
             constexpr int CPR = BN * 2 / 16;  // 24 chunks of 16 bytes per row
             const int nins = (CPR * p.lr_r + 63) / 64;
@@ -468,28 +472,26 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     const float *c_sw = reinterpret_cast<const float *>(smem + L::C_SW);
     const uint8_t *c_bias = smem + L::C_BIAS;
     const uint8_t *c_zp = smem + L::C_ZP;
-    // per-feature constants of this lane's 12 groups of 4 features
-    float swv[FN][4][4], bsv[FN][4][4];
-    int zcv[FN][4][4];  // (8 - z) * 2^SHIFT
+    // per-feature constants of a group of 4 features (row scale with the code factor, bias,
+    // (8 - z) * 2^SHIFT), read from LDS where they are used: holding all 12 groups in
+    // registers through the epilogue made the low-rank form spill, and each reload's vmcnt(0)
+    // then also waited for the output stores of the previous token block
+    auto consts = [&](int j, int g, float (&sw)[4], float (&bs)[4], int (&zc)[4]) __attribute__((always_inline)) {
+        const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
+        const float4 sw4 = *reinterpret_cast<const float4 *>(c_sw + nl);
+        sw[0] = sw4.x * kUnscale; sw[1] = sw4.y * kUnscale; sw[2] = sw4.z * kUnscale; sw[3] = sw4.w * kUnscale;
+        const uint4 b4 = p.bias ? *reinterpret_cast<const uint4 *>(c_bias + 4 * nl) : make_uint4(0, 0, 0, 0);
+        const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
-            const float4 sw4 = *reinterpret_cast<const float4 *>(c_sw + nl);
-            swv[j][g][0] = sw4.x * kUnscale; swv[j][g][1] = sw4.y * kUnscale;
-            swv[j][g][2] = sw4.z * kUnscale; swv[j][g][3] = sw4.w * kUnscale;
-            const uint4 b4 = p.bias ? *reinterpret_cast<const uint4 *>(c_bias + 4 * nl) : make_uint4(0, 0, 0, 0);
-            const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bsv[j][g][r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
-            if constexpr (ASYM) {
-                const uint4 z4 = *reinterpret_cast<const uint4 *>(c_zp + 4 * nl);
-                zcv[j][g][0] = (8 - (int)z4.x) << SHIFT; zcv[j][g][1] = (8 - (int)z4.y) << SHIFT;
-                zcv[j][g][2] = (8 - (int)z4.z) << SHIFT; zcv[j][g][3] = (8 - (int)z4.w) << SHIFT;
-            }
+        for (int r = 0; r < 4; ++r) bs[r] = __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+        if constexpr (ASYM) {
+            const uint4 z4 = *reinterpret_cast<const uint4 *>(c_zp + 4 * nl);
+            zc[0] = (8 - (int)z4.x) << SHIFT; zc[1] = (8 - (int)z4.y) << SHIFT;
+            zc[2] = (8 - (int)z4.z) << SHIFT; zc[3] = (8 - (int)z4.w) << SHIFT;
+        } else {
+            zc[0] = zc[1] = zc[2] = zc[3] = 0;
         }
-    }
+    };
     if constexpr (EPI == kEpiI32) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -501,9 +503,12 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + 4 * kb;
+                    float sw[4], bs[4];
+                    int zc[4];
+                    consts(j, g, sw, bs, zc);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < p.N) Y[n + r] = (acc[j][i][4 * g + r] + (ASYM ? zcv[j][g][r] * rsv[i] : 0)) >> SHIFT;
+                        if (n + r < p.N) Y[n + r] = (acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0)) >> SHIFT;
                 }
         }
         return;
@@ -518,60 +523,75 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // the B operand (columns = tokens).  Each lane holds the same 8 consecutive ranks q of
     // both operands (k-steps of 16, ranks past r zero).  t (f32) goes in as a bf16 high part
     // plus a bf16 remainder, so its products keep about 16 significant bits; l2 is bf16.
-    const int lrr = EPI == kEpiLowRank ? p.lr_r : 0;
-    const int nks = (lrr + 15) >> 4;  // uniform
+    constexpr int LRK = epi_lrk(EPI);
+    const int lrr = epi_lr(EPI) ? p.lr_r : 0;
     const uint16_t *l2t = reinterpret_cast<const uint16_t *>(smem + L::LDS_BYTES);
+    // t of token block i (8 consecutive ranks per k-step per lane), as raw floats: each block's
+    // loads are issued before the previous block's output stores, since a wait for a load
+    // issued after stores (vmcnt counts both) would also wait for those stores to drain.  One
+    // block at a time keeps the epilogue's registers low; the scheduling barriers keep the
+    // unrolled blocks from overlapping (the register ceiling would otherwise push the main
+    // loop's values into AGPRs).
+    fl8 tv[LRK];
+    auto load_t = [&](int i) __attribute__((always_inline)) {
+        const float *tr = p.lr_t + min<int64_t>(m0 + wm * WTM + i * 32 + lr, p.M - 1) * p.lr_ldt;
+#pragma unroll
+        for (int ks = 0; ks < LRK; ++ks) {
+            const int q0 = 16 * ks + 8 * kb;
+            if ((lrr & 3) == 0 && (p.lr_ldt & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
+                const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const float4 u = q0 < lrr ? *reinterpret_cast<const float4 *>(tr + q0) : z;
+                const float4 w = q0 + 4 < lrr ? *reinterpret_cast<const float4 *>(tr + q0 + 4) : z;
+                tv[ks] = fl8{u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tv[ks][e] = q0 + e < lrr ? tr[q0 + e] : 0.0f;
+            }
+        }
+    };
+    if constexpr (epi_lr(EPI)) load_t(0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        if constexpr (epi_lr(EPI)) __builtin_amdgcn_sched_barrier(0);
         const int64_t mrow0 = m0 + wm * WTM + i * 32;
-        bf8 th[4], tl[4];
-        // (keeps this block's t loads here rather than hoisted for all blocks at once)
-        if constexpr (EPI == kEpiLowRank) asm volatile("" ::: "memory");
-        if (nks) {
-            const float *tr = p.lr_t + min<int64_t>(mrow0 + lr, p.M - 1) * p.lr_ldt;
+        bf8 th[LRK], tl[LRK];
+        if constexpr (epi_lr(EPI)) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks >= nks) break;
-                const int q0 = 16 * ks + 8 * kb;
-                fl8 v;
-                if ((lrr & 3) == 0 && (p.lr_ldt & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
-                    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    const float4 u = q0 < lrr ? *reinterpret_cast<const float4 *>(tr + q0) : z;
-                    const float4 w = q0 + 4 < lrr ? *reinterpret_cast<const float4 *>(tr + q0 + 4) : z;
-                    v = fl8{u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = q0 + e < lrr ? tr[q0 + e] : 0.0f;
-                }
-                th[ks] = __builtin_convertvector(v, bf8);
-                tl[ks] = __builtin_convertvector(v - __builtin_convertvector(th[ks], fl8), bf8);
+            for (int ks = 0; ks < LRK; ++ks) {
+                th[ks] = __builtin_convertvector(tv[ks], bf8);
+                tl[ks] = __builtin_convertvector(tv[ks] - __builtin_convertvector(th[ks], fl8), bf8);
             }
+            if (i + 1 < FM) load_t(i + 1);  // before this block's stores
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+            if constexpr (epi_lr(EPI)) __builtin_amdgcn_sched_barrier(0);
             fl16 lacc = {};
             const int nl = wn * WTN + j * 32 + lr;  // feature within the tile
+            if constexpr (epi_lr(EPI)) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if (ks >= nks) break;
-                uint32_t h[8];
+                for (int ks = 0; ks < LRK; ++ks) {
+                    uint32_t h[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int q = 16 * ks + 8 * kb + e;
-                    h[e] = q < lrr ? l2t[q * BN + nl] : 0u;
+                    for (int e = 0; e < 8; ++e) {
+                        const int q = 16 * ks + 8 * kb + e;
+                        h[e] = q < lrr ? l2t[q * BN + nl] : 0u;
+                    }
+                    const bf8 la = __builtin_bit_cast(bf8, make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16,
+                                                                      h[4] | h[5] << 16, h[6] | h[7] << 16));
+                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, th[ks], lacc, 0, 0, 0);
+                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, tl[ks], lacc, 0, 0, 0);
                 }
-                const bf8 la = __builtin_bit_cast(bf8, make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16,
-                                                                  h[4] | h[5] << 16, h[6] | h[7] << 16));
-                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, th[ks], lacc, 0, 0, 0);
-                lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, tl[ks], lacc, 0, 0, 0);
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float y[4];
+                float y[4], sw[4], bs[4];
+                int zc[4];
+                consts(j, g, sw, bs, zc);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int a = acc[j][i][4 * g + r] + (ASYM ? zcv[j][g][r] * rsv[i] : 0);
-                    y[r] = fmaf((float)a, sxv[i] * swv[j][g][r], bsv[j][g][r]) + lacc[4 * g + r];
+                    const int a = acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0);
+                    y[r] = fmaf((float)a, sxv[i] * sw[r], bs[r]) + lacc[4 * g + r];
                 }
                 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
                 typedef float fl2 __attribute__((ext_vector_type(2)));
@@ -639,21 +659,29 @@ __global__ void __launch_bounds__(256) k_gemm_tail(LinearArgs p, int tiles_m, in
         for (int r = 0; r < nv; ++r) Y[r] = a[r] >> SHIFT;
         return;
     }
-    // low-rank term of the 4 outputs: independent loads per rank (unrolled, so many are in
-    // flight), 8-byte l2 reads when the rows allow it
+    // low-rank term of the 4 outputs: the loads of 16 ranks at a time are all issued before
+    // their fmas (one round trip per 16 ranks), 8-byte l2 reads when the rows allow it
     float lw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (p.lr_t) {
         const float *tm_ = p.lr_t + m * p.lr_ldt;
         const uint16_t *l2 = p.lr_l2 + n;
         if (nv == 4 && (p.N & 3) == 0) {
-#pragma unroll 8
-            for (int q = 0; q < p.lr_r; ++q) {
-                const float tq = tm_[q];
-                const uint2 w = *reinterpret_cast<const uint2 *>(l2 + (int64_t)q * p.N);
-                lw[0] = fmaf(tq, bf16_lo(w.x), lw[0]);
-                lw[1] = fmaf(tq, bf16_hi(w.x), lw[1]);
-                lw[2] = fmaf(tq, bf16_lo(w.y), lw[2]);
-                lw[3] = fmaf(tq, bf16_hi(w.y), lw[3]);
+            for (int q0 = 0; q0 < p.lr_r; q0 += 16) {
+                float tq[16];
+                uint2 w[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int q = min(q0 + u, p.lr_r - 1);  // past r: a repeated rank, weighted 0 below
+                    tq[u] = q0 + u < p.lr_r ? tm_[q] : 0.0f;
+                    w[u] = *reinterpret_cast<const uint2 *>(l2 + (int64_t)q * p.N);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    lw[0] = fmaf(tq[u], bf16_lo(w[u].x), lw[0]);
+                    lw[1] = fmaf(tq[u], bf16_hi(w[u].x), lw[1]);
+                    lw[2] = fmaf(tq[u], bf16_lo(w[u].y), lw[2]);
+                    lw[3] = fmaf(tq[u], bf16_hi(w[u].y), lw[3]);
+                }
             }
         } else {
             for (int r = 0; r < nv; ++r)
@@ -711,7 +739,7 @@ hipError_t launch_t(const LinearArgs &a, const TileRange &tr, unsigned grid, hip
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(base + maxl2));
     if (attr != hipSuccess) return attr;
     const int l2_dma = a.N % 8 == 0;
-    const size_t lds = base + (EPI == kEpiLowRank ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
+    const size_t lds = base + (epi_lr(EPI) ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
     hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, a, tm, tn, l2_dma, tr);
     return hipGetLastError();
@@ -721,7 +749,11 @@ template <int ABITS, bool ASYM, bool KTAIL>
 hipError_t launch_epi(const LinearArgs &a, const TileRange &tr, hipStream_t st) {
     const unsigned grid = (unsigned)tr.count;
     if (a.y_i32) return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(a, tr, grid, st);
-    if (a.lr_t) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(a, tr, grid, st);
+    if (a.lr_t) {
+        if (a.lr_r <= 16) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(a, tr, grid, st);
+        if (a.lr_r <= 32) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(a, tr, grid, st);
+        return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(a, tr, grid, st);
+    }
     return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(a, tr, grid, st);
 }
 
