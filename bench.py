@@ -31,8 +31,10 @@ Workloads (sizes of FLUX / Z-Image style DiT blocks and text-encoder linears):
   small_m_w4a16      small_m shapes (symmetric codes) as W4A16                metric: weight GB/s
 The default run also times the small-M text-encoder linear at M = 1 and 16 (K = 12288) and
 reports them under "detail" (--no-small-m-detail skips that).
-  mfma_peak    the library's int8 MFMA rate probe (not a layer): the chip's sustained
+  mfma_peak    the int8 MFMA rate probe (libw4probe.so, not a layer): the chip's sustained
                dense int8 rate with random and with constant operands
+  hbm_peak     the streaming-read probe (libw4probe.so): the HBM read rate a plain kernel
+               reaches on 25 MB, the practical ceiling of the small-M kernels
 """
 import argparse
 import ctypes
@@ -64,7 +66,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="attn_proj",
                     choices=["attn_proj", "mlp_up", "mlp_down", "small_m", "double_block", "tiny", "mfma_peak",
-                             "attn_proj_grouped", "attn_proj_w4a16", "small_m_w4a16"])
+                             "attn_proj_grouped", "attn_proj_w4a16", "small_m_w4a16", "hbm_peak"])
+    ap.add_argument("--probe-mb", type=int, default=25, help="hbm_peak: buffer size in MB")
     ap.add_argument("--gw", type=int, default=128, help="grouped-scale workloads: inputs per weight scale")
     ap.add_argument("--lowrank", type=int, default=0, metavar="R",
                     help="single-linear workloads: add a rank-R low-rank branch (x . L1 computed once, untimed, "
@@ -321,6 +324,8 @@ def main():
         return bench_double_block(args, dev)
     if args.workload == "mfma_peak":
         return bench_mfma_peak(args, dev)
+    if args.workload == "hbm_peak":
+        return bench_hbm_peak(args, dev)
 
     layer_specs, cfg = build_workload(args, dev)
     if args.lowrank:
@@ -619,14 +624,77 @@ def measured_traffic(kernel, cfg):
     return ent["bytes"]
 
 
+def probe_library():
+    """libw4probe.so: the measurement probes (include/w4_probe.h), built beside libw4.so."""
+    path = os.path.join(ROOT, "int4_weight_quantized_block_amd", "libw4probe.so")
+    if not os.path.exists(path):
+        raise SystemExit("libw4probe.so is not built (%s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    lib.w4_probe_mfma_rate.restype = ctypes.c_int
+    lib.w4_probe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4_probe_read_rate.restype = ctypes.c_int
+    lib.w4_probe_read_rate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    return lib
+
+
+def bench_hbm_peak(args, dev):
+    """The HBM read rate a plain streaming kernel reaches on a buffer the size of one small-M
+    linear's weights (K = 12288 -> N = 4096: 25.2 MB), cycling through copies larger than the
+    256 MB Infinity Cache, for a few grid sizes: the practical ceiling the small-M kernels'
+    HBM fractions should be read against.  Not a step of the layer."""
+    import torch
+    P = probe_library()
+    nbytes = args.probe_mb * 1000 * 1000 // 16 * 16
+    ncopy = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(ncopy)]
+    st = torch.cuda.current_stream(dev)
+    best = None
+    rates = {}
+    for blocks in (256, 512, 1024, 2048, 4096):
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        for i in range(2):
+            assert P.w4_probe_read_rate(bufs[i % ncopy].data_ptr(), nbytes, blocks, sink.data_ptr(), st.cuda_stream) == 0
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            s2 = torch.cuda.current_stream().cuda_stream
+            for i in range(args.steps):
+                assert P.w4_probe_read_rate(bufs[i % ncopy].data_ptr(), nbytes, blocks, sink.data_ptr(), s2) == 0
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / args.steps * 1e-3
+        rates[blocks] = {"us": round(t * 1e6, 3), "gbs": round(nbytes / t / 1e9, 1)}
+        log("bench: read %d MB with %d workgroups: %.2f us, %.0f GB/s" % (nbytes // 1000000, blocks, t * 1e6,
+                                                                          nbytes / t / 1e9))
+        if best is None or t < best[1]:
+            best = (blocks, t)
+    gbs = nbytes / best[1] / 1e9
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "kernel": "k_read_rate", "traffic": None, "launch_us": round(best[1] * 1e6, 3)}
+    out = {
+        "metric": "plain streaming read rate (probe)", "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 2, "ms_per_step": round(best[1] * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": "hbm_peak", "bytes": nbytes, "copies": ncopy, "parallelism": "single-gpu"},
+        "roofline": roof, "cpu_baseline": None, "detail": {"by_workgroups": rates, "best_workgroups": best[0]},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_mfma_peak(args, dev):
     """The chip's sustained dense int8 MFMA rate: the library's probe (back-to-back
     v_mfma_i32_32x32x32_i8, eight waves per SIMD) with pseudo-random and with constant
     operands, K launches each between HIP events.  Not a step of the layer: it measures the
     ceiling the GEMM's roofline fraction should be read against."""
     import torch
-    import int4_weight_quantized_block_amd as w4
-    L = w4.load_library()
+    L = probe_library()
     blocks, iters = 256 * 8, 4000
     ops = blocks * 4.0 * iters * 4 * 2 * 32 ** 3
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
@@ -634,12 +702,12 @@ def bench_mfma_peak(args, dev):
     rate = {}
     for rnd in (0, 1):
         for _ in range(2):
-            w4._check(L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream))
+            assert L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream) == 0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(st)
         for _ in range(args.steps):
-            w4._check(L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream))
+            assert L.w4_probe_mfma_rate(blocks, iters, rnd, sink.data_ptr(), st.cuda_stream) == 0
         e1.record(st)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / args.steps * 1e-3

@@ -286,15 +286,6 @@ const char *w4_last_error(void);
 /* Library version string (static). */
 const char *w4_version(void);
 
-/* w4_probe_mfma_rate - a measurement probe, not a step of the layer (no passage defines it):
- * `blocks` workgroups of 4 waves, each wave running `iters` rounds of four independent
- * v_mfma_i32_32x32x32_i8 (the GEMM's shape) on register operands that are pseudo-random
- * (random_operands != 0) or constant; one int32 checksum per lane goes to sink
- * (blocks * 256 int32, 16-byte aligned).  Work: blocks * 4 * iters * 4 * 2 * 32^3 int ops.
- * Timing it (events around the launch on the caller's stream) gives the sustained dense int8
- * MFMA rate, with and without the datapath toggling that real operands cause.
- * Asynchronous; W4_ERR_INVALID_ARG for blocks or iters out of range or a NULL sink. */
-int w4_probe_mfma_rate(int64_t blocks, int iters, int random_operands, int32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -82,9 +82,6 @@ struct GroupedArgs {
 size_t grouped_workspace_bytes(int64_t M, int64_t N, int64_t K, int gw);
 hipError_t launch_gemm_grouped(const GroupedArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
 
-// Measurement probe: blocks workgroups of 4 waves, each wave iters rounds of 4 int8 MFMAs.
-hipError_t launch_mfma_rate(int64_t blocks, int iters, bool random_operands, int32_t *sink, hipStream_t st);
-
 hipError_t launch_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r,
                                float *t, hipStream_t st, int64_t ldt = 0);
 

@@ -1,10 +1,17 @@
-// Measurement probe, not part of the layer: the sustained dense int8 MFMA rate of the chip.
-// Each wave keeps four independent 32x32 int32 accumulators busy with back-to-back
-// v_mfma_i32_32x32x32_i8 (the shape the GEMM uses) on register operands that are either
-// pseudo-random or constant; random operands toggle more of the datapath and draw more
-// power, which is what real activation codes and weights do.
+// Measurement probes, not part of the layer (built as their own library, libw4probe.so,
+// declared in include/w4_probe.h):
+//  - the sustained dense int8 MFMA rate of the chip: each wave keeps four independent 32x32
+//    int32 accumulators busy with back-to-back v_mfma_i32_32x32x32_i8 (the shape the GEMM
+//    uses) on register operands that are either pseudo-random or constant; random operands
+//    toggle more of the datapath and draw more power, which is what real activation codes and
+//    weights do;
+//  - the HBM read rate a plain streaming kernel reaches on a buffer of a given size (the
+//    practical ceiling of the HBM-bound small-M kernels, which stream ~25 MB per launch).
+#include "w4_probe.h"
+
+#include <hip/hip_runtime.h>
+
 #include "common.h"
-#include "kernels.h"
 
 namespace w4 {
 
@@ -50,12 +57,50 @@ __global__ void __launch_bounds__(256) k_mfma_rate(int iters, int32_t *__restric
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-}  // namespace
-
-hipError_t launch_mfma_rate(int64_t blocks, int iters, bool random_operands, int32_t *sink, hipStream_t st) {
-    if (random_operands) hipLaunchKernelGGL(k_mfma_rate<true>, dim3((unsigned)blocks), dim3(256), 0, st, iters, sink);
-    else hipLaunchKernelGGL(k_mfma_rate<false>, dim3((unsigned)blocks), dim3(256), 0, st, iters, sink);
-    return hipGetLastError();
+// Every thread reads 16-byte chunks t, t + T, t + 2T, ... of the buffer (T = threads in the
+// grid, so each wave instruction reads 1 KB contiguous), 8 loads in flight per batch, and
+// writes the XOR of what it read (so the loads cannot be dropped).
+__global__ void __launch_bounds__(256) k_read_rate(const uint4 *__restrict__ src, int64_t chunks,
+                                                   int32_t *__restrict__ sink) {
+    const int64_t T = (int64_t)gridDim.x * 256;
+    int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    for (; c + 7 * T < chunks; c += 8 * T) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[c + u * T];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; c < chunks; c += T) {
+        const uint4 v = src[c];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = (int32_t)x;
 }
 
+}  // namespace
 }  // namespace w4
+
+extern "C" {
+
+int w4_probe_mfma_rate(int64_t blocks, int iters, int random_operands, int32_t *sink, void *stream) {
+    if (blocks < 1 || blocks > (int64_t)1 << 24 || iters < 1 || !sink || ((uintptr_t)sink & 15)) return 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (random_operands)
+        hipLaunchKernelGGL(w4::k_mfma_rate<true>, dim3((unsigned)blocks), dim3(256), 0, st, iters, sink);
+    else
+        hipLaunchKernelGGL(w4::k_mfma_rate<false>, dim3((unsigned)blocks), dim3(256), 0, st, iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int w4_probe_read_rate(const void *src, int64_t bytes, int64_t blocks, int32_t *sink, void *stream) {
+    if (!src || !sink || ((uintptr_t)src & 15) || ((uintptr_t)sink & 15) || bytes < 16 || bytes % 16 || blocks < 1 ||
+        blocks > (int64_t)1 << 20)
+        return 1;
+    hipLaunchKernelGGL(w4::k_read_rate, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4 *>(src), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+}  // extern "C"

@@ -236,15 +236,6 @@ int w4_lowrank_down(const void *x, const void *l1, int64_t M, int64_t K, int r, 
     return hip_status(w4::launch_lowrank_down(x, l1, M, K, r, t, static_cast<hipStream_t>(stream)), fn);
 }
 
-int w4_probe_mfma_rate(int64_t blocks, int iters, int random_operands, int32_t *sink, void *stream) {
-    const char *fn = "w4_probe_mfma_rate";
-    if (blocks < 1 || blocks > (int64_t)1 << 24 || iters < 1)
-        return fail(W4_ERR_INVALID_ARG, "%s: blocks=%lld iters=%d", fn, (long long)blocks, iters);
-    W4_CHECK_PTR(sink);
-    return hip_status(w4::launch_mfma_rate(blocks, iters, random_operands != 0, sink, static_cast<hipStream_t>(stream)),
-                      fn);
-}
-
 // xf: NULL, or bf16 X for the fused small-M kernel (rotation and quantization inside the GEMM
 // launch; q, tok_scale and tok_rowsum are then not read).
 static int linear_impl(const char *fn, const void *q, const float *tok_scale, const int32_t *tok_rowsum,

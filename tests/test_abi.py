@@ -205,10 +205,28 @@ def test_grouped_validation(lib):
     assert cg(M=0) == w4.W4_OK
 
 
-def test_probe_validation(lib):
-    assert lib.w4_probe_mfma_rate(0, 10, 1, A, None) == w4.W4_ERR_INVALID_ARG
-    assert lib.w4_probe_mfma_rate(8, 0, 1, A, None) == w4.W4_ERR_INVALID_ARG
-    assert lib.w4_probe_mfma_rate(8, 10, 1, None, None) == w4.W4_ERR_INVALID_ARG
+def test_probe_library_is_separate_and_validates():
+    """The measurement probes live in libw4probe.so (include/w4_probe.h), not in the layer's
+    library; invalid arguments return 1 before anything is launched."""
+    probe_h = os.path.join(ROOT, "include", "w4_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(probe_h).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(w4_probe_\w+)\s*\(", text)))
+    assert names == ["w4_probe_mfma_rate", "w4_probe_read_rate"]
+    main = w4.load_library()
+    assert not any(hasattr(main, n) for n in names)
+    path = os.path.join(os.path.dirname(w4.library_path()), "libw4probe.so")
+    if not os.path.exists(path):
+        from int4_weight_quantized_block_amd import build
+        build.build()
+    P = ctypes.CDLL(path)
+    P.w4_probe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.w4_probe_read_rate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.w4_probe_mfma_rate(0, 10, 1, A, None) == 1
+    assert P.w4_probe_mfma_rate(8, 0, 1, A, None) == 1
+    assert P.w4_probe_mfma_rate(8, 10, 1, None, None) == 1
+    assert P.w4_probe_read_rate(A, 100, 8, A, None) == 1        # not a multiple of 16
+    assert P.w4_probe_read_rate(U, 1024, 8, A, None) == 1
+    assert P.w4_probe_read_rate(A, 1024, 0, A, None) == 1
 
 
 def test_error_message_is_per_thread(lib):
