@@ -22,8 +22,8 @@
 // natural (int8 x int8, bf16) or even/odd on both sides (int4 x int4).
 //
 // Tiles.  4 waves, WM x WN of them, each FM x FN blocks of 32 x 32.  Large M: 2 x 2 waves of
-// 2 x 2 blocks (128 x 128 tile), a 3-deep LDS ring of 64-k stages.  Small M (<= 64): 1 x 4
-// waves of FM x 1 blocks (32 or 64 tokens x 128 features), a deeper ring, and K split over
+// 2 x 2 blocks (128 x 128 tile), an LDS ring of 64-k stages.  Small M (<= 64): 1 x 4
+// waves of FM x 1 blocks (32 or 64 tokens x 128 features), and K split over
 // several workgroups whose partial sums (fp32, or int32 for the raw output) go to the
 // caller's workspace and are added in a fixed order by k_grp_reduce, which applies the
 // epilogue.  Each stage (activations, weights, and the stage's weight scales, one dword per
@@ -443,24 +443,27 @@ hipError_t launch_cfg(const GrpArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// K ranges for a small-M grid: about two workgroups per compute unit, each range a whole
-// number of stages and of groups.
+// K ranges for a small-M grid: about three workgroups per compute unit, each range a whole
+// number of stages and of groups and at least 4 stages long.
 int plan_s(int64_t M, int64_t N, int64_t K, int gw) {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t tiles = (N + 127) / 128;
     int S = 1;
-    while (S < 16 && tiles * S * 2 <= 2 * ncu && K % (2 * S * std::max(gw, BK)) == 0 && K / (2 * S) >= 4 * BK)
+    while (S < 32 && tiles * S < 3 * ncu && K % (2 * S * std::max(gw, BK)) == 0 && K / (2 * S) >= 4 * BK)
         S *= 2;
     return S;
 }
 
+// Ring depths (measured at 4096 x 3072 x 3072 and at 1 and 16 tokens x 4096 -> 12288): large
+// M, 6 stages for integer activations and 3 for bf16 (whose stages are twice as large; deeper
+// rings cost occupancy); small M, 4 stages with K split over about three workgroups per CU.
 template <int AT, int EPI>
 hipError_t launch_at(const GrpArgs &a, hipStream_t st) {
-    if (a.M > 64) return launch_cfg<AT, 2, 2, 2, 2, 3, EPI>(a, st);
-    if (a.M > 32) return launch_cfg<AT, 2, 1, 1, 4, 6, EPI>(a, st);
-    return launch_cfg<AT, 1, 1, 1, 4, 6, EPI>(a, st);
+    if (a.M > 64) return AT == 16 ? launch_cfg<AT, 2, 2, 2, 2, 3, EPI>(a, st) : launch_cfg<AT, 2, 2, 2, 2, 6, EPI>(a, st);
+    if (a.M > 32) return launch_cfg<AT, 2, 1, 1, 4, 4, EPI>(a, st);
+    return launch_cfg<AT, 1, 1, 1, 4, 4, EPI>(a, st);
 }
 
 template <int AT, bool I32>
