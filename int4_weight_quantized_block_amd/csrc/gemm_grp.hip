@@ -466,10 +466,387 @@ hipError_t launch_at(const GrpArgs &a, hipStream_t st) {
     return launch_cfg<AT, 1, 1, 1, 4, 4, EPI>(a, st);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Streaming form for M <= 16 (the HBM-bound regime): no workgroup barrier in the main loop and
+// no K split.  A workgroup of NW waves owns R = 16 RB weight rows; in each stage of 256 NW k,
+// wave w takes k in [256 w, 256 w + 256) and streams, through its own LDS ring of D stages,
+// its slice of every staged token, its 128-byte piece of each of the R rows and those rows'
+// scales of the groups in its slice (direct global -> LDS loads), multiplying a stage as soon
+// as its own loads have landed.  Output layout of the 16 x 16 MFMA: lane l, register r holds
+// weight row 4 (l / 16) + r of token l % 16.  The k order inside an MFMA is chosen so that each
+// MFMA covers whole groups: integer activations, v_mfma_i32_16x16x64_i8 over 64 consecutive k
+// (lane group kb the 16 k at 16 kb); bf16 activations, v_mfma_f32_16x16x32_bf16 over 32
+// consecutive k (lane group kb the 8 k at 8 kb).  After each group the lane's four int32 (or
+// fp32) sums are scaled by their rows' group scales into fp32 running sums; the waves' sums
+// are added through LDS in a fixed order at the end.
+constexpr int kGsDepth = 2;  // stages in flight per wave
+
+template <int AT, int TM, int RB, int NW, int GW>
+struct GSL {
+    static constexpr int KS = 256 * NW;                                  // k per stage
+    static constexpr int R = 16 * RB;
+    static constexpr int TB = AT == 8 ? 256 : AT == 4 ? 128 : 512;       // token bytes per wave and stage
+    static constexpr int CPT = TB / 16;                                  // 16-byte chunks per token slice
+    static constexpr int ACT = TM * TB < 1024 ? 1024 : TM * TB;          // whole 1 KB loads
+    static constexpr int WB = R * 128;                                   // weight bytes per wave and stage
+    static constexpr int SB = 512 / GW;                                  // scale bytes per row and wave-stage
+    static constexpr int SCL = GW == 256 ? 1 : (R * SB / 4 + 63) / 64;   // scale loads (dwords per lane)
+    static constexpr int SCB = SCL * 256;
+    static constexpr int SLOT = ACT + WB + SCB;
+    static constexpr int D = kGsDepth;
+    static constexpr int LA = ACT / 1024, LB = WB / 1024;
+    static constexpr int LPS = LA + LB + SCL;                            // loads per stage
+    static constexpr int RED = NW * RB * 1024;                           // fp32 tiles of the waves
+    static constexpr int RING = NW * D * SLOT > RED ? NW * D * SLOT : RED;
+    static constexpr int C_SX = RING, C_BIAS = C_SX + 256;
+    static constexpr int LDS = C_BIAS + 256;
+    static constexpr int NG = 256 / GW;                                  // groups per wave-stage
+    static_assert(R <= 64 && (D - 1) * LPS <= 63 && LDS <= 160 * 1024, "grouped streaming layout");
+};
+
+template <int AT, int TM, int RB, int NW, int GW, bool I32>
+__global__ void __launch_bounds__(64 * NW) k_grp_stream(GrpArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using L = GSL<AT, TM, RB, NW, GW>;
+    constexpr int R = L::R;
+    constexpr uint32_t ASTEP = L::KS * (AT == 16 ? 2 : AT == 8 ? 1 : 0) + (AT == 4 ? L::KS / 2 : 0);
+    constexpr uint32_t BSTEP = L::KS / 2;
+    constexpr bool INT = AT != 16;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * R;
+    const int64_t K = p.K, M = p.M;
+    const int nst = (int)(K / L::KS);
+    const int64_t rowA = (K * AT) / 8;
+    const int64_t rowB = K / 2;
+    const int64_t ng = K / GW;  // scale groups per row
+    const uint32_t smem_base = lds_addr(smem);
+    const int ring = wave * L::D * L::SLOT;
+
+    // per-lane load offsets at stage 0: LDS position (t, c) of a token slice holds global
+    // chunk c ^ (t & (CPT - 1)); position (r, c) of a weight row holds chunk c ^ (r & 7)
+    uint32_t arow[L::LA], ain[L::LA], brow[L::LB], bin[L::LB], srow[L::SCL], sin_[L::SCL];
+#pragma unroll
+    for (int j = 0; j < L::LA; ++j) {
+        const int f = min(j * 64 + lane, TM * L::CPT - 1);
+        const int t = f / L::CPT, c = f % L::CPT;
+        arow[j] = (uint32_t)(min<int64_t>(t, M - 1) * rowA);
+        ain[j] = (uint32_t)(wave * L::TB + 16 * (c ^ (t & (L::CPT - 1))));
+    }
+#pragma unroll
+    for (int j = 0; j < L::LB; ++j) {
+        const int r = 8 * j + lane / 8;
+        brow[j] = (uint32_t)((min<int64_t>(n0 + r, p.N - 1) - n0) * rowB);
+        bin[j] = (uint32_t)(128 * wave + 16 * ((lane & 7) ^ (r & 7)));
+    }
+    // scales: GW = 256, one fp16 per row (lane = row); GW = 128, one dword (two groups) per
+    // row; GW = 64, two dwords per row (lane = 2 row + half)
+#pragma unroll
+    for (int j = 0; j < L::SCL; ++j) {
+        const int f = j * 64 + lane;
+        const int r = GW == 64 ? min(f / 2, R - 1) : min(f, R - 1);
+        const int h = GW == 64 ? f % 2 : 0;
+        srow[j] = (uint32_t)((min<int64_t>(n0 + r, p.N - 1) - n0) * ng * 2);
+        sin_[j] = (uint32_t)(((int64_t)256 * wave / GW) * 2 + 4 * h);
+    }
+    const uint64_t abase = (uint64_t)p.A;
+    const uint64_t bbase = (uint64_t)(p.B + n0 * rowB);
+    const uint64_t sbase = (uint64_t)(p.gs + n0 * ng);
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const uint32_t slot = smem_base + (uint32_t)(ring + (i % L::D) * L::SLOT);
+#pragma unroll
+        for (int j = 0; j < L::LA; ++j) gl_lds16_so(abase, arow[j] + ain[j] + (uint32_t)i * ASTEP, slot + 1024 * j);
+#pragma unroll
+        for (int j = 0; j < L::LB; ++j) gl_lds16_so(bbase, brow[j] + bin[j] + (uint32_t)i * BSTEP, slot + L::ACT + 1024 * j);
+        const uint32_t soff = (uint32_t)i * (uint32_t)(L::KS / GW * 2);
+#pragma unroll
+        for (int j = 0; j < L::SCL; ++j) {
+            if constexpr (GW == 256) gl_lds2_so(sbase, srow[j] + sin_[j] + soff, slot + L::ACT + L::WB + 256 * j);
+            else gl_lds4_so(sbase, srow[j] + sin_[j] + soff, slot + L::ACT + L::WB + 256 * j);
+        }
+    };
+
+    // constants first (wave 0): token scales and biases, one dword each (oldest loads, so the
+    // stage waits below need not count them)
+    if (wave == 0) {
+        const uint32_t t = (uint32_t)min<int64_t>(lane, M - 1);
+        if (INT) gl_lds4_so((uint64_t)p.sx, 4 * t, smem_base + L::C_SX);
+        const uint32_t c = (uint32_t)(min<int64_t>(n0 + min(lane, R - 1), p.N - 1) - n0);
+        if (p.bias && p.bias_bf16) gl_lds2_so((uint64_t)((const uint16_t *)p.bias + n0), 2 * c, smem_base + L::C_BIAS);
+        else if (p.bias) gl_lds4_so((uint64_t)((const float *)p.bias + n0), 4 * c, smem_base + L::C_BIAS);
+    }
+    for (int i = 0; i < L::D; ++i)
+        if (i < nst) issue(i);
+
+    typedef typename std::conditional<INT, v4i, v4f>::type Acc;
+    Acc acc[RB];
+    v4f accf[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = Acc{0, 0, 0, 0};
+        accf[rb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int tt = min(lr, (int)M - 1);
+
+    // The stage's scales of the lane's rows 16 rb + 4 kb + 0..3, read from the slot into
+    // registers with the operands (the slot is refilled before the MFMAs): per row one dword
+    // (GW = 256: the group's fp16 zero-extended; GW = 128: the two groups) or two (GW = 64).
+    constexpr int SCW = GW == 64 ? 2 : 1;
+    uint4 scv[RB][SCW];
+    auto read_scales = [&](const uint8_t *sc) __attribute__((always_inline)) {
+        if constexpr (!I32) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r0 = 16 * rb + 4 * kb;
+#pragma unroll
+                for (int h = 0; h < SCW; ++h) scv[rb][h] = *reinterpret_cast<const uint4 *>(sc + 4 * SCW * r0 + 16 * h);
+            }
+        }
+    };
+    // scale group g (0 .. NG - 1) into the running sums
+    auto flush = [&](int g) __attribute__((always_inline)) {
+        if constexpr (!I32) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                uint32_t w[4];
+                if constexpr (GW == 64) {
+                    const uint32_t d[8] = {scv[rb][0].x, scv[rb][0].y, scv[rb][0].z, scv[rb][0].w,
+                                           scv[rb][1].x, scv[rb][1].y, scv[rb][1].z, scv[rb][1].w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = d[2 * r + g / 2] >> (16 * (g & 1));
+                } else {
+                    const uint32_t d[4] = {scv[rb][0].x, scv[rb][0].y, scv[rb][0].z, scv[rb][0].w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w[r] = d[r] >> (16 * g);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = __half2float(__ushort_as_half((uint16_t)w[r]));
+                    accf[rb][r] = fmaf((float)acc[rb][r], sv, accf[rb][r]);
+                    acc[rb][r] = 0;
+                }
+            }
+        }
+    };
+
+    for (int i = 0; i < nst; ++i) {
+        wait_rem<L::LPS, L::D - 1>(min(L::D - 1, nst - 1 - i));
+        const uint8_t *sl = smem + ring + (i % L::D) * L::SLOT;
+        const uint8_t *ws_ = sl + L::ACT;
+        const uint8_t *sc = sl + L::ACT + L::WB;
+        const uint8_t *ta = sl + tt * L::TB;
+        if constexpr (INT) {
+            // two 64-k MFMAs per 128-k half u; 16 k per lane group
+            uint4 xa[4];
+            uint2 wv[4][RB];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // q = 2 u + h: k in [64 q, 64 q + 64)
+                if constexpr (AT == 8) {
+                    const int g = 4 * q + kb;  // global chunk of the token slice
+                    xa[q] = *reinterpret_cast<const uint4 *>(ta + 16 * (g ^ (tt & (L::CPT - 1))));
+                } else {
+                    const int g = 2 * q + (kb >> 1);
+                    const uint2 x2 = *reinterpret_cast<const uint2 *>(ta + 16 * (g ^ (tt & (L::CPT - 1))) + 8 * (kb & 1));
+                    xa[q] = make_uint4(x2.x, x2.y, 0, 0);
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int r = 16 * rb + lr;
+                    const int g = 2 * q + (kb >> 1);
+                    wv[q][rb] = *reinterpret_cast<const uint2 *>(ws_ + r * 128 + 16 * (g ^ (r & 7)) + 8 * (kb & 1));
+                }
+            }
+            read_scales(sc);
+            wait_lgkmcnt0();
+            if (i + L::D < nst) issue(i + L::D);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                v4i a;
+                if constexpr (AT == 8) a = __builtin_bit_cast(v4i, xa[q]);
+                else a = evod(xa[q].x, xa[q].y);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    v4i w;
+                    if constexpr (AT == 8) {
+                        uint32_t lo0, hi0, lo1, hi1;
+                        unpack_nat(wv[q][rb].x, lo0, hi0);
+                        unpack_nat(wv[q][rb].y, lo1, hi1);
+                        w = v4i{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+                    } else {
+                        w = evod(wv[q][rb].x, wv[q][rb].y);
+                    }
+                    acc[rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w, a, acc[rb], 0, 0, 0);
+                }
+                if constexpr (GW == 64) flush(q);
+                else if constexpr (GW == 128) {
+                    if (q & 1) flush(q >> 1);
+                }
+            }
+            if constexpr (GW == 256) flush(0);
+        } else {
+            // four 32-k MFMAs per 128-k half u; 8 k per lane group
+            bf8 xa[8];
+            uint32_t wv[8][RB];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {  // k in [32 q, 32 q + 32)
+                const int g = 4 * q + kb;
+                xa[q] = *reinterpret_cast<const bf8 *>(ta + 16 * (g ^ (tt & (L::CPT - 1))));
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int r = 16 * rb + lr;
+                    wv[q][rb] = *reinterpret_cast<const uint32_t *>(ws_ + r * 128 + 16 * (q ^ (r & 7)) + 4 * kb);
+                }
+            }
+            read_scales(sc);
+            wait_lgkmcnt0();
+            if (i + L::D < nst) issue(i + L::D);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16_codes(wv[q][rb]), xa[q], acc[rb], 0, 0, 0);
+                if constexpr (GW == 64) {
+                    if (q & 1) flush(q >> 1);
+                } else if constexpr (GW == 128) {
+                    if ((q & 3) == 3) flush(q >> 2);
+                }
+            }
+            if constexpr (GW == 256) flush(0);
+        }
+    }
+
+    // ---- reduction of the NW waves' tiles in a fixed order, then the epilogue
+    wait_vmcnt<0>();
+    __syncthreads();
+    v4f *red = reinterpret_cast<v4f *>(smem);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        v4f v;
+        if constexpr (I32) v = __builtin_bit_cast(v4f, acc[rb]);
+        else v = accf[rb];
+        red[(wave * RB + rb) * 64 + lane] = v;
+    }
+    __syncthreads();
+    constexpr float UNSCALE = AT == 4 ? 1.0f / 256 : 1.0f / 16;
+    constexpr int SHIFT = AT == 4 ? 8 : 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        if (rb % NW != wave) continue;
+        const int64_t m = lr;
+        if (m >= M) continue;
+        const int rl = 16 * rb + 4 * kb;
+        const int64_t nb = n0 + rl;
+        if constexpr (I32) {
+            v4i t = __builtin_bit_cast(v4i, red[rb * 64 + lane]);
+#pragma unroll
+            for (int q = 1; q < NW; ++q) t += __builtin_bit_cast(v4i, red[(q * RB + rb) * 64 + lane]);
+            int32_t *Y = reinterpret_cast<int32_t *>(p.Y) + m * p.N;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) Y[nb + r] = t[r] >> SHIFT;
+        } else {
+            v4f t = red[rb * 64 + lane];
+#pragma unroll
+            for (int q = 1; q < NW; ++q) t += red[(q * RB + rb) * 64 + lane];
+            const float xs = INT ? *reinterpret_cast<const float *>(smem + L::C_SX + 4 * m) * UNSCALE : UNSCALE;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = t[r] * xs;
+            if (p.lr_t) {
+                const float *tr = p.lr_t + m * p.lr_ldt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t nc = min<int64_t>(nb + r, p.N - 1);
+                    float l = y[r];
+                    for (int q = 0; q < p.lr_r; ++q) l = fmaf(tr[q], bf16_to_f32(p.lr_l2[(int64_t)q * p.N + nc]), l);
+                    y[r] = l;
+                }
+            }
+            if (p.bias) {
+                const uint4 b4 = *reinterpret_cast<const uint4 *>(smem + L::C_BIAS + 4 * rl);
+                const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] += __uint_as_float(p.bias_bf16 ? bw[r] << 16 : bw[r]);
+            }
+            uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y) + m * p.N;
+            if (nb + 3 < p.N && (p.N & 3) == 0) {
+                *reinterpret_cast<uint2 *>(Y + nb) =
+                    make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16), f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < p.N) Y[nb + r] = (uint16_t)f32_to_bf16(y[r]);
+            }
+        }
+    }
+}
+
+template <int AT, int TM, int RB, int NW, int GW, bool I32>
+hipError_t launch_gs_k(const GrpArgs &a, hipStream_t st) {
+    using L = GSL<AT, TM, RB, NW, GW>;
+    auto kern = k_grp_stream<AT, TM, RB, NW, GW, I32>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
+    if (attr != hipSuccess) return attr;
+    const unsigned grid = (unsigned)((a.N + L::R - 1) / L::R);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), L::LDS, st, a);
+    return hipGetLastError();
+}
+
+int num_cus() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    return ncu;
+}
+
+// Waves per workgroup of the grouped streaming launch: 8 (two per SIMD) when 16-row
+// workgroups give about one per CU and K holds whole 2048-k stages, else 4 (K % 1024 == 0).
+int gs_waves(int64_t M, int64_t N, int64_t K) {
+    if (M <= 8 && (N + 15) / 16 <= num_cus() && K % 2048 == 0) return 8;
+    return K % 1024 == 0 ? 4 : 0;
+}
+
+template <int AT, int TM, int GW, bool I32>
+hipError_t gs_shape(const GrpArgs &a, hipStream_t st) {
+    if constexpr (TM <= 8) {
+        if (gs_waves(a.M, a.N, a.K) == 8) return launch_gs_k<AT, TM, 1, 8, GW, I32>(a, st);
+        return launch_gs_k<AT, TM, 1, 4, GW, I32>(a, st);
+    } else {
+        const int64_t rb = (a.N + 16 * 256 - 1) / (16 * 256);
+        if (rb <= 1) return launch_gs_k<AT, TM, 1, 4, GW, I32>(a, st);
+        if (rb <= 2) return launch_gs_k<AT, TM, 2, 4, GW, I32>(a, st);
+        if (rb <= 3) return launch_gs_k<AT, TM, 3, 4, GW, I32>(a, st);
+        return launch_gs_k<AT, TM, 4, 4, GW, I32>(a, st);
+    }
+}
+
+template <int AT, int GW, bool I32>
+hipError_t gs_tm(const GrpArgs &a, hipStream_t st) {
+    if (a.M <= 1) return gs_shape<AT, 1, GW, I32>(a, st);
+    if (a.M <= 2) return gs_shape<AT, 2, GW, I32>(a, st);
+    if (a.M <= 4) return gs_shape<AT, 4, GW, I32>(a, st);
+    if (a.M <= 8) return gs_shape<AT, 8, GW, I32>(a, st);
+    return gs_shape<AT, 16, GW, I32>(a, st);
+}
+
+// The streaming form takes M <= 16, gw >= 64 and K a whole number of 1024-k stages.
+bool gs_ok(const GrpArgs &a) { return a.M <= 16 && a.gw >= 64 && gs_waves(a.M, a.N, a.K) != 0; }
+
+template <int AT, bool I32>
+hipError_t launch_gs(const GrpArgs &a, hipStream_t st) {
+    switch (a.gw) {
+        case 64: return gs_tm<AT, 64, I32>(a, st);
+        case 128: return gs_tm<AT, 128, I32>(a, st);
+        default: return gs_tm<AT, 256, I32>(a, st);
+    }
+}
+
 template <int AT, bool I32>
 hipError_t launch_grp(GrpArgs a, void *ws, size_t ws_bytes, hipStream_t st) {
     a.S = 1;
     a.part = nullptr;
+    if (gs_ok(a)) return launch_gs<AT, I32>(a, st);
     if (a.M <= 64) {
         const int S = plan_s(a.M, a.N, a.K, a.gw);
         const size_t need = (size_t)S * a.M * a.N * 4;

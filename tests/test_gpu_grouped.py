@@ -155,6 +155,10 @@ def grouped_case(M, N, K, g, gw, bits, seed, lr_rank=0, bias_dtype=torch.bfloat1
     (8, 4096, 12288, 256, 256, 8, True),      # few tokens, K split
     (1, 3000, 4096, 16, 64, 4, False),        # one token
     (20, 2048, 3072, 256, 32, 4, True),
+    (16, 3000, 8192, 256, 64, 8, True),       # streaming form: 16 tokens, ragged N, low-rank
+    (5, 1000, 3072, 64, 128, 4, False),       # streaming form, 4 waves (K not whole 2048-k stages)
+    (2, 12288, 12288, 256, 128, 8, True),     # streaming form, N past 16 rows per CU
+    (16, 16384, 4096, 256, 256, 4, False),    # streaming form, 64 rows per workgroup
 ])
 def test_linear_grouped_int_matches_oracle(M, N, K, g, gw, bits, lr):
     """W4A8 / W4A4 with grouped fp16 weight scales: the raw integer sums on the oracle's codes
@@ -190,6 +194,9 @@ def test_linear_grouped_int_matches_oracle(M, N, K, g, gw, bits, lr):
     (16, 4096, 4096, 256, False, None),
     (1, 12288, 4096, 128, False, torch.bfloat16),
     (33, 777, 12288, 64, True, torch.bfloat16),
+    (3, 1000, 2048, 64, True, torch.float32),     # streaming form, gw = 64, low-rank
+    (16, 12288, 3072, 64, False, torch.bfloat16),  # streaming form, 48 rows per workgroup
+    (9, 520, 1024, 256, True, None),              # streaming form, one stage
 ])
 def test_linear_w4a16_matches_oracle(M, N, K, gw, lr, bias_dtype):
     """W4A16 (no rotation): bf16 activations times the grouped int4 weights on the bf16 matrix
@@ -211,9 +218,9 @@ def test_linear_w4a16_matches_oracle(M, N, K, gw, lr, bias_dtype):
 
 
 def test_grouped_ksplit_equals_single_pass():
-    """A few tokens with and without the workspace that splits K: integer sums identical, bf16
-    outputs within the bar of each other (the fp32 group sums are added in another order)."""
-    M, N, K, gw = 12, 2048, 8192, 128
+    """17 to 64 tokens with and without the workspace that splits K: integer sums identical,
+    bf16 outputs within the bar of each other (the fp32 group sums are added in another order)."""
+    M, N, K, gw = 24, 2048, 8192, 128
     say("grouped split M=%d N=%d K=%d gw=%d" % (M, N, K, gw))
     need = w4.w4_grouped_workspace_bytes(M, N, K, 8, gw)
     assert need > 0
