@@ -233,7 +233,8 @@ def cpu_baseline(layer, rows_wanted):
 COPY_BYTES = 512 << 20
 # kernel-name prefix -> (short name, source file)
 KERNEL_SOURCE = {"k_gemm<": ("k_gemm", "gemm.hip"), "k_gemv": ("k_gemv", "gemv.hip"),
-                 "k_rotquant": ("k_rotquant", "rotquant.hip"), "k_gemm_grp": ("k_gemm_grp", "gemm_grp.hip")}
+                 "k_rotquant": ("k_rotquant", "rotquant.hip"), "k_gemm_grp": ("k_gemm_grp", "gemm_grp.hip"),
+                 "k_grp_stream": ("k_grp_stream", "gemm_grp.hip")}
 
 
 def copy_calibration(dev):
@@ -251,7 +252,7 @@ def copy_calibration(dev):
 
 def traffic_workload(workload, M, K):
     """Key of a workload in profiles/traffic.json (small-M entries carry their shape)."""
-    return "small_m_M%d_K%d" % (M, K) if workload == "small_m" else workload
+    return "%s_M%d_K%d" % (workload, M, K) if workload in ("small_m", "small_m_w4a16") else workload
 
 
 def ingest_counters(fetch_dir, write_dir, workload):
@@ -455,7 +456,7 @@ def time_layer(args, dev, spec):
                      Y.data_ptr(), w4.W4_OUT_BF16, wsg.data_ptr(), wsg.numel(), sptr) for x, (p, s, _) in zip(Xs, Ps)]
         f_lin = L.w4_linear_grouped
         fused = False
-        kernel = "k_gemm_grp"
+        kernel = "k_grp_stream" if M <= 16 and gw >= 64 and K % 1024 == 0 else "k_gemm_grp"
     else:
         lrp = None
         if getattr(args, "lowrank", 0):
@@ -614,7 +615,8 @@ def measured_traffic(kernel, cfg):
         data = json.load(open(path))
     except ValueError:
         return None
-    key = "%s:%s" % (kernel, traffic_workload(cfg["workload"], cfg.get("M"), cfg.get("K")))
+    short = "k_gemv" if kernel.startswith("k_gemv") else kernel  # counters are kept per source file
+    key = "%s:%s" % (short, traffic_workload(cfg["workload"], cfg.get("M"), cfg.get("K")))
     ent = data.get(key)
     if not ent:
         return None

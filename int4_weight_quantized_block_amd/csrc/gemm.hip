@@ -230,9 +230,11 @@ struct TileRange {
 };
 
 // Tile id -> (tile row, tile column): ids walk M within groups of GN column tiles, so the
-// workgroups that share A and B panels run close together.
+// workgroups that share A and B panels run close together.  GN = 8: an XCD's 32 tiles of a
+// round then cover 4 row panels x 8 column panels (at 4096 tokens x 3072 features, 3.1 MB of
+// int8 codes + 2.4 MB of packed weights, the least of the 32-tile rectangles).
 __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int &tm, int &tn) {
-    constexpr int GN = 4;
+    constexpr int GN = 8;
     const int gsize = GN * tiles_m;
     const int grp = tile / gsize;
     const int first_n = grp * GN;

@@ -173,14 +173,25 @@ __global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int ti
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
-    // tile and K range: XCD x (blocks dealt round-robin) takes a contiguous run of tiles,
-    // walking M inside each column of tiles so the weight panel stays in its L2
+    // tile and K range: the blocks are dealt to the 8 XCDs round-robin; XCD x takes one of
+    // 4 x 2 rectangular regions of the tile grid (when the grid divides so), walking M inside
+    // each column of its region, so the A and B panels it streams are a quarter of M and half
+    // of N; otherwise a contiguous run of column-major tiles
     const int ntiles = tiles_m * tiles_n;
     int b = (int)blockIdx.x;
     const int kp = b / ntiles;
     b -= kp * ntiles;
-    if (ntiles % 8 == 0) b = (b % 8) * (ntiles / 8) + b / 8;
-    const int tm = b % tiles_m, tn = b / tiles_m;
+    int tm, tn;
+    if (tiles_m % 4 == 0 && tiles_n % 2 == 0) {
+        const int x = b % 8, j = b / 8;                    // XCD, index inside its region
+        const int rm = tiles_m / 4, rn = tiles_n / 2;      // region size
+        tm = (x % 4) * rm + j % rm;
+        tn = (x / 4) * rn + j / rm;
+    } else {
+        if (ntiles % 8 == 0) b = (b % 8) * (ntiles / 8) + b / 8;
+        tm = b % tiles_m;
+        tn = b / tiles_m;
+    }
     const int64_t m0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t KS = p.K / p.S;
     const int64_t kbeg = kp * KS;
