@@ -469,9 +469,12 @@ def time_layer(args, dev, spec):
             lr_keep = (t_lr, l2_lr, lr_c)
             lrp = ctypes.byref(lr_c)
         rq_args = [(x.data_ptr(), xdt, M, K, g, bits, qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), sptr) for x in Xs]
+        # the GEMM half with the workspace w4_linear gives it (K-split partials where planned),
+        # so the per-launch time is that of the step's kernels
+        wsm = torch.zeros((max(256, w4.w4_workspace_bytes(M, N, K, bits, 0)),), dtype=torch.uint8, device=dev)
         mm_args = [(qbuf.data_ptr(), sx.data_ptr(), rs.data_ptr(), bits, p.data_ptr(), s.data_ptr(),
                     z.data_ptr() if z is not None else None, bptr, w4.W4_BF16, lrp, M, N, K,
-                    Y.data_ptr(), w4.W4_OUT_BF16, None, 0, sptr) for p, s, z in Ps]
+                    Y.data_ptr(), w4.W4_OUT_BF16, wsm.data_ptr(), wsm.numel(), sptr) for p, s, z in Ps]
         # the step: the whole layer through w4_linear (rotate + quantize into its workspace, then
         # the GEMM; one fused launch for a single token, see w4_linear_fused)
         wsl = torch.empty((max(256, w4.w4_linear_workspace_bytes(M, N, K, bits)),), dtype=torch.uint8, device=dev)

@@ -625,12 +625,48 @@ __global__ void __launch_bounds__(256) k_gemv_reduce(LinearArgs p, int S, const 
     const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (id >= p.M * nq) return;
     const int64_t m = id / nq, nb = (id % nq) * 4;
+    const bool vec = (p.N & 3) == 0;  // 16-byte rows: whole quads of partials and constants
     int a[4] = {0, 0, 0, 0};
-    for (int s = 0; s < S; ++s) {
-        const int32_t *P = part + ((int64_t)s * p.M + m) * p.N;
+    float swv[4], bsv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int zv[4] = {8, 8, 8, 8};
+    if (vec) {
+        for (int s = 0; s < S; ++s) {
+            const int4 v = *reinterpret_cast<const int4 *>(part + ((int64_t)s * p.M + m) * p.N + nb);
+            a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
+        }
+        const float4 w4v = *reinterpret_cast<const float4 *>(p.sw + nb);
+        swv[0] = w4v.x; swv[1] = w4v.y; swv[2] = w4v.z; swv[3] = w4v.w;
+        if (p.bias) {
+            if (p.bias_bf16) {
+                const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(p.bias) + nb);
+                bsv[0] = __uint_as_float(b.x << 16); bsv[1] = __uint_as_float(b.x & 0xffff0000u);
+                bsv[2] = __uint_as_float(b.y << 16); bsv[3] = __uint_as_float(b.y & 0xffff0000u);
+            } else {
+                const float4 b = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(p.bias) + nb);
+                bsv[0] = b.x; bsv[1] = b.y; bsv[2] = b.z; bsv[3] = b.w;
+            }
+        }
+        if (asym) {
+            const uint32_t z = *reinterpret_cast<const uint32_t *>(p.zp + nb);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (nb + r < p.N) a[r] += P[nb + r];
+            for (int r = 0; r < 4; ++r) zv[r] = (int)((z >> (8 * r)) & 0xffu);
+        }
+    } else {
+        for (int s = 0; s < S; ++s) {
+            const int32_t *P = part + ((int64_t)s * p.M + m) * p.N;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) a[r] += P[nb + r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = min<int64_t>(nb + r, p.N - 1);
+            swv[r] = p.sw[n];
+            if (p.bias)
+                bsv[r] = p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
+                                     : reinterpret_cast<const float *>(p.bias)[n];
+            if (asym) zv[r] = p.zp[n];
+        }
     }
     const float sxm = p.sx[m];
     const int rsm = asym ? p.rowsum[m] : 0;
@@ -640,12 +676,9 @@ __global__ void __launch_bounds__(256) k_gemv_reduce(LinearArgs p, int S, const 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t n = min<int64_t>(nb + r, p.N - 1);
-        int v = a[r] + (asym ? ((8 - (int)p.zp[n]) << SHIFT) * rsm : 0);
+        int v = a[r] + (asym ? ((8 - zv[r]) << SHIFT) * rsm : 0);
         yi[r] = v >> SHIFT;
-        const float bs = !p.bias ? 0.0f
-                                 : p.bias_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[n])
-                                               : reinterpret_cast<const float *>(p.bias)[n];
-        y[r] = fmaf((float)v, sxm * (p.sw[n] * kUnscale), bs);
+        y[r] = fmaf((float)v, sxm * (swv[r] * kUnscale), bsv[r]);
         if (p.lr_t) {
             const float *tr = p.lr_t + m * p.lr_ldt;
             float l = 0.0f;
@@ -710,6 +743,242 @@ hipError_t split_mb(const LinearArgs &a, const SplitPlan &pl, int32_t *part, hip
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Streaming K-split path for 16 < M <= 64 (with a workspace).  A workgroup of 4 waves owns
+// R = 16 RB weight rows and one of S equal K ranges; in each stage of 512 k, wave w takes
+// k in [128 w, 128 w + 128) and streams its 128-k slice of every one of the (up to 64) tokens
+// and its 64-byte piece of each of the R rows through its own 2-stage LDS ring (direct
+// global -> LDS loads), multiplying a stage as soon as its own loads have landed.  Per 64 k,
+// one v_mfma_i32_16x16x64_i8 per (16-token block, 16-row block), lane group kb taking the
+// 16 k at 16 kb in both operands.  The 4 waves' partial tiles are summed through LDS in a
+// fixed order and stored as int32 partials [S, M, N]; k_gemv_reduce adds the S ranges in
+// a fixed order and applies the epilogue.  Workgroup b takes K range b % S, so the blocks
+// dealt round-robin to one XCD share a K range and its token slices stay in that XCD's L2.
+constexpr int kSkWaves = 4;
+constexpr int kSkStage = 128 * kSkWaves;  // k per stage
+
+template <int ABITS, int MB, int RB>
+struct SKL {
+    static constexpr int T = 16 * MB, R = 16 * RB;
+    static constexpr int TB = ABITS == 8 ? 128 : 64;            // token bytes per wave and stage
+    static constexpr int CPT = TB / 16;                          // 8 or 4 chunks
+    static constexpr int ACT = T * TB < 1024 ? 1024 : T * TB;    // whole 1 KB loads
+    static constexpr int WB = R * 64;                            // weight bytes per wave and stage
+    static constexpr int SLOT = ACT + WB;
+    static constexpr int D = 2;
+    static constexpr int LA = ACT / 1024, LB = WB / 1024;
+    static constexpr int LPS = LA + LB;
+    static constexpr int RED = kSkWaves * RB * MB * 1024;        // v4i tiles of the waves
+    static constexpr int RING = kSkWaves * D * SLOT > RED ? kSkWaves * D * SLOT : RED;
+    static constexpr int LDS = RING;
+    static_assert(WB % 1024 == 0 && (D - 1) * LPS <= 63 && LDS <= 160 * 1024, "split stream layout");
+};
+
+template <int ABITS, int MB, int RB>
+__global__ void __launch_bounds__(64 * kSkWaves) k_gemv_sk(LinearArgs p, int S, int32_t *__restrict__ part, int asym) {
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+    using L = SKL<ABITS, MB, RB>;
+    constexpr int R = L::R, CPT = L::CPT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kb = lane >> 4;
+    const int sp = (int)blockIdx.x % S, tile = (int)blockIdx.x / S;
+    const int64_t n0 = (int64_t)tile * R;
+    const int64_t K = p.K, M = p.M;
+    const int64_t KS = K / S;
+    const int nst = (int)(KS / kSkStage);
+    const int64_t rowA = ABITS == 8 ? K : K / 2;
+    const int64_t rowB = K / 2;
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t xr = asym ? 0x88888888u : 0u;
+    const int ring = wave * L::D * L::SLOT;
+    constexpr uint32_t ASTEP = kSkStage * ABITS / 8, BSTEP = kSkStage / 2;
+
+    // LDS position (t, c) of a token slice holds global chunk c ^ (t & (CPT - 1)); position
+    // (r, c) of a 64-byte weight piece holds chunk c ^ ((r >> 1) & 3)
+    uint32_t arow[L::LA], ain[L::LA], brow[L::LB], bin[L::LB];
+#pragma unroll
+    for (int j = 0; j < L::LA; ++j) {
+        const int f = min(j * 64 + lane, L::T * CPT - 1);
+        const int t = f / CPT, c = f % CPT;
+        arow[j] = (uint32_t)(min<int64_t>(t, M - 1) * rowA);
+        ain[j] = (uint32_t)(KS * sp * ABITS / 8 + wave * L::TB + 16 * (c ^ (t & (CPT - 1))));
+    }
+#pragma unroll
+    for (int j = 0; j < L::LB; ++j) {
+        const int r = 16 * j + lane / 4;
+        brow[j] = (uint32_t)((min<int64_t>(n0 + r, p.N - 1) - n0) * rowB);
+        bin[j] = (uint32_t)(KS * sp / 2 + 64 * wave + 16 * ((lane & 3) ^ ((r >> 1) & 3)));
+    }
+    const uint64_t bbase = (uint64_t)(p.B + n0 * rowB);
+    auto issue = [&](int i) __attribute__((always_inline)) {
+        const uint32_t slot = smem_base + (uint32_t)(ring + (i % L::D) * L::SLOT);
+#pragma unroll
+        for (int j = 0; j < L::LA; ++j) gl_lds16_so((uint64_t)p.A, arow[j] + ain[j] + (uint32_t)i * ASTEP, slot + 1024 * j);
+#pragma unroll
+        for (int j = 0; j < L::LB; ++j) gl_lds16_so(bbase, brow[j] + bin[j] + (uint32_t)i * BSTEP, slot + L::ACT + 1024 * j);
+    };
+    for (int i = 0; i < L::D; ++i)
+        if (i < nst) issue(i);
+
+    v4i acc[MB][RB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[mb][rb] = v4i{0, 0, 0, 0};
+
+    for (int i = 0; i < nst; ++i) {
+        wait_rem<L::LPS, L::D - 1>(min(L::D - 1, nst - 1 - i));
+        const uint8_t *sl = smem + ring + (i % L::D) * L::SLOT;
+        uint4 xa[2][MB];
+        uint2 wv[2][RB];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // k in [64 h, 64 h + 64) of the wave's slice
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int t = min(16 * mb + lr, (int)M - 1);
+                const uint8_t *ta = sl + (16 * mb + lr) * L::TB;
+                if constexpr (ABITS == 8) {
+                    xa[h][mb] = *reinterpret_cast<const uint4 *>(ta + 16 * ((4 * h + kb) ^ (t & (CPT - 1))));
+                } else {
+                    const uint2 x2 = *reinterpret_cast<const uint2 *>(ta + 16 * ((2 * h + (kb >> 1)) ^ (t & (CPT - 1))) +
+                                                                      8 * (kb & 1));
+                    xa[h][mb] = make_uint4(x2.x, x2.y, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r = 16 * rb + lr;
+                wv[h][rb] = *reinterpret_cast<const uint2 *>(sl + L::ACT + r * 64 + 16 * ((2 * h + (kb >> 1)) ^ ((r >> 1) & 3)) +
+                                                             8 * (kb & 1));
+            }
+        }
+        wait_lgkmcnt0();  // this wave's reads of the slot are complete before it is refilled
+        if (i + L::D < nst) issue(i + L::D);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i w[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint32_t d0 = wv[h][rb].x ^ xr, d1 = wv[h][rb].y ^ xr;
+                if constexpr (ABITS == 8) {
+                    uint32_t lo0, hi0, lo1, hi1;
+                    unpack_nat(d0, lo0, hi0);
+                    unpack_nat(d1, lo1, hi1);
+                    w[rb] = v4i{(int)lo0, (int)hi0, (int)lo1, (int)hi1};
+                } else {
+                    w[rb] = evod(d0, d1);
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                v4i a;
+                if constexpr (ABITS == 8) a = __builtin_bit_cast(v4i, xa[h][mb]);
+                else a = evod(xa[h][mb].x, xa[h][mb].y);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) acc[mb][rb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[rb], a, acc[mb][rb], 0, 0, 0);
+            }
+        }
+    }
+
+    // fixed-order sum of the 4 waves' tiles, then int32 partials: 16x16 layout, lane l,
+    // register r holds row 4 (l / 16) + r of token l % 16
+    wait_vmcnt<0>();
+    __syncthreads();
+    v4i *red = reinterpret_cast<v4i *>(smem);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) red[((wave * MB + mb) * RB + rb) * 64 + lane] = acc[mb][rb];
+    __syncthreads();
+    for (int b = wave; b < MB * RB; b += kSkWaves) {
+        const int mb = b / RB, rb = b % RB;
+        v4i t = red[(mb * RB + rb) * 64 + lane];
+#pragma unroll
+        for (int q = 1; q < kSkWaves; ++q) t += red[((q * MB + mb) * RB + rb) * 64 + lane];
+        const int64_t m = 16 * mb + lr;
+        const int64_t nb = n0 + 16 * rb + 4 * kb;
+        if (m >= M) continue;
+        int32_t *P = part + ((int64_t)sp * M + m) * p.N;
+        if (nb + 3 < p.N && (p.N & 3) == 0) {
+            *reinterpret_cast<int4 *>(P + nb) = make_int4(t[0], t[1], t[2], t[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (nb + r < p.N) P[nb + r] = t[r];
+        }
+    }
+}
+
+// Plan of the split stream: 32, 48 or 64 rows per workgroup and S K ranges (whole 512-k
+// stages, at least 2 per range), minimising the per-CU bytes of the busiest round: weight
+// bytes (HBM), token bytes (re-read from L2, weighted 0.3) and the partials written and read
+// back.  S = 0: no plan.
+struct SkPlan {
+    int RB, S;
+    unsigned grid;
+};
+
+// Used where it measured faster than the split and ring kernels (M = 24 ... 64 at K = 4096 and
+// 12288): a plan with several K ranges, or up to 32 tokens; one K range at 48-64 tokens (at
+// K = 4096, N = 12288) lost to the ring kernel.
+SkPlan plan_sk(int64_t M, int64_t N, int64_t K, int act_bits);
+bool sk_used(const SkPlan &pl, int64_t M) { return pl.S >= 2 || (pl.S == 1 && M <= 32); }
+
+SkPlan plan_sk(int64_t M, int64_t N, int64_t K, int act_bits) {
+    SkPlan best{0, 0, 0};
+    if (M <= 16 || M > 64 || K % kSkStage) return best;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    double bestv = 1e30;
+    for (int rb = 4; rb >= 2; --rb) {
+        const int64_t tiles = (N + 16 * rb - 1) / (16 * rb);
+        for (int S = 1; S <= 8; S *= 2) {
+            if (K % ((int64_t)S * kSkStage) || K / S < 2 * kSkStage) continue;
+            const int64_t wg = tiles * S, rounds = (wg + ncu - 1) / ncu, KS = K / S;
+            const double v = (double)rounds * (16.0 * rb * KS / 2 + 0.3 * (double)M * KS * act_bits / 8) +
+                             2.0 * S * (double)M * N * 4 / ncu;
+            if (v < bestv) {
+                bestv = v;
+                best = SkPlan{rb, S, (unsigned)wg};
+            }
+        }
+    }
+    return best;
+}
+
+template <int ABITS, int MB, int RB>
+hipError_t launch_sk_t(const LinearArgs &a, const SkPlan &pl, int32_t *part, hipStream_t st) {
+    using L = SKL<ABITS, MB, RB>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv_sk<ABITS, MB, RB>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((k_gemv_sk<ABITS, MB, RB>), dim3(pl.grid), dim3(64 * kSkWaves), L::LDS, st, a, pl.S, part,
+                       a.zp ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = a.M * ((a.N + 3) / 4);
+    hipLaunchKernelGGL((k_gemv_reduce<ABITS>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a, pl.S,
+                       part, a.zp ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int ABITS, int MB>
+hipError_t sk_rb(const LinearArgs &a, const SkPlan &pl, int32_t *part, hipStream_t st) {
+    switch (pl.RB) {
+        case 2: return launch_sk_t<ABITS, MB, 2>(a, pl, part, st);
+        case 3: return launch_sk_t<ABITS, MB, 3>(a, pl, part, st);
+        default: return launch_sk_t<ABITS, MB, 4>(a, pl, part, st);
+    }
+}
+
+template <int ABITS>
+hipError_t sk_mb(const LinearArgs &a, const SkPlan &pl, int32_t *part, hipStream_t st) {
+    if (a.M <= 32) return sk_rb<ABITS, 2>(a, pl, part, st);
+    if (a.M <= 48) return sk_rb<ABITS, 3>(a, pl, part, st);
+    return sk_rb<ABITS, 4>(a, pl, part, st);
+}
 
 // ---------------------------------------------------------------------------------------
 // Streaming path for M <= 16 (no workspace, one pass over K): every wave streams its own
@@ -1359,6 +1628,8 @@ hipError_t fused_tm(const LinearArgs &a, const void *X, hipStream_t st) {
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits) {
     if (M <= 16) return 0;  // the streaming kernel needs none
+    const SkPlan sk = plan_sk(M, N, K, act_bits);
+    if (sk_used(sk, M)) return (size_t)sk.S * (size_t)M * (size_t)N * sizeof(int32_t);
     const SplitPlan pl = plan_split(M, N, K, act_bits);
     return pl.S > 1 ? (size_t)pl.S * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
 }
@@ -1367,6 +1638,13 @@ hipError_t launch_gemv(const LinearArgs &a, int act_bits, void *ws, size_t ws_by
     if (a.M == 0) return hipSuccess;
     if (a.M > 64) return hipErrorInvalidValue;
     if (a.M <= 16) return act_bits == 8 ? launch_stream<8>(a, st) : launch_stream<4>(a, st);
+    {
+        const SkPlan sk = plan_sk(a.M, a.N, a.K, act_bits);
+        if (sk_used(sk, a.M) && ws && ws_bytes >= (size_t)sk.S * (size_t)a.M * (size_t)a.N * sizeof(int32_t)) {
+            int32_t *part = static_cast<int32_t *>(ws);
+            return act_bits == 8 ? sk_mb<8>(a, sk, part, st) : sk_mb<4>(a, sk, part, st);
+        }
+    }
     const SplitPlan pl = plan_split(a.M, a.N, a.K, act_bits);
     const size_t need = pl.S > 1 ? (size_t)pl.S * (size_t)a.M * (size_t)a.N * sizeof(int32_t) : 0;
     if (pl.S >= 1 && (need == 0 || (ws && ws_bytes >= need))) {
