@@ -94,53 +94,72 @@ struct GrpArgs {
     void *part;              // [S, M, N] partial sums (split)
 };
 
-// Issue the loads of one stage (global k0 .. k0 + 63) into LDS slot `st`.
+// Per-lane byte offsets of one stage's direct loads, relative to the stage's uniform base
+// addresses (computed once: rows clamped to the last valid row, chunks swizzled), and the
+// number of lanes of the last activation instruction that carry a chunk.
 template <int AT, int FM, int FN, int WM, int WN, int STAGES>
-__device__ __forceinline__ void issue_stage(const GrpArgs &p, uint8_t *smem, int slot, int64_t m0, int64_t n0,
-                                            int64_t k0, int wave, int lane) {
+struct StageOffsets {
+    using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
+    uint32_t a[C::AI], w[C::WI], s;
+};
+
+template <int AT, int FM, int FN, int WM, int WN, int STAGES>
+__device__ __forceinline__ StageOffsets<AT, FM, FN, WM, WN, STAGES> stage_offsets(const GrpArgs &p, int64_t m0,
+                                                                                 int64_t n0, int wave, int lane) {
+    using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
+    StageOffsets<AT, FM, FN, WM, WN, STAGES> o;
+    const int ebits = AT == 8 ? 8 : AT == 4 ? 4 : 16;
+    const int64_t krow = (p.K * ebits) / 8;  // activation row bytes
+#pragma unroll
+    for (int i = 0; i < C::AI; ++i) {
+        const int ci = min(wave * C::CA + i * 64 + lane, (wave + 1) * C::CA - 1);
+        const int r = (ci * 16) / C::AROW, pc = ci % (C::AROW / 16);
+        const int64_t rr = min<int64_t>(m0 + r, p.M - 1) - m0;
+        o.a[i] = (uint32_t)(rr * krow + 16 * swz<C::AROW>(r, pc));
+    }
+#pragma unroll
+    for (int i = 0; i < C::WI; ++i) {
+        const int ci = min(wave * C::CW + i * 64 + lane, (wave + 1) * C::CW - 1);
+        const int n = ci / 2, pc = ci % 2;
+        const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
+        o.w[i] = (uint32_t)(nn * (p.K / 2) + 16 * swz<32>(n, pc));
+    }
+    {
+        const int nf = C::BN / 4;
+        const int n = wave * nf + min(lane, nf - 1);
+        const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
+        o.s = (uint32_t)(nn * (p.K / p.gw) * 2);
+    }
+    return o;
+}
+
+// Issue the loads of one stage (global k0 .. k0 + 63) into LDS slot `slot`.  Lanes past a
+// wave's share issue nothing (their offsets are clamped only to stay in range); every
+// instruction keeps at least one active lane, so each counts once in vmcnt.
+template <int AT, int FM, int FN, int WM, int WN, int STAGES>
+__device__ __forceinline__ void issue_stage(const GrpArgs &p, const StageOffsets<AT, FM, FN, WM, WN, STAGES> &o,
+                                            uint8_t *smem, int slot, int64_t m0, int64_t n0, int64_t k0, int wave,
+                                            int lane) {
     using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
     const uint32_t base = lds_addr(smem) + slot * C::STAGE;
     const int ebits = AT == 8 ? 8 : AT == 4 ? 4 : 16;
-    const int64_t krow = (p.K * ebits) / 8;  // activation row bytes
-    // activations
-    {
-        const uint64_t g0 = (uint64_t)(p.A + m0 * krow + (k0 * ebits) / 8);
+    const int64_t krow = (p.K * ebits) / 8;
+    const uint64_t ga = (uint64_t)(p.A + m0 * krow + (k0 * ebits) / 8);
 #pragma unroll
-        for (int i = 0; i < C::AI; ++i) {
-            const int ci = wave * C::CA + i * 64 + lane;
-            const int r = (ci * 16) / C::AROW, pc = ci % (C::AROW / 16);
-            const int c = swz<C::AROW>(r, pc);
-            const int64_t rr = min<int64_t>(m0 + r, p.M - 1) - m0;
-            if (i * 64 + lane < C::CA)
-                gl_lds16_so(g0, (uint32_t)(rr * krow + 16 * c), base + (wave * C::CA + i * 64) * 16);
-        }
-    }
-    // weights
-    {
-        const uint64_t g0 = (uint64_t)(p.B + n0 * (p.K / 2) + k0 / 2);
+    for (int i = 0; i < C::AI; ++i)
+        if (C::CA % 64 == 0 || i * 64 + lane < C::CA) gl_lds16_so(ga, o.a[i], base + (wave * C::CA + i * 64) * 16);
+    const uint64_t gb = (uint64_t)(p.B + n0 * (p.K / 2) + k0 / 2);
 #pragma unroll
-        for (int i = 0; i < C::WI; ++i) {
-            const int ci = wave * C::CW + i * 64 + lane;
-            const int n = ci / 2, pc = ci % 2;
-            const int c = swz<32>(n, pc);
-            const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
-            if (i * 64 + lane < C::CW)
-                gl_lds16_so(g0, (uint32_t)(nn * (p.K / 2) + 16 * c), base + C::ACT + (wave * C::CW + i * 64) * 16);
-        }
-    }
+    for (int i = 0; i < C::WI; ++i)
+        if (C::CW % 64 == 0 || i * 64 + lane < C::CW) gl_lds16_so(gb, o.w[i], base + C::ACT + (wave * C::CW + i * 64) * 16);
     // scales of this stage: one dword per feature (gw = 32: the stage's two groups; else the
     // group holding the stage, zero-extended)
-    {
-        const int64_t ng = p.K / p.gw;
-        const uint64_t g0 = (uint64_t)(p.gs + n0 * ng);
-        const int nf = C::BN / 4;
-        const int n = wave * nf + lane;
-        const int64_t nn = min<int64_t>(n0 + n, p.N - 1) - n0;
-        const uint32_t lb = base + C::ACT + C::WB + wave * nf * 4;
-        if (lane < nf) {
-            if (p.gw == 32) gl_lds4_so(g0, (uint32_t)((nn * ng + k0 / 32) * 2), lb);
-            else gl_lds2_so(g0, (uint32_t)((nn * ng + k0 / p.gw) * 2), lb);
-        }
+    const int nf = C::BN / 4;
+    const uint64_t gs = (uint64_t)(p.gs + n0 * (p.K / p.gw) + k0 / p.gw);
+    const uint32_t lb = base + C::ACT + C::WB + wave * nf * 4;
+    if (lane < nf) {
+        if (p.gw == 32) gl_lds4_so(gs, o.s, lb);
+        else gl_lds2_so(gs, o.s, lb);
     }
 }
 
@@ -163,8 +182,11 @@ __device__ __forceinline__ bf8 bf16_codes(uint32_t d) {
     return r;
 }
 
+// Two waves per SIMD (at most 256 registers per lane): one wave's group scaling and operand
+// unpacking then runs beside the other's MFMAs.
 template <int AT, int FM, int FN, int WM, int WN, int STAGES, int EPI>
-__global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int tiles_n) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_gemm_grp(GrpArgs p, int tiles_m,
+                                                                                           int tiles_n) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
     constexpr bool INT = AT != 16;
@@ -216,9 +238,10 @@ __global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int ti
             }
         }
 
+    const StageOffsets<AT, FM, FN, WM, WN, STAGES> so = stage_offsets<AT, FM, FN, WM, WN, STAGES>(p, m0, n0, wave, lane);
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue_stage<AT, FM, FN, WM, WN, STAGES>(p, smem, s, m0, n0, kbeg + s * BK, wave, lane);
+        if (s < nk) issue_stage<AT, FM, FN, WM, WN, STAGES>(p, so, smem, s, m0, n0, kbeg + s * BK, wave, lane);
 
     int gstep = 0;  // steps into the current group
     for (int kt = 0; kt < nk; ++kt) {
@@ -232,7 +255,7 @@ __global__ void __launch_bounds__(256) k_gemm_grp(GrpArgs p, int tiles_m, int ti
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (kt + STAGES - 1 < nk)
-            issue_stage<AT, FM, FN, WM, WN, STAGES>(p, smem, (kt + STAGES - 1) % STAGES, m0, n0,
+            issue_stage<AT, FM, FN, WM, WN, STAGES>(p, so, smem, (kt + STAGES - 1) % STAGES, m0, n0,
                                                     kbeg + (int64_t)(kt + STAGES - 1) * BK, wave, lane);
         const uint8_t *st = smem + slot * C::STAGE;
         const uint8_t *wst = st + C::ACT;
