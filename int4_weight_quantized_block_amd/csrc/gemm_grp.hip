@@ -73,7 +73,7 @@ template <int ROWBYTES>
 __device__ __forceinline__ int swz(int r, int c) {
     if constexpr (ROWBYTES == 128) return c ^ (r & 7);
     else if constexpr (ROWBYTES == 64) return c ^ ((r >> 1) & 3);
-    else return c ^ ((r >> 2) & 1);  // 32-byte rows
+    else return c ^ ((r >> 3) & 1);  // 32-byte rows: rows r and r + 8 of a 16-lane read differ
 }
 
 struct GrpArgs {
@@ -490,12 +490,12 @@ int plan_s(int64_t M, int64_t N, int64_t K, int gw) {
     return S;
 }
 
-// Ring depths (measured at 4096 x 3072 x 3072 and at 1 and 16 tokens x 4096 -> 12288): large
-// M, 6 stages for integer activations and 3 for bf16 (whose stages are twice as large; deeper
-// rings cost occupancy); small M, 4 stages with K split over about three workgroups per CU.
+// Ring depths (measured at 4096 x 3072 x 3072 and at 1 and 16 tokens x 4096 -> 12288, two waves
+// per SIMD): large M, 3 stages for int8 and bf16 activations, 4 for int4; small M, 4 stages
+// with K split over about three workgroups per CU.
 template <int AT, int EPI>
 hipError_t launch_at(const GrpArgs &a, hipStream_t st) {
-    if (a.M > 64) return AT == 16 ? launch_cfg<AT, 2, 2, 2, 2, 3, EPI>(a, st) : launch_cfg<AT, 2, 2, 2, 2, 6, EPI>(a, st);
+    if (a.M > 64) return AT == 4 ? launch_cfg<AT, 2, 2, 2, 2, 4, EPI>(a, st) : launch_cfg<AT, 2, 2, 2, 2, 3, EPI>(a, st);
     if (a.M > 32) return launch_cfg<AT, 2, 1, 1, 4, 4, EPI>(a, st);
     return launch_cfg<AT, 1, 1, 1, 4, 4, EPI>(a, st);
 }
