@@ -79,6 +79,34 @@ struct Lay {
     static constexpr int LDS_BYTES = C_ZP + BN * 4;
 };
 
+constexpr int SROW = WTN * 2 + 16;            // epilogue staging row: 96 bf16 + pad
+constexpr int STG_BYTES = kWaves * 32 * SROW;  // one block of 32 tokens per wave
+
+// LDS placement of the low-rank operands for ranks r <= 16 * LRK (r % 4 == 0): the tile's
+// rows of t (fp32, RP ranks + 16 pad bytes per row, so that the 16-byte reads of 8
+// consecutive lanes hit distinct banks) and l2 transposed to [feature][rank] (bf16, same
+// padding), so that every MFMA operand is one 16-byte LDS read.  Each goes into a ring slot
+// that is free by the epilogue when it fits (t: the slot of stage nk - 3; l2T: past the
+// output staging in the slot of stage nk - 2), else past the l2 tile.
+template <int ABITS, int LRK>
+struct LrLay {
+    static constexpr int RP = 16 * LRK;
+    static constexpr int T_PITCH = RP * 4 + 16;
+    static constexpr int T_CPR = T_PITCH / 16;                 // 16-byte chunks per row (last: pad)
+    static constexpr int T_BYTES = BM * T_PITCH;
+    static constexpr int T_INS = BM * T_CPR / 64 / kWaves;     // direct loads per wave
+    static constexpr int L2T_PITCH = RP * 2 + 16;
+    static constexpr int L2T_BYTES = BN * L2T_PITCH;
+    static constexpr int L2_BYTES = 6 * 1024 * LRK;            // the [r, BN] l2 tile (whole 1 KB loads)
+    static constexpr bool T_IN_SLOT = T_BYTES <= Lay<ABITS>::STAGE;
+    static constexpr bool L2T_IN_SLOT = STG_BYTES + L2T_BYTES <= Lay<ABITS>::STAGE;
+    static constexpr int DED = Lay<ABITS>::LDS_BYTES + L2_BYTES;  // dedicated room past the l2 tile
+    static constexpr int T_DED = DED, L2T_DED = DED + (T_IN_SLOT ? 0 : T_BYTES);
+    static constexpr int LDS_TOTAL = L2T_DED + (L2T_IN_SLOT ? 0 : L2T_BYTES);
+    static_assert(BM * T_CPR % (64 * kWaves) == 0, "t staging loads");
+    static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+};
+
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float fl8 __attribute__((ext_vector_type(8)));
 typedef float fl16 __attribute__((ext_vector_type(16)));
@@ -221,6 +249,10 @@ enum Epi { kEpiBf16 = 0, kEpiLowRank = 1, kEpiI32 = 2, kEpiPartial = 3, kEpiLowR
 // of 16 ranks on the bf16 MFMA)
 constexpr bool epi_lr(int e) { return e == kEpiLowRank || e == kEpiLowRank16 || e == kEpiLowRank32; }
 constexpr int epi_lrk(int e) { return e == kEpiLowRank16 ? 1 : e == kEpiLowRank32 ? 2 : 4; }
+// r <= 16 / 32 with r % 4 == 0, 16-byte aligned t rows and N % 8 == 0: t and l2 staged in LDS
+// (LrLay); kEpiLowRank (any r <= 64) reads t from global memory per token block
+constexpr bool epi_lr_lds(int e) { return e == kEpiLowRank16 || e == kEpiLowRank32; }
+constexpr int epi_lds_k(int e) { return epi_lr_lds(e) ? epi_lrk(e) : 1; }  // LrLay's LRK
 
 // The tiles one launch covers: ids [base, base + count); with kEpiPartial each tile is split
 // into kparts equal K ranges (one workgroup each) whose partial tiles go to part.
@@ -295,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
     // through registers (a one-off wait, ragged N only).  The prologue's wait and barrier
     // make it visible to every wave.
     if constexpr (epi_lr(EPI)) {
-        if (l2_dma) {
+        if (epi_lr_lds(EPI) || l2_dma) {
             constexpr int CPR = BN * 2 / 16;  // 24 chunks of 16 bytes per row
             const int nins = (CPR * p.lr_r + 63) / 64;
             const uint32_t lb = lds_addr(smem) + L::LDS_BYTES;
@@ -305,7 +337,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
                 const int64_t nn = min<int64_t>(n0 + 8 * (c % CPR), p.N - 8) - n0;
                 gl_lds16_so((uint64_t)(p.lr_l2 + n0), (uint32_t)((int64_t)q * p.N * 2 + nn * 2), lb + ins * 1024);
             }
-        } else {
+        } else if constexpr (!epi_lr_lds(EPI)) {
             uint16_t *lt = reinterpret_cast<uint16_t *>(smem + L::LDS_BYTES);
             const int tot = p.lr_r * BN;
             for (int e0 = tid; e0 < tot; e0 += 8 * kThreads) {
@@ -382,6 +414,27 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         }
     };
 
+    // Low-rank forms with staged operands: the tile's t rows go to LDS by direct loads, issued
+    // once the slot of stage nk - 3 is free (or at the epilogue when nk < 3), so their latency
+    // hides under the last stages.  Chunk c of a staged row holds ranks 4c .. 4c+3; the padding
+    // chunk and chunks past r re-read the row's last chunk (finite values that meet zero ranks
+    // of l2T); rows past M repeat row M - 1 (computed, never stored).
+    using LL = LrLay<ABITS, epi_lds_k(EPI)>;
+    constexpr int TW = epi_lr_lds(EPI) ? LL::T_INS : 0;
+    const uint32_t t_lds = smem_base + (uint32_t)(LL::T_IN_SLOT ? (nk % STAGES) * L::STAGE : LL::T_DED);
+    auto issue_t = [&]() __attribute__((always_inline)) {
+        const int last = (p.lr_r >> 2) - 1;
+#pragma unroll
+        for (int u = 0; u < LL::T_INS; ++u) {
+            const int ins = wave * LL::T_INS + u;
+            const int c = ins * 64 + lane;
+            const int row = c / LL::T_CPR, cc = min(c % LL::T_CPR, last);
+            const int64_t rr = min<int64_t>(m0 + row, p.M - 1) - m0;
+            gl_lds16_so((uint64_t)(p.lr_t + m0 * p.lr_ldt), (uint32_t)((rr * p.lr_ldt + 4 * cc) * 4),
+                        t_lds + (uint32_t)ins * 1024);
+        }
+    };
+
     v16i acc[FN][FM];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
@@ -429,9 +482,14 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         half_stage<ABITS, ASYM, true, false>(fa, oa, fb, ob, smem + slot * L::STAGE, 1, wm, wn, lr, kb, acc, load_one,
                                              0, 0);
         if (kt + 2 < nk) wait_vmcnt<L::LOADS>();
+        else if (epi_lr_lds(EPI) && nk >= 3) wait_vmcnt<TW>();  // the staged t may still be in flight
         else wait_vmcnt<0>();
         wait_lgkmcnt0();
         __builtin_amdgcn_s_barrier();
+        // every wave has read stage kt: with kt = nk - 3 its slot is the t slot
+        if constexpr (epi_lr_lds(EPI)) {
+            if (kt == nk - 3) issue_t();
+        }
         half_stage<ABITS, ASYM, true, false>(fb, ob, fa, oa, smem + nslot * L::STAGE, 0, wm, wn, lr, kb, acc, load_one,
                                              0, 0);
         slot = nslot;
@@ -515,10 +573,121 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         }
         return;
     }
-    constexpr int SROW = WTN * 2 + 16;  // staged row: 96 bf16 + pad
     uint8_t *stg = smem + ((nk + 1) % STAGES) * L::STAGE + wave * 32 * SROW;
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     const bool full_n = (p.N & 7) == 0;  // 16-byte aligned rows
+    // stores of a staged block: 32 rows x 12 chunks of 16 bytes; LDS operations of one wave
+    // complete in order, so the reads see this block's writes and the next block's writes
+    // follow these reads
+    auto store_block = [&](int64_t mrow0) __attribute__((always_inline)) {
+        constexpr int CPR = WTN * 2 / 16;
+#pragma unroll
+        for (int k = 0; k < 32 * CPR / 64; ++k) {
+            const int c = lane + 64 * k;
+            const int row = c / CPR, ch = c % CPR;
+            const int64_t m = mrow0 + row, n = n0 + wn * WTN + ch * 8;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * SROW + ch * 16);
+            if (m >= p.M || n >= p.N) continue;
+            if (full_n && n + 7 < p.N) {
+                // streaming store: the output is not read again by this kernel
+                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(Y + m * p.N + n));
+            } else {
+                const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
+                for (int r = 0; r < 8 && n + r < p.N; ++r) Y[m * p.N + n + r] = h[r];
+            }
+        }
+    };
+    // a block's outputs as bf16 into this wave's staging rows (y: 4 consecutive features of
+    // token lr per register group g)
+    auto stage_bf16 = [&](int j, const float (&y)[16]) __attribute__((always_inline)) {
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        typedef float fl2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const fl2 f01 = {y[4 * g], y[4 * g + 1]}, f23 = {y[4 * g + 2], y[4 * g + 3]};
+            const bf2 h0 = __builtin_convertvector(f01, bf2);
+            const bf2 h1 = __builtin_convertvector(f23, bf2);
+            *reinterpret_cast<uint2 *>(stg + lr * SROW + (j * 32 + 8 * g + 4 * kb) * 2) =
+                make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
+        }
+    };
+
+    if constexpr (epi_lr_lds(EPI)) {
+        // Low-rank branch from LDS: lr[n][m] = sum_q l2[q][n] t[m][q] on the bf16 MFMA with l2
+        // transposed as the A operand (rows = features) and t as the B operand (columns =
+        // tokens), so the product lands in the accumulators' 32x32 layout; it is accumulated
+        // onto the dequantized output (the MFMA's C operand).  t (f32) goes in as a bf16 high
+        // part plus a bf16 remainder (about 16 significant bits per product); l2 is bf16.
+        constexpr int LRK = epi_lrk(EPI);
+        const int lrr = p.lr_r;
+        if (nk < 3) issue_t();
+        // l2 [q][BN] -> l2T [BN][RP] (ranks past r zero), by all waves, while t lands
+        const uint16_t *l2s = reinterpret_cast<const uint16_t *>(smem + L::LDS_BYTES);
+        uint8_t *l2t = LL::L2T_IN_SLOT ? smem + ((nk + 1) % STAGES) * L::STAGE + STG_BYTES : smem + LL::L2T_DED;
+        for (int e = tid; e < BN * (LL::RP / 8); e += kThreads) {
+            const int n = e % BN, q8 = e / BN;
+            uint32_t h[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) h[u] = 8 * q8 + u < lrr ? l2s[(8 * q8 + u) * BN + n] : 0u;
+            *reinterpret_cast<uint4 *>(l2t + n * LL::L2T_PITCH + 16 * q8) =
+                make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+        }
+        wait_vmcnt<0>();  // this wave's t loads (no stores are in flight yet)
+        wait_lgkmcnt0();
+        __builtin_amdgcn_s_barrier();
+        const uint8_t *ts = smem + (LL::T_IN_SLOT ? (nk % STAGES) * L::STAGE : LL::T_DED);
+        bf8 la[FN][LRK];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int ks = 0; ks < LRK; ++ks)
+                la[j][ks] = *reinterpret_cast<const bf8 *>(l2t + (wn * WTN + j * 32 + lr) * LL::L2T_PITCH +
+                                                           (16 * ks + 8 * kb) * 2);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 32 + lr;
+            bf8 th[LRK], tl[LRK];
+#pragma unroll
+            for (int ks = 0; ks < LRK; ++ks) {
+                const uint8_t *tp = ts + row * LL::T_PITCH + (16 * ks + 8 * kb) * 4;
+                const float4 u = *reinterpret_cast<const float4 *>(tp);
+                const float4 w = *reinterpret_cast<const float4 *>(tp + 16);
+                const fl8 tv = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+                th[ks] = __builtin_convertvector(tv, bf8);
+                tl[ks] = __builtin_convertvector(tv - __builtin_convertvector(th[ks], fl8), bf8);
+            }
+            fl16 y[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float sw[4], bs[4];
+                    int zc[4];
+                    consts(j, g, sw, bs, zc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int a = acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0);
+                        y[j][4 * g + r] = fmaf((float)a, sxv[i] * sw[r], bs[r]);
+                    }
+                }
+#pragma unroll
+            for (int ks = 0; ks < LRK; ++ks)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[j][ks], th[ks], y[j], 0, 0, 0);
+                    y[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[j][ks], tl[ks], y[j], 0, 0, 0);
+                }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                float yv[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) yv[v] = y[j][v];
+                stage_bf16(j, yv);
+            }
+            store_block(m0 + wm * WTM + i * 32);
+        }
+        return;
+    }
 
     // Low-rank branch on the bf16 MFMA: lr[n][m] = sum_q l2[q][n] t[m][q] comes out in the
     // accumulators' 32x32 layout when l2 transposed is the A operand (rows = features) and t
@@ -540,7 +709,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
 #pragma unroll
         for (int ks = 0; ks < LRK; ++ks) {
             const int q0 = 16 * ks + 8 * kb;
-            if ((lrr & 3) == 0 && (p.lr_ldt & 3) == 0) {  // 16-byte aligned rows: whole quads valid or not
+            // 16-byte aligned rows: whole quads valid or not
+            if ((lrr & 3) == 0 && (p.lr_ldt & 3) == 0 && ((uintptr_t)p.lr_t & 15) == 0) {
                 const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 const float4 u = q0 < lrr ? *reinterpret_cast<const float4 *>(tr + q0) : z;
                 const float4 w = q0 + 4 < lrr ? *reinterpret_cast<const float4 *>(tr + q0 + 4) : z;
@@ -604,24 +774,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
                     make_uint2(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1));
             }
         }
-        // 32 rows x 12 chunks of 16 bytes; LDS operations of one wave complete in order, so
-        // the reads see this block's writes and the next block's writes follow these reads
-        constexpr int CPR = WTN * 2 / 16;
-#pragma unroll
-        for (int k = 0; k < 32 * CPR / 64; ++k) {
-            const int c = lane + 64 * k;
-            const int row = c / CPR, ch = c % CPR;
-            const int64_t m = mrow0 + row, n = n0 + wn * WTN + ch * 8;
-            const uint4 v = *reinterpret_cast<const uint4 *>(stg + row * SROW + ch * 16);
-            if (m >= p.M || n >= p.N) continue;
-            if (full_n && n + 7 < p.N) {
-                // streaming store: the output is not read again by this kernel
-                __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(Y + m * p.N + n));
-            } else {
-                const uint16_t *h = reinterpret_cast<const uint16_t *>(&v);
-                for (int r = 0; r < 8 && n + r < p.N; ++r) Y[m * p.N + n + r] = h[r];
-            }
-        }
+        store_block(mrow0);
     }
 }
 
@@ -634,12 +787,39 @@ __global__ void __launch_bounds__(256) k_gemm_tail(LinearArgs p, int tiles_m, in
     constexpr int SHIFT = ABITS == 8 ? 4 : 8;
     constexpr float kUnscale = ABITS == 8 ? 1.0f / 16 : 1.0f / 256;
     constexpr int PER_TILE = BM * BN / 4 / 256;  // workgroups per tile
+    constexpr int TROWS = 8;                     // tile rows one workgroup touches (at most 7)
+    // low-rank operands of the workgroup: the tile's l2 columns [r, BN] and its t rows
+    __shared__ __attribute__((aligned(16))) uint16_t l2s[64 * BN];
+    __shared__ float ts[TROWS * 64];
     const int t = (int)blockIdx.x / PER_TILE;
     const int idx = ((int)blockIdx.x % PER_TILE) * 256 + (int)threadIdx.x;
     const int ml = idx / (BN / 4), nl = 4 * (idx % (BN / 4));
+    const int ml0 = ((int)blockIdx.x % PER_TILE) * 256 / (BN / 4);
     int tm, tn;
     tile_coords(tr.base + t, tiles_m, tiles_n, tm, tn);
     const int64_t m = (int64_t)tm * BM + ml, n = (int64_t)tn * BN + nl;
+    const bool lr = p.lr_t && !p.y_i32;
+    if (lr) {
+        const int64_t n0 = (int64_t)tn * BN;
+        const int r = p.lr_r;
+        if ((p.N & 7) == 0 && ((uintptr_t)p.lr_l2 & 15) == 0) {  // 16-byte rows; chunks all in [0, N) or all past it
+            for (int c = threadIdx.x; c < r * (BN / 8); c += 256) {
+                const int q = c / (BN / 8), cn = 8 * (c % (BN / 8));
+                const int64_t col = min<int64_t>(n0 + cn, p.N - 8);  // past N: unused columns
+                *reinterpret_cast<uint4 *>(l2s + q * BN + cn) =
+                    *reinterpret_cast<const uint4 *>(p.lr_l2 + (int64_t)q * p.N + col);
+            }
+        } else {
+            for (int c = threadIdx.x; c < r * BN; c += 256)
+                l2s[c] = p.lr_l2[(int64_t)(c / BN) * p.N + min<int64_t>(n0 + c % BN, p.N - 1)];
+        }
+        for (int c = threadIdx.x; c < TROWS * r; c += 256) {
+            const int row = c / r, q = c % r;
+            const int64_t mm = min<int64_t>((int64_t)tm * BM + ml0 + row, p.M - 1);
+            ts[row * 64 + q] = p.lr_t[mm * p.lr_ldt + q];
+        }
+        __syncthreads();
+    }
     if (m >= p.M || n >= p.N) return;
     const int32_t *P = tr.part + (int64_t)t * tr.kparts * (BM * BN) + ml * BN + nl;
     int4 s = *reinterpret_cast<const int4 *>(P);
@@ -661,34 +841,18 @@ __global__ void __launch_bounds__(256) k_gemm_tail(LinearArgs p, int tiles_m, in
         for (int r = 0; r < nv; ++r) Y[r] = a[r] >> SHIFT;
         return;
     }
-    // low-rank term of the 4 outputs: the loads of 16 ranks at a time are all issued before
-    // their fmas (one round trip per 16 ranks), 8-byte l2 reads when the rows allow it
+    // low-rank term of the 4 outputs from the staged operands (columns past N hold copies,
+    // never stored)
     float lw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (p.lr_t) {
-        const float *tm_ = p.lr_t + m * p.lr_ldt;
-        const uint16_t *l2 = p.lr_l2 + n;
-        if (nv == 4 && (p.N & 3) == 0) {
-            for (int q0 = 0; q0 < p.lr_r; q0 += 16) {
-                float tq[16];
-                uint2 w[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int q = min(q0 + u, p.lr_r - 1);  // past r: a repeated rank, weighted 0 below
-                    tq[u] = q0 + u < p.lr_r ? tm_[q] : 0.0f;
-                    w[u] = *reinterpret_cast<const uint2 *>(l2 + (int64_t)q * p.N);
-                }
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    lw[0] = fmaf(tq[u], bf16_lo(w[u].x), lw[0]);
-                    lw[1] = fmaf(tq[u], bf16_hi(w[u].x), lw[1]);
-                    lw[2] = fmaf(tq[u], bf16_lo(w[u].y), lw[2]);
-                    lw[3] = fmaf(tq[u], bf16_hi(w[u].y), lw[3]);
-                }
-            }
-        } else {
-            for (int r = 0; r < nv; ++r)
+    if (lr) {
+        const float *tq = ts + (ml - ml0) * 64;
 #pragma unroll 8
-                for (int q = 0; q < p.lr_r; ++q) lw[r] = fmaf(tm_[q], bf16_to_f32(l2[(int64_t)q * p.N + r]), lw[r]);
+        for (int q = 0; q < p.lr_r; ++q) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(l2s + q * BN + nl);
+            lw[0] = fmaf(tq[q], bf16_lo(w.x), lw[0]);
+            lw[1] = fmaf(tq[q], bf16_hi(w.x), lw[1]);
+            lw[2] = fmaf(tq[q], bf16_lo(w.y), lw[2]);
+            lw[3] = fmaf(tq[q], bf16_hi(w.y), lw[3]);
         }
     }
     const float sx = p.sx[m];
@@ -734,14 +898,17 @@ TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
 template <int ABITS, bool ASYM, bool KTAIL, int EPI>
 hipError_t launch_t(const LinearArgs &a, const TileRange &tr, unsigned grid, hipStream_t st) {
     // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
-    // 24 * r 16-byte chunks, at most 24 KB for r <= 64)
+    // 24 * r 16-byte chunks, at most 24 KB for r <= 64), plus the staged t and l2T where they
+    // do not fit in free ring slots
     constexpr size_t base = Lay<ABITS>::LDS_BYTES, maxl2 = 24 * 1024;
-    static_assert(base + maxl2 <= 160 * 1024, "LDS budget");
+    constexpr size_t maxlds = epi_lr_lds(EPI) ? (size_t)LrLay<ABITS, epi_lds_k(EPI)>::LDS_TOTAL : base + maxl2;
+    static_assert(maxlds <= 160 * 1024, "LDS budget");
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL, EPI>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(base + maxl2));
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)maxlds);
     if (attr != hipSuccess) return attr;
-    const int l2_dma = a.N % 8 == 0;
-    const size_t lds = base + (epi_lr(EPI) ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
+    const int l2_dma = a.N % 8 == 0 && ((uintptr_t)a.lr_l2 & 15) == 0;  // 16-byte aligned l2 rows
+    const size_t lds = epi_lr_lds(EPI) ? maxlds
+                       : base + (epi_lr(EPI) ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
     const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
     hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, a, tm, tn, l2_dma, tr);
     return hipGetLastError();
@@ -752,8 +919,10 @@ hipError_t launch_epi(const LinearArgs &a, const TileRange &tr, hipStream_t st) 
     const unsigned grid = (unsigned)tr.count;
     if (a.y_i32) return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(a, tr, grid, st);
     if (a.lr_t) {
-        if (a.lr_r <= 16) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(a, tr, grid, st);
-        if (a.lr_r <= 32) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(a, tr, grid, st);
+        const bool staged = a.N % 8 == 0 && ((uintptr_t)a.lr_l2 & 15) == 0 && a.lr_r % 4 == 0 && a.lr_ldt % 4 == 0 &&
+                            ((uintptr_t)a.lr_t & 15) == 0;
+        if (staged && a.lr_r <= 16) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(a, tr, grid, st);
+        if (staged && a.lr_r <= 32) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(a, tr, grid, st);
         return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(a, tr, grid, st);
     }
     return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(a, tr, grid, st);

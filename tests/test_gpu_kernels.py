@@ -235,16 +235,25 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,N,K,bits,asym,r", [
-    (300, 384, 512, 8, False, 32), (300, 389, 512, 8, True, 5), (260, 200, 768, 4, False, 20),
-    (300, 392, 256, 4, True, 40), (257, 384, 512, 8, False, 64), (513, 191, 320, 8, False, 63),
-    (8, 389, 512, 8, False, 20), (40, 384, 512, 4, True, 64),
+@pytest.mark.parametrize("M,N,K,bits,asym,r,tcol", [
+    (300, 384, 512, 8, False, 32, None), (300, 389, 512, 8, True, 5, None), (260, 200, 768, 4, False, 20, None),
+    (300, 392, 256, 4, True, 40, None), (257, 384, 512, 8, False, 64, None), (513, 191, 320, 8, False, 63, None),
+    (8, 389, 512, 8, False, 20, None), (40, 384, 512, 4, True, 64, None),
+    # large-M kernel with t and l2 staged in LDS (N % 8 == 0, r % 4 == 0, r <= 32): one,
+    # two (K tail) and three stages, int4 codes with t past the ring, ragged M over three
+    # tile rows, and t as a 16-byte aligned column range of a wider tensor
+    (270, 256, 128, 8, True, 16, None), (300, 392, 192, 4, True, 12, None), (300, 384, 384, 8, True, 24, None),
+    (300, 200, 320, 4, False, 32, None), (520, 384, 1024, 8, False, 28, None), (300, 384, 512, 8, False, 32, 8),
+    (300, 200, 512, 4, True, 16, 4),
+    # t starting at float 2 (8-byte aligned): refused with W4_ERR_ALIGN before any launch
+    (300, 384, 512, 8, False, 32, 2),
 ])
-def test_linear_lowrank_ranks(M, N, K, bits, asym, r):
+def test_linear_lowrank_ranks(M, N, K, bits, asym, r, tcol):
     """The low-rank branch at ranks that fill 1..4 k-steps of 16 (r % 4 != 0 included), with
     factors large enough that the branch carries a good part of the output; ragged N takes
-    the element-wise l2 staging of the large-M kernel."""
-    say("linear lowrank M=%d N=%d K=%d bits=%d asym=%s r=%d" % (M, N, K, bits, asym, r))
+    the element-wise l2 staging of the large-M kernel.  With tcol, t is columns tcol ..
+    tcol + r of a wider f32 tensor (row stride r + 12)."""
+    say("linear lowrank M=%d N=%d K=%d bits=%d asym=%s r=%d tcol=%s" % (M, N, K, bits, asym, r, tcol))
     g = 64
     rg = rng(7 * M + N + r)
     X = act_input(M, K, seed=M + 5 * r)
@@ -260,6 +269,14 @@ def test_linear_lowrank_ranks(M, N, K, bits, asym, r):
     t = w4.w4_lowrank_down(Xd, L1.t().contiguous().to(DEV))
     tref = oracle.to_f64(X) @ oracle.to_f64(L1)
     assert np.abs(np_(t) - tref).max() <= 1e-4 * np.abs(tref).max()
+    if tcol is not None:
+        wide = torch.full((M, r + 12), float("nan"), dtype=torch.float32, device=DEV)
+        wide[:, tcol:tcol + r] = t
+        t = wide[:, tcol:tcol + r]
+        if tcol % 4:
+            with pytest.raises(w4.W4Error, match="W4_ERR_ALIGN"):
+                w4.w4_linear(Xd, g, bits, *args, lowrank=w4.LowRank(l2=L2.to(DEV), t=t))
+            return
     y = w4.w4_linear(Xd, g, bits, *args, lowrank=w4.LowRank(l2=L2.to(DEV), t=t))
     err = rel_frob(y, ref["y64"])
     say("  rel frob %.3e" % err)
