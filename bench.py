@@ -770,23 +770,32 @@ def bench_double_block(args, dev):
 
     r = synth.LOWRANK
 
+    def timed(record, fn):
+        e0 = torch.cuda.Event(enable_timing=True) if record else None
+        if record:
+            e0.record(stream)
+        fn()
+        if record:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e1.record(stream)
+            gemm_times.append((e0, e1))
+
+    def lin_out(lins, name, t):
+        packed, s_w, bias, L1, L2 = lins[name]
+        return w4.LinearOut(packed=packed, row_scale=s_w, bias=bias, lowrank=w4.LowRank(l2=L2, t=t), out=outs[name])
+
     def step(record):
         for x, attn, lins in blocks:
             cache = w4.RotationCache()
-            for name, inp, l1, cols in (("qkv", x, lins["x_l1"], slice(0, r)), ("up", x, lins["x_l1"], slice(r, 2 * r)),
-                                        ("out", attn, lins["out"][3], slice(0, r))):
-                packed, s_w, bias, L1, L2 = lins[name]
-                q, sx, rs, tt = cache.get(inp, 256, 8, l1=l1)   # codes and x . L1 in one pass
-                t = tt[:, cols]
-                e0 = torch.cuda.Event(enable_timing=True) if record else None
-                if record:
-                    e0.record(stream)
-                w4.w4_linear_cached_rot(q, sx, rs, 8, packed, s_w, bias=bias, lowrank=w4.LowRank(l2=L2, t=t),
-                                        out=outs[name])
-                if record:
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e1.record(stream)
-                    gemm_times.append((e0, e1))
+            # QKV and MLP-up read the block input: one rotate-quant pass gives the codes and
+            # x . L1 of both, and their GEMMs run as one launch
+            q, sx, rs, tt = cache.get(x, 256, 8, l1=lins["x_l1"])
+            pair = [lin_out(lins, "qkv", tt[:, :r]), lin_out(lins, "up", tt[:, r:2 * r])]
+            timed(record, lambda: w4.w4_linear_cached_rot_multi(q, sx, rs, 8, pair))
+            q, sx, rs, tt = cache.get(attn, 256, 8, l1=lins["out"][3])
+            o = lin_out(lins, "out", tt)
+            timed(record, lambda: w4.w4_linear_cached_rot(q, sx, rs, 8, o.packed, o.row_scale, bias=o.bias,
+                                                          lowrank=o.lowrank, out=o.out))
             torch.nn.functional.gelu(outs["up"], out=h)  # host glue between the MLP linears
             packed, s_w, bias, L1, L2 = lins["down"]
             q, sx, rs, t = w4.w4_rotate_quant_act_lowrank(h, 256, 8, L1)

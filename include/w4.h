@@ -154,6 +154,37 @@ int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *t
                          const w4_lowrank *lr, int64_t M, int64_t N, int64_t K, void *Y,
                          int y_kind, void *ws, size_t ws_bytes, void *stream);
 
+/* One linear of w4_linear_cached_rot_multi: the arguments of w4_linear_cached_rot that differ
+ * between linears reading the same activation codes.  lr, when not NULL, must supply t. */
+typedef struct w4_linear_out {
+    const uint8_t *packed;
+    const float *row_scale;
+    const uint8_t *zp;
+    const void *bias;
+    int bias_dtype;
+    const w4_lowrank *lr;
+    int64_t N;
+    void *Y;
+    int y_kind;
+} w4_linear_out;
+
+/* w4_linear_cached_rot_multi - count linears on the same rotated and quantized activations
+ * (stable-diffusion.cpp PR #2010, "Summary": the activation work of one input is shared by
+ * every linear that reads it, e.g. the fused QKV and the MLP up-projection of a block with
+ * parallel attention and MLP).
+ *  q, tok_scale, tok_rowsum, act_bits, M, K : as for w4_linear_cached_rot, shared
+ *  outs[i]   : host array of count (1..8) linears; output i is written to outs[i].Y
+ *  ws        : serves the linears that run on their own, as in w4_linear_cached_rot
+ * For M > 64, consecutive linears i, i + 1 with the same weight mode (zp NULL or not), output
+ * kind and low-rank form run as ONE launch, so the tiles of both fill the compute units
+ * together instead of each leaving its last round partly idle; each such output equals
+ * w4_linear_cached_rot's without a workspace bit for bit.  The other linears run exactly as
+ * w4_linear_cached_rot.  Every argument is checked before anything is launched. */
+#define W4_MULTI_MAX 8
+int w4_linear_cached_rot_multi(const void *q, const float *tok_scale, const int32_t *tok_rowsum,
+                               int act_bits, int64_t M, int64_t K, int count,
+                               const w4_linear_out *outs, void *ws, size_t ws_bytes, void *stream);
+
 /* w4_linear - the whole layer: w4_rotate_quant_act into the workspace, then
  * w4_linear_cached_rot.  Arguments as above; ws must hold at least
  * w4_workspace_bytes(M, N, K, act_bits, r) + room for the activation codes, i.e.

@@ -31,7 +31,7 @@ __all__ = [
     "W4_MAX_K", "EXPORTS", "w4_linear_noalloc", "w4_noalloc_scratch_bytes",
     "w4_pack_weights_grouped", "w4_linear_cached_rot_grouped", "w4_linear_grouped",
     "w4_grouped_workspace_bytes", "w4_linear_grouped_workspace_bytes", "w4_rotate_quant_act_lowrank",
-    "w4_rotate_quant_act_lowrank_fused",
+    "w4_rotate_quant_act_lowrank_fused", "w4_linear_cached_rot_multi", "LinearOut", "MULTI_MAX",
 ]
 
 W4_OK, W4_ERR_INVALID_ARG, W4_ERR_SHAPE, W4_ERR_UNSUPPORTED, W4_ERR_ALIGN, W4_ERR_HIP, \
@@ -61,12 +61,19 @@ class _LowRankC(ctypes.Structure):
 
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
+
+class _LinearOutC(ctypes.Structure):
+    _fields_ = [("packed", _P), ("row_scale", _P), ("zp", _P), ("bias", _P), ("bias_dtype", _I),
+                ("lr", ctypes.POINTER(_LowRankC)), ("N", _I64), ("Y", _P), ("y_kind", _I)]
+
 # name -> (restype, argtypes), mirroring include/w4.h
 EXPORTS = {
     "w4_pack_weights": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P]),
     "w4_rotate_quant_act": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P]),
     "w4_linear_cached_rot": (_I, [_P, _P, _P, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
                                   _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "w4_linear_cached_rot_multi": (_I, [_P, _P, _P, _I, _I64, _I64, _I, ctypes.POINTER(_LinearOutC), _P, _SZ,
+                                        _P]),
     "w4_linear": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
                        _I64, _P, _I, _P, _SZ, _P]),
     "w4_linear_noalloc": (_I, [_P, _I, _I64, _I64, _I, _I, _P, _P, _P, _P, _I, ctypes.POINTER(_LowRankC),
@@ -355,6 +362,84 @@ def w4_linear_cached_rot(q, tok_scale, tok_rowsum, act_bits: int, packed, row_sc
     if out is not None:
         increment_version(out)  # the library wrote it through a raw pointer
     return Y
+
+
+@dataclass
+class LinearOut:
+    """One linear of ``w4_linear_cached_rot_multi``: packed weights [N, K/2] with their row
+    scales (and zero points), optional bias [N] and low-rank branch (t given), and the output
+    (a new tensor unless ``out`` is given)."""
+    packed: torch.Tensor
+    row_scale: torch.Tensor
+    zp: Optional[torch.Tensor] = None
+    bias: Optional[torch.Tensor] = None
+    lowrank: Optional[LowRank] = None
+    out_i32: bool = False
+    out: Optional[torch.Tensor] = None
+
+
+MULTI_MAX = 8
+
+
+def w4_linear_cached_rot_multi(q, tok_scale, tok_rowsum, act_bits: int, outs, ws=None):
+    """Several linears on the same codes from ``w4_rotate_quant_act`` (consecutive compatible
+    pairs run as one launch for M > 64).  Returns the list of outputs Y_i [M, N_i]."""
+    lib = load_library()
+    if act_bits not in (4, 8):
+        raise ValueError("act_bits must be 4 or 8, got %r" % (act_bits,))
+    outs = list(outs)
+    if not 1 <= len(outs) <= MULTI_MAX:
+        raise ValueError("outs must hold 1..%d linears, got %d" % (MULTI_MAX, len(outs)))
+    K = 2 * _matrix(outs[0].packed, "outs[0].packed")[1]
+    M = _matrix(q, "q")[0]
+    _shape(q, "q", (M, K) if act_bits == 8 else (M, K // 2))
+    _shape(tok_scale, "tok_scale", (M,))
+    _shape(tok_rowsum, "tok_rowsum", (M,))
+    for i, o in enumerate(outs):
+        N, Kh = _matrix(o.packed, "outs[%d].packed" % i)
+        if 2 * Kh != K:
+            raise ValueError("outs[%d].packed has K=%d, expected %d" % (i, 2 * Kh, K))
+        _check_weights(o.packed, o.row_scale, o.zp, o.bias, N, K)
+        if o.lowrank is not None and not o.out_i32:
+            if o.lowrank.t is None:
+                raise ValueError("outs[%d].lowrank must give t" % i)
+            o.lowrank.check(M, N, K, need_t=True)
+        if o.out is not None:
+            _shape(o.out, "outs[%d].out" % i, (M, N))
+    _dev(q, "q", (torch.int8,) if act_bits == 8 else (torch.uint8,))
+    _dev(tok_scale, "tok_scale", (torch.float32,))
+    _dev(tok_rowsum, "tok_rowsum", (torch.int32,))
+    arr = (_LinearOutC * len(outs))()
+    keep, Ys = [], []
+    for i, o in enumerate(outs):
+        _dev(o.packed, "packed", (torch.uint8,))
+        _dev(o.row_scale, "row_scale", (torch.float32,))
+        _opt(o.zp, "zp", (torch.uint8,))
+        _opt(o.bias, "bias", (torch.float32, torch.bfloat16))
+        N = o.packed.shape[0]
+        Y = _y(M, N, o.out_i32, o.packed.device, o.out)
+        Ys.append(Y)
+        c = arr[i]
+        c.packed, c.row_scale = o.packed.data_ptr(), o.row_scale.data_ptr()
+        c.zp = o.zp.data_ptr() if o.zp is not None else None
+        c.bias = o.bias.data_ptr() if o.bias is not None else None
+        c.bias_dtype = _fdtype(o.bias) if o.bias is not None else W4_BF16
+        if o.lowrank is not None and not o.out_i32:
+            lrc = o.lowrank.as_c()
+            keep.append(lrc)
+            c.lr = ctypes.pointer(lrc)
+        c.N, c.Y = N, Y.data_ptr()
+        c.y_kind = W4_OUT_I32 if o.out_i32 else W4_OUT_BF16
+    need = max(w4_workspace_bytes(M, o.packed.shape[0], K, act_bits, 0) for o in outs)
+    ws = _ws(need, q.device, ws)
+    _check(lib.w4_linear_cached_rot_multi(
+        q.data_ptr(), tok_scale.data_ptr(), tok_rowsum.data_ptr(), act_bits, M, K, len(outs), arr,
+        ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+        _stream(q.device)))
+    for o in outs:
+        if o.out is not None:
+            increment_version(o.out)  # the library wrote it through a raw pointer
+    return Ys
 
 
 def w4_linear(X, g: int, act_bits: int, packed, row_scale, zp=None, bias=None,

@@ -276,8 +276,18 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
     tn = first_n + in % gn;
 }
 
+// One or two linears launched as one grid: tile ids [0, n0) are the first's, the rest the
+// second's.  Two linears that read the same activation codes (same M, K and code width, the
+// same weight mode and epilogue form) fill the compute units together, where each alone would
+// leave its last round partly idle.
+struct GemmPair {
+    LinearArgs p[2];
+    int tiles_m[2], tiles_n[2];
+    int n0;
+};
+
 template <int ABITS, bool ASYM, bool KTAIL, int EPI>
-__global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, int tiles_n, int l2_dma, TileRange tr) {
+__global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, TileRange tr) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
     const int tid = threadIdx.x;
@@ -296,8 +306,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm(LinearArgs p, int tiles_m, in
         if (tr.count % 8 == 0) tile = (blockIdx.x % 8) * (tr.count / 8) + blockIdx.x / 8;
         tile += tr.base;
     }
+    const int pi = tile >= gp.n0 ? 1 : 0;
+    const LinearArgs &p = gp.p[pi];
     int tm, tn;
-    tile_coords(tile, tiles_m, tiles_n, tm, tn);
+    tile_coords(tile - pi * gp.n0, gp.tiles_m[pi], gp.tiles_n[pi], tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t K = p.K;
     // stages of this workgroup (the last holds 64 valid k when KTAIL); a K range of a split
@@ -895,8 +907,25 @@ TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
     return pl;
 }
 
+GemmPair single(const LinearArgs &a) {
+    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
+    return GemmPair{{a, a}, {tm, tm}, {tn, tn}, tm * tn};
+}
+
+bool l2_rows_aligned(const LinearArgs &a) { return a.N % 8 == 0 && ((uintptr_t)a.lr_l2 & 15) == 0; }
+
+// The epilogue form of a linear (the k_gemm instantiation its tiles need)
+int epi_kind(const LinearArgs &a) {
+    if (a.y_i32) return kEpiI32;
+    if (!a.lr_t) return kEpiBf16;
+    const bool staged = l2_rows_aligned(a) && a.lr_r % 4 == 0 && a.lr_ldt % 4 == 0 && ((uintptr_t)a.lr_t & 15) == 0;
+    if (staged && a.lr_r <= 16) return kEpiLowRank16;
+    if (staged && a.lr_r <= 32) return kEpiLowRank32;
+    return kEpiLowRank;
+}
+
 template <int ABITS, bool ASYM, bool KTAIL, int EPI>
-hipError_t launch_t(const LinearArgs &a, const TileRange &tr, unsigned grid, hipStream_t st) {
+hipError_t launch_t(const GemmPair &gp, const TileRange &tr, unsigned grid, hipStream_t st) {
     // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
     // 24 * r 16-byte chunks, at most 24 KB for r <= 64), plus the staged t and l2T where they
     // do not fit in free ring slots
@@ -906,26 +935,24 @@ hipError_t launch_t(const LinearArgs &a, const TileRange &tr, unsigned grid, hip
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL, EPI>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)maxlds);
     if (attr != hipSuccess) return attr;
-    const int l2_dma = a.N % 8 == 0 && ((uintptr_t)a.lr_l2 & 15) == 0;  // 16-byte aligned l2 rows
-    const size_t lds = epi_lr_lds(EPI) ? maxlds
-                       : base + (epi_lr(EPI) ? (size_t)((24 * a.lr_r + 63) / 64) * 1024 : 0);
-    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, a, tm, tn, l2_dma, tr);
+    const LinearArgs &a = gp.p[0], &b = gp.p[1];
+    const int l2_dma = l2_rows_aligned(a) && l2_rows_aligned(b);
+    const int rmax = std::max(a.lr_r, b.lr_r);
+    const size_t lds = epi_lr_lds(EPI) ? maxlds : base + (epi_lr(EPI) ? (size_t)((24 * rmax + 63) / 64) * 1024 : 0);
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, gp, l2_dma, tr);
     return hipGetLastError();
 }
 
 template <int ABITS, bool ASYM, bool KTAIL>
-hipError_t launch_epi(const LinearArgs &a, const TileRange &tr, hipStream_t st) {
+hipError_t launch_epi(const GemmPair &gp, const TileRange &tr, hipStream_t st) {
     const unsigned grid = (unsigned)tr.count;
-    if (a.y_i32) return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(a, tr, grid, st);
-    if (a.lr_t) {
-        const bool staged = a.N % 8 == 0 && ((uintptr_t)a.lr_l2 & 15) == 0 && a.lr_r % 4 == 0 && a.lr_ldt % 4 == 0 &&
-                            ((uintptr_t)a.lr_t & 15) == 0;
-        if (staged && a.lr_r <= 16) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(a, tr, grid, st);
-        if (staged && a.lr_r <= 32) return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(a, tr, grid, st);
-        return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(a, tr, grid, st);
+    switch (epi_kind(gp.p[0])) {
+        case kEpiI32: return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(gp, tr, grid, st);
+        case kEpiLowRank16: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(gp, tr, grid, st);
+        case kEpiLowRank32: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(gp, tr, grid, st);
+        case kEpiLowRank: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(gp, tr, grid, st);
+        default: return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(gp, tr, grid, st);
     }
-    return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(a, tr, grid, st);
 }
 
 template <int ABITS, bool ASYM>
@@ -934,18 +961,29 @@ hipError_t launch_k(const LinearArgs &a, void *ws, size_t ws_bytes, hipStream_t 
     const int tiles = pl.tmain + pl.ttail;
     const size_t need = (size_t)pl.ttail * pl.S * BM * BN * sizeof(int32_t);
     const TileRange all{0, tiles, 1, nullptr};
-    if (a.K % BK) return launch_epi<ABITS, ASYM, true>(a, all, st);
-    if (pl.S < 2 || !ws || ws_bytes < need) return launch_epi<ABITS, ASYM, false>(a, all, st);
+    const GemmPair gp = single(a);
+    if (a.K % BK) return launch_epi<ABITS, ASYM, true>(gp, all, st);
+    if (pl.S < 2 || !ws || ws_bytes < need) return launch_epi<ABITS, ASYM, false>(gp, all, st);
     // whole rounds, then the tail's K ranges, then their sum and epilogue
-    hipError_t e = launch_epi<ABITS, ASYM, false>(a, TileRange{0, pl.tmain, 1, nullptr}, st);
+    hipError_t e = launch_epi<ABITS, ASYM, false>(gp, TileRange{0, pl.tmain, 1, nullptr}, st);
     if (e != hipSuccess) return e;
     const TileRange tail{pl.tmain, pl.ttail, pl.S, static_cast<int32_t *>(ws)};
-    e = launch_t<ABITS, ASYM, false, kEpiPartial>(a, tail, (unsigned)(pl.ttail * pl.S), st);
+    e = launch_t<ABITS, ASYM, false, kEpiPartial>(gp, tail, (unsigned)(pl.ttail * pl.S), st);
     if (e != hipSuccess) return e;
-    const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
     hipLaunchKernelGGL((k_gemm_tail<ABITS, ASYM>), dim3((unsigned)(pl.ttail * (BM * BN / 4 / 256))), dim3(256), 0, st,
-                       a, tm, tn, tail);
+                       a, gp.tiles_m[0], gp.tiles_n[0], tail);
     return hipGetLastError();
+}
+
+template <int ABITS, bool ASYM>
+hipError_t launch_pair_t(const LinearArgs &a, const LinearArgs &b, hipStream_t st) {
+    GemmPair gp = single(a);
+    const GemmPair gb = single(b);
+    gp.p[1] = b;
+    gp.tiles_m[1] = gb.tiles_m[0];
+    gp.tiles_n[1] = gb.tiles_n[0];
+    const TileRange all{0, gp.n0 + gb.n0, 1, nullptr};
+    return a.K % BK ? launch_epi<ABITS, ASYM, true>(gp, all, st) : launch_epi<ABITS, ASYM, false>(gp, all, st);
 }
 
 }  // namespace
@@ -954,6 +992,19 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 64 || N <= 0 || K <= 0) return 0;
     const TailPlan pl = tail_plan(M, N, K);
     return pl.S > 1 ? (size_t)pl.ttail * pl.S * BM * BN * sizeof(int32_t) : 0;
+}
+
+bool gemm_pairable(const LinearArgs &a, const LinearArgs &b) {
+    if (a.M <= 64 || a.M != b.M || a.K != b.K || !a.zp != !b.zp || a.y_i32 != b.y_i32) return false;
+    if (epi_kind(a) != epi_kind(b)) return false;
+    const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN + (b.N + BN - 1) / BN);
+    return tiles < ((int64_t)1 << 31);
+}
+
+hipError_t launch_gemm_pair(const LinearArgs &a, const LinearArgs &b, int act_bits, hipStream_t st) {
+    if (!gemm_pairable(a, b)) return hipErrorInvalidValue;
+    if (act_bits == 8) return a.zp ? launch_pair_t<8, true>(a, b, st) : launch_pair_t<8, false>(a, b, st);
+    return a.zp ? launch_pair_t<4, true>(a, b, st) : launch_pair_t<4, false>(a, b, st);
 }
 
 hipError_t launch_gemm(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st) {

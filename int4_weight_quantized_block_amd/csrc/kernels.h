@@ -49,6 +49,11 @@ struct LinearArgs {
 // fill whole rounds of the compute units) the last partial round is split along K.
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const LinearArgs &a, int act_bits, void *ws, size_t ws_bytes, hipStream_t st);
+// Two large-M linears on the same activation codes as one launch (no K split), when they have
+// the same M > 64, K, weight mode, output kind and epilogue form (gemm_pairable); each output
+// equals launch_gemm's without a workspace bit for bit.  hipErrorInvalidValue otherwise.
+bool gemm_pairable(const LinearArgs &a, const LinearArgs &b);
+hipError_t launch_gemm_pair(const LinearArgs &a, const LinearArgs &b, int act_bits, hipStream_t st);
 // Small-M path (M <= 64).  With a workspace of gemv_workspace_bytes() bytes (0 when none is
 // needed) the K-split kernel runs; without one, the LDS-ring kernel.
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K, int act_bits);

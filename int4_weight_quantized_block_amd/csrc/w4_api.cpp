@@ -328,6 +328,83 @@ int w4_linear_cached_rot(const void *q, const float *tok_scale, const int32_t *t
                        Y, y_kind, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+// The LinearArgs of one output of w4_linear_cached_rot_multi, after the checks linear_impl
+// makes (a low-rank branch must supply t).
+static int multi_args(const char *fn, int i, const void *q, const float *tok_scale, const int32_t *tok_rowsum,
+                      int act_bits, int64_t M, int64_t K, const w4_linear_out &o, w4::LinearArgs &a) {
+    if (int e = check_linear_shape(fn, M, o.N, K, act_bits)) return e;
+    if (o.y_kind != W4_OUT_BF16 && o.y_kind != W4_OUT_I32)
+        return fail(W4_ERR_INVALID_ARG, "%s: outs[%d].y_kind=%d", fn, i, o.y_kind);
+    if (o.bias && o.bias_dtype != W4_F32 && o.bias_dtype != W4_BF16)
+        return fail(W4_ERR_INVALID_ARG, "%s: outs[%d].bias_dtype=%d", fn, i, o.bias_dtype);
+    const uint8_t *packed = o.packed, *zp = o.zp;
+    const float *row_scale = o.row_scale;
+    const void *bias = o.bias, *Y = o.Y;
+    W4_CHECK_PTR(q);
+    W4_CHECK_PTR(tok_scale);
+    W4_CHECK_PTR(tok_rowsum);
+    W4_CHECK_PTR(packed);
+    W4_CHECK_PTR(row_scale);
+    W4_CHECK_OPT_PTR(zp);
+    W4_CHECK_OPT_PTR(bias);
+    W4_CHECK_PTR(Y);
+    a = w4::LinearArgs{};
+    const w4_lowrank *lr = o.lr;
+    if (lr && o.y_kind == W4_OUT_BF16) {
+        if (lr->r < 1 || lr->r > 64) return fail(W4_ERR_UNSUPPORTED, "%s: outs[%d] lowrank r=%d", fn, i, lr->r);
+        if (!lr->l2 || !lr->t) return fail(W4_ERR_INVALID_ARG, "%s: outs[%d] lowrank needs t and l2", fn, i);
+        if (!aligned16(lr->l2) || !aligned16(lr->t))
+            return fail(W4_ERR_ALIGN, "%s: outs[%d] lowrank t / l2 not 16-byte aligned", fn, i);
+        if (lr->ldt != 0 && lr->ldt < lr->r)
+            return fail(W4_ERR_INVALID_ARG, "%s: outs[%d] lowrank ldt=%d < r=%d", fn, i, lr->ldt, lr->r);
+        a.lr_t = lr->t;
+        a.lr_l2 = static_cast<const uint16_t *>(lr->l2);
+        a.lr_r = lr->r;
+        a.lr_ldt = lr->ldt ? lr->ldt : lr->r;
+    }
+    a.A = static_cast<const uint8_t *>(q);
+    a.sx = tok_scale;
+    a.rowsum = tok_rowsum;
+    a.B = packed;
+    a.sw = row_scale;
+    a.zp = zp;
+    a.bias = o.y_kind == W4_OUT_BF16 ? bias : nullptr;
+    a.bias_bf16 = o.bias_dtype == W4_BF16;
+    a.Y = o.Y;
+    a.y_i32 = o.y_kind == W4_OUT_I32;
+    a.M = M;
+    a.N = o.N;
+    a.K = K;
+    return W4_OK;
+}
+
+int w4_linear_cached_rot_multi(const void *q, const float *tok_scale, const int32_t *tok_rowsum, int act_bits,
+                               int64_t M, int64_t K, int count, const w4_linear_out *outs, void *ws,
+                               size_t ws_bytes, void *stream) {
+    const char *fn = "w4_linear_cached_rot_multi";
+    if (count < 1 || count > W4_MULTI_MAX) return fail(W4_ERR_INVALID_ARG, "%s: count=%d (1..%d)", fn, count, W4_MULTI_MAX);
+    if (!outs) return fail(W4_ERR_INVALID_ARG, "%s: outs is NULL", fn);
+    if (ws && !aligned16(ws)) return fail(W4_ERR_ALIGN, "%s: ws not 16-byte aligned", fn);
+    w4::LinearArgs args[W4_MULTI_MAX];
+    for (int i = 0; i < count; ++i)
+        if (int e = multi_args(fn, i, q, tok_scale, tok_rowsum, act_bits, M, K, outs[i], args[i])) return e;
+    if (M == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < count;) {
+        if (i + 1 < count && w4::gemm_pairable(args[i], args[i + 1])) {
+            if (int e = hip_status(w4::launch_gemm_pair(args[i], args[i + 1], act_bits, st), fn)) return e;
+            i += 2;
+            continue;
+        }
+        const w4::LinearArgs &a = args[i];
+        const hipError_t e = M <= 64 ? w4::launch_gemv(a, act_bits, ws, ws ? ws_bytes : 0, st)
+                                     : w4::launch_gemm(a, act_bits, ws, ws ? ws_bytes : 0, st);
+        if (int r = hip_status(e, fn)) return r;
+        ++i;
+    }
+    return ok();
+}
+
 // The whole layer: rotate-quantize into the front of ws, then the GEMM half.  The codes,
 // token scales, row sums and (when computed here) the low-rank t must fit ws; the K-split
 // partial sums take whatever room is left (with less, the kernels do not split K).

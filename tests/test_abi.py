@@ -132,6 +132,44 @@ def test_linear_cached_rot_validation(lib):
     assert cached(lib, M=0) == w4.W4_OK
 
 
+def test_linear_cached_rot_multi_validation(lib):
+    """Every output is checked before anything is launched; a low-rank branch must give t."""
+    def outs(n=2, **kw):
+        arr = (w4._LinearOutC * n)()
+        for i in range(n):
+            o = arr[i]
+            o.packed, o.row_scale, o.zp, o.bias, o.bias_dtype = A, A, None, None, w4.W4_BF16
+            o.N, o.Y, o.y_kind = 64, A, w4.W4_OUT_BF16
+        for k, v in kw.items():
+            setattr(arr[n - 1], k, v)
+        return arr
+
+    def multi(arr, count=None, M=100, K=256, bits=8, q=A):
+        n = len(arr) if count is None else count
+        return lib.w4_linear_cached_rot_multi(q, A, A, bits, M, K, n, arr, None, 0, None)
+
+    assert multi(outs(), count=0) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(9)) == w4.W4_ERR_INVALID_ARG                           # more than W4_MULTI_MAX
+    assert lib.w4_linear_cached_rot_multi(A, A, A, 8, 100, 256, 2, None, None, 0, None) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(), bits=2) == w4.W4_ERR_UNSUPPORTED
+    assert multi(outs(), K=100) == w4.W4_ERR_SHAPE
+    assert multi(outs(N=0)) == w4.W4_ERR_SHAPE                                # the second output
+    assert multi(outs(y_kind=7)) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(zp=U)) == w4.W4_ERR_ALIGN
+    assert multi(outs(Y=None)) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(bias=A, bias_dtype=5)) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(), q=None) == w4.W4_ERR_INVALID_ARG
+    lr = w4._LowRankC(A, A, None, A, 16)                                     # x and l1 but no t
+    assert multi(outs(lr=ctypes.pointer(lr))) == w4.W4_ERR_INVALID_ARG
+    lr = w4._LowRankC(None, None, U, A, 16)
+    assert multi(outs(lr=ctypes.pointer(lr))) == w4.W4_ERR_ALIGN
+    lr = w4._LowRankC(None, None, A, A, 65)
+    assert multi(outs(lr=ctypes.pointer(lr))) == w4.W4_ERR_UNSUPPORTED
+    lr = w4._LowRankC(None, None, A, A, 16, 8)                               # ldt < r
+    assert multi(outs(lr=ctypes.pointer(lr))) == w4.W4_ERR_INVALID_ARG
+    assert multi(outs(), M=0) == w4.W4_OK
+
+
 def test_linear_validation(lib):
     def lin(M=100, K=256, g=64, ws=A, ws_bytes=0, Y=A, x_dtype=w4.W4_BF16):
         return lib.w4_linear(A, x_dtype, M, K, g, 8, A, A, None, None, w4.W4_BF16, None, 64, Y, w4.W4_OUT_BF16,
@@ -337,6 +375,20 @@ def test_binding_rejects_mis_shaped_tensors_before_launch():
     # well-shaped CPU tensors get past the shape checks and stop at the device check
     with pytest.raises(ValueError, match="GPU tensor"):
         w4.w4_linear_cached_rot(**good)
+    # several linears on the same codes: every output is checked against (M, N_i, K)
+    o = lambda **kw: w4.LinearOut(**dict(dict(packed=u8(N, K // 2), row_scale=f32(N)), **kw))
+    codes = dict(q=i8(M, K), tok_scale=f32(M), tok_rowsum=i32(M), act_bits=8)
+    for bad in ([o(), o(packed=u8(N, K))],                  # another K
+                [o(), o(row_scale=f32(N + 1))],
+                [o(bias=_bf(N - 1))],
+                [o(lowrank=w4.LowRank(l2=_bf(r, N), x=_bf(M, K), l1=_bf(r, K)))],   # no t
+                [o(lowrank=w4.LowRank(l2=_bf(r, N), t=f32(M + 1, r)))],
+                [o(out=torch.zeros(M, N - 1, dtype=torch.bfloat16))],
+                [], [o()] * 9):
+        with pytest.raises(ValueError):
+            w4.w4_linear_cached_rot_multi(outs=bad, **codes)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        w4.w4_linear_cached_rot_multi(outs=[o(), o()], **codes)
 
 
 def test_rotation_cache_key_includes_stream(monkeypatch):

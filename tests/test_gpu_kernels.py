@@ -283,6 +283,59 @@ def test_linear_lowrank_ranks(M, N, K, bits, asym, r, tcol):
     assert err <= FROB_TOL
 
 
+@pytest.mark.parametrize("M,K,Ns,bits,asym,ranks,i32", [
+    (600, 1024, (960, 1280), 8, False, (32, 32), False),        # one launch, staged low-rank branches
+    (300, 448, (389, 200, 384), 4, True, (28, 30, 0), False),   # K tail, generic low-rank, ragged N; third alone
+    (520, 512, (384, 392), 8, True, (0, 0), True),              # raw accumulators
+    (300, 512, (384, 256, 512), 8, False, (16, 0, 0), False),   # forms differ: 0 alone, 1 + 2 together
+    (48, 1024, (512, 768), 8, False, (16, 16), False),          # M <= 64: the small-M kernels one by one
+])
+def test_linear_multi_equals_separate(M, K, Ns, bits, asym, ranks, i32):
+    """Several linears on one set of codes: each output equals w4_linear_cached_rot's for the
+    same linear bit for bit (large M, no split tail at these sizes), whether it shares a
+    launch or not; the first case is also checked against the oracle.  The low-rank t of all
+    outputs comes from one rotate-quant pass with the L1 factors stacked."""
+    say("multi M=%d K=%d Ns=%s bits=%d asym=%s ranks=%s i32=%s" % (M, K, Ns, bits, asym, ranks, i32))
+    g = 256 if K % 256 == 0 else 64
+    rg = rng(M + K + sum(Ns))
+    X = act_input(M, K, seed=M + 11 * K)
+    Xd = X.to(DEV)
+    Ws, L1s, L2s, biases = [], [], [], []
+    for N, r in zip(Ns, ranks):
+        Ws.append(torch.from_numpy((rg.standard_normal((N, K)) * 0.02).astype(np.float32)).to(torch.bfloat16))
+        biases.append(torch.from_numpy((rg.standard_normal(N) * 0.01).astype(np.float32)).to(torch.bfloat16))
+        L1s.append(torch.from_numpy((rg.standard_normal((K, r)) * 0.05).astype(np.float32)).to(torch.bfloat16)
+                   if r else None)
+        L2s.append(torch.from_numpy((rg.standard_normal((r, N)) * 0.2).astype(np.float32)).to(torch.bfloat16)
+                   if r else None)
+    stacked = [L1 for L1 in L1s if L1 is not None]
+    if stacked:
+        l1 = torch.cat([L1.t() for L1 in stacked], 0).contiguous().to(DEV)
+        q, sx, rs, t = w4.w4_rotate_quant_act_lowrank(Xd, g, bits, l1)
+    else:
+        q, sx, rs = w4.w4_rotate_quant_act(Xd, g, bits)
+    outs, lows, col = [], [], 0
+    for W, b, r, L2 in zip(Ws, biases, ranks, L2s):
+        packed, sw, zp = w4.w4_pack_weights(W.to(DEV), g, asym)
+        low = w4.LowRank(l2=L2.to(DEV), t=t[:, col:col + r]) if r else None
+        col += r
+        lows.append(low)
+        outs.append(w4.LinearOut(packed=packed, row_scale=sw, zp=zp, bias=b.to(DEV), lowrank=low, out_i32=i32))
+    ys = w4.w4_linear_cached_rot_multi(q, sx, rs, bits, outs)
+    tiny = torch.empty(256, dtype=torch.uint8, device=DEV) if M > 64 else None
+    for i, (o, y) in enumerate(zip(outs, ys)):
+        y1 = w4.w4_linear_cached_rot(q, sx, rs, bits, o.packed, o.row_scale, o.zp, bias=o.bias,
+                                     lowrank=o.lowrank, out_i32=i32, ws=tiny)
+        view = (lambda a: a) if i32 else (lambda a: a.view(torch.int16))
+        assert torch.equal(view(y), view(y1)), "output %d differs from its own call" % i
+    if ranks == (32, 32):
+        for i, (W, b, L1, L2) in enumerate(zip(Ws, biases, L1s, L2s)):
+            ref = oracle.linear(X, W, g, bits, asym, bias=b, L1=L1, L2=L2)
+            err = rel_frob(ys[i], ref["y64"])
+            say("  output %d rel frob %.3e" % (i, err))
+            assert err <= FROB_TOL
+
+
 @pytest.mark.parametrize("M,N,K,bits,asym", [(4608, 3072, 3072, 4, True), (4608, 2880, 2048, 8, False),
                                              (2500, 5996, 1024, 8, True)])
 def test_gemm_split_tail_equals_single_pass(M, N, K, bits, asym):

@@ -43,17 +43,20 @@ def weights_on_gpu(W, g, asym):
     return (packed, s, zp), ref
 
 
-def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag="", codes=None):
+def check_layer(X, W, bias, g, bits, asym, lowrank=None, cache=None, tag="", codes=None, keep=None):
     """Run one linear on the GPU at full size and check it against the oracle on every row.
 
     Checked: the GPU's packed weights and scales; its token scales and activation codes; the
     int32 accumulators of the oracle's own codes (exact, all M x N); the bf16 layer output of
     the GPU's own rotation and packing, as in the timed path (relative Frobenius error over
-    all M x N).  Returns (Y_gpu, oracle y64)."""
+    all M x N).  Returns (Y_gpu, oracle y64); ``keep`` (a dict) receives the GPU's packed
+    weights (packed, scales, zero points)."""
     M, K = X.shape
     N = W.shape[0]
     say("%s: M=%d K=%d N=%d g=%d bits=%d asym=%s" % (tag, M, K, N, g, bits, asym))
     (packed, s_w, zp), pw = weights_on_gpu(W, g, asym)
+    if keep is not None:
+        keep.update(packed=packed, s_w=s_w, zp=zp)
     Xd = X if X.is_cuda else X.to(DEV)
     Xc = X.cpu() if X.is_cuda else X
     if codes is not None:
@@ -137,18 +140,27 @@ def test_double_block_cached_lowrank(b):
     cache = w4.RotationCache()
     l1_x = torch.cat([blk["qkv"]["L1"], blk["up"]["L1"]], dim=0)   # stacked [64, K]
     r = blk["qkv"]["L1"].shape[0]
-    outs = {}
+    outs, kept = {}, {}
     for name, inp, l1, cols in (("qkv", blk["x"], l1_x, slice(0, r)), ("up", blk["x"], l1_x, slice(r, 2 * r)),
                                 ("out", blk["attn"], blk["out"]["L1"], slice(0, r))):
         p = blk[name]
         q, sx, rs, t = cache.get(inp, 256, 8, l1=l1)
         low = w4.LowRank(l2=p["L2"], t=t[:, cols])
-        outs[name], y64 = check_layer(inp, p["W"].cpu(), p["bias"], 256, 8, False,
-                                      lowrank=(p["L1"], p["L2"], low), codes=(q, sx, rs), tag="block%d.%s" % (b, name))
+        kept[name] = {"low": low}
+        outs[name], y64 = check_layer(inp, p["W"].cpu(), p["bias"], 256, 8, False, lowrank=(p["L1"], p["L2"], low),
+                                      codes=(q, sx, rs), tag="block%d.%s" % (b, name), keep=kept[name])
         if name == "up":
             h = oracle.gelu_bf16(oracle.bf16_rne(y64)).to(DEV)   # the down-proj input, all rows
         del y64
-    assert cache.hits == 1 and cache.misses == 2
+    # the timed path's launch: QKV and MLP-up as one grid on the shared codes; each output
+    # equals its own call above bit for bit
+    q, sx, rs, t = cache.get(blk["x"], 256, 8, l1=l1_x)
+    pair = [w4.LinearOut(packed=kept[n]["packed"], row_scale=kept[n]["s_w"], bias=blk[n]["bias"].to(DEV),
+                         lowrank=kept[n]["low"]) for n in ("qkv", "up")]
+    for n, y in zip(("qkv", "up"), w4.w4_linear_cached_rot_multi(q, sx, rs, 8, pair)):
+        assert torch.equal(y.view(torch.int16), outs[n].view(torch.int16)), "block%d.%s: one launch vs own call" % (b, n)
+    del pair, kept
+    assert cache.hits == 2 and cache.misses == 2
     # down-proj input: GELU of the oracle's up-projection output (computed above, all rows);
     p = blk["down"]
     q, sx, rs, t = w4.w4_rotate_quant_act_lowrank(h, 256, 8, p["L1"])
