@@ -286,7 +286,7 @@ struct GemmPair {
     int n0;
 };
 
-template <int ABITS, bool ASYM, bool KTAIL, int EPI>
+template <int ABITS, bool ASYM, bool KTAIL, int EPI, bool PAIR>
 __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, TileRange tr) {
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     using L = Lay<ABITS>;
@@ -306,8 +306,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
         if (tr.count % 8 == 0) tile = (blockIdx.x % 8) * (tr.count / 8) + blockIdx.x / 8;
         tile += tr.base;
     }
-    const int pi = tile >= gp.n0 ? 1 : 0;
-    const LinearArgs &p = gp.p[pi];
+    // (a single linear reads p[0] at fixed offsets: selecting the problem per workgroup
+    // costs registers and time that only a pair needs)
+    const int pi = PAIR && tile >= gp.n0 ? 1 : 0;
+    const LinearArgs &p = gp.p[PAIR ? pi : 0];
     int tm, tn;
     tile_coords(tile - pi * gp.n0, gp.tiles_m[pi], gp.tiles_n[pi], tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
@@ -924,7 +926,7 @@ int epi_kind(const LinearArgs &a) {
     return kEpiLowRank;
 }
 
-template <int ABITS, bool ASYM, bool KTAIL, int EPI>
+template <int ABITS, bool ASYM, bool KTAIL, int EPI, bool PAIR = false>
 hipError_t launch_t(const GemmPair &gp, const TileRange &tr, unsigned grid, hipStream_t st) {
     // LDS: ring + constants, plus the low-rank l2 tile (whole 1 KB direct-load blocks of
     // 24 * r 16-byte chunks, at most 24 KB for r <= 64), plus the staged t and l2T where they
@@ -932,26 +934,26 @@ hipError_t launch_t(const GemmPair &gp, const TileRange &tr, unsigned grid, hipS
     constexpr size_t base = Lay<ABITS>::LDS_BYTES, maxl2 = 24 * 1024;
     constexpr size_t maxlds = epi_lr_lds(EPI) ? (size_t)LrLay<ABITS, epi_lds_k(EPI)>::LDS_TOTAL : base + maxl2;
     static_assert(maxlds <= 160 * 1024, "LDS budget");
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL, EPI>),
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<ABITS, ASYM, KTAIL, EPI, PAIR>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)maxlds);
     if (attr != hipSuccess) return attr;
     const LinearArgs &a = gp.p[0], &b = gp.p[1];
     const int l2_dma = l2_rows_aligned(a) && l2_rows_aligned(b);
     const int rmax = std::max(a.lr_r, b.lr_r);
     const size_t lds = epi_lr_lds(EPI) ? maxlds : base + (epi_lr(EPI) ? (size_t)((24 * rmax + 63) / 64) * 1024 : 0);
-    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI>), dim3(grid), dim3(kThreads), lds, st, gp, l2_dma, tr);
+    hipLaunchKernelGGL((k_gemm<ABITS, ASYM, KTAIL, EPI, PAIR>), dim3(grid), dim3(kThreads), lds, st, gp, l2_dma, tr);
     return hipGetLastError();
 }
 
-template <int ABITS, bool ASYM, bool KTAIL>
+template <int ABITS, bool ASYM, bool KTAIL, bool PAIR = false>
 hipError_t launch_epi(const GemmPair &gp, const TileRange &tr, hipStream_t st) {
     const unsigned grid = (unsigned)tr.count;
     switch (epi_kind(gp.p[0])) {
-        case kEpiI32: return launch_t<ABITS, ASYM, KTAIL, kEpiI32>(gp, tr, grid, st);
-        case kEpiLowRank16: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16>(gp, tr, grid, st);
-        case kEpiLowRank32: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32>(gp, tr, grid, st);
-        case kEpiLowRank: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank>(gp, tr, grid, st);
-        default: return launch_t<ABITS, ASYM, KTAIL, kEpiBf16>(gp, tr, grid, st);
+        case kEpiI32: return launch_t<ABITS, ASYM, KTAIL, kEpiI32, PAIR>(gp, tr, grid, st);
+        case kEpiLowRank16: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank16, PAIR>(gp, tr, grid, st);
+        case kEpiLowRank32: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank32, PAIR>(gp, tr, grid, st);
+        case kEpiLowRank: return launch_t<ABITS, ASYM, KTAIL, kEpiLowRank, PAIR>(gp, tr, grid, st);
+        default: return launch_t<ABITS, ASYM, KTAIL, kEpiBf16, PAIR>(gp, tr, grid, st);
     }
 }
 
@@ -983,7 +985,7 @@ hipError_t launch_pair_t(const LinearArgs &a, const LinearArgs &b, hipStream_t s
     gp.tiles_m[1] = gb.tiles_m[0];
     gp.tiles_n[1] = gb.tiles_n[0];
     const TileRange all{0, gp.n0 + gb.n0, 1, nullptr};
-    return a.K % BK ? launch_epi<ABITS, ASYM, true>(gp, all, st) : launch_epi<ABITS, ASYM, false>(gp, all, st);
+    return a.K % BK ? launch_epi<ABITS, ASYM, true, true>(gp, all, st) : launch_epi<ABITS, ASYM, false, true>(gp, all, st);
 }
 
 }  // namespace
