@@ -189,8 +189,9 @@ int w4_linear_cached_rot_multi(const void *q, const float *tok_scale, const int3
  * w4_linear_cached_rot.  Arguments as above; ws must hold at least
  * w4_workspace_bytes(M, N, K, act_bits, r) + room for the activation codes, i.e.
  * w4_linear_workspace_bytes(M, N, K, act_bits, r_needed).  For one bf16 token (M = 1,
- * K <= 16384, N <= 32 x the compute units, K a multiple of 2048) a single kernel rotates,
- * quantizes and multiplies, the fused ConvRot path of the INT4 README ("Inference / INT4");
+ * N <= 32 x the compute units, K a multiple of 3072 up to 12288 or of 2048 up to 16384) a
+ * single kernel rotates, quantizes and multiplies, the fused ConvRot path of the INT4 README
+ * ("Inference / INT4");
  * Y is the same bit for bit, and the workspace then holds no codes (its contents are
  * scratch either way). */
 int w4_linear(const void *X, int x_dtype, int64_t M, int64_t K, int g, int act_bits,

@@ -381,6 +381,8 @@ def test_gemm_split_tail_equals_single_pass(M, N, K, bits, asym):
     (1, 64, 2048, 256, 8, True, torch.float32, True),        # fused, one stage (fewer than the ring)
     (1, 8192, 4096, 256, 8, True, torch.bfloat16, False),    # fused, 32 rows per workgroup
     (1, 4100, 4096, 256, 8, True, torch.bfloat16, False),    # fused, 32 rows per workgroup, ragged N
+    (1, 700, 3072, 256, 8, True, torch.bfloat16, True),      # fused with 12 waves, one stage, low-rank
+    (1, 2000, 6144, 64, 4, False, None, False),              # fused with 12 waves, 2 stages = the ring
     (1, 12288, 4096, 256, 8, True, torch.bfloat16, False),   # past 32 rows per CU: two launches
     (1, 12300, 2048, 64, 4, True, torch.bfloat16, True),     # two launches, ragged N
     (2, 2048, 4096, 256, 8, True, torch.bfloat16, True),     # two tokens: two launches
@@ -441,6 +443,7 @@ def test_fused_small_m_zero_token(asym):
     (8, 5000, 2048, 256, 8, True),     # ragged N
     (1, 2048, 2048, 256, 8, True),     # fused, one stage
     (1, 4096, 4096, 64, 8, True),      # fused, 2 stages = the ring depth
+    (1, 3000, 3072, 256, 8, True),     # fused with 12 waves, one stage
 ])
 def test_small_m_short_k_constants(M, N, K, g, bits, asym):
     """Small-M kernels whose whole K fits in the stages issued up front: the per-row constants
@@ -617,6 +620,7 @@ def test_pack_weights_exact_ties():
     (520, 4096, 256, 4, False, True),     # W4A4 with the low-rank branch
     (4096, 12288, 256, 8, True, False),   # the text-encoder shape
     (300, 16384, 64, 8, False, False),
+    (700, 3072, 256, 8, True, True),      # 12 waves per workgroup, one stage
 ])
 def test_fused_single_token_matches_oracle(N, K, g, bits, asym, lr):
     """The one-launch path compared with the oracle directly: its int32 accumulators equal the
