@@ -243,6 +243,7 @@ def test_linear_matches_oracle(M, N, K, g, bits, asym, lr, bias_dtype):
     # two (K tail) and three stages, int4 codes with t past the ring, ragged M over three
     # tile rows, and t as a 16-byte aligned column range of a wider tensor
     (270, 256, 128, 8, True, 16, None), (300, 392, 192, 4, True, 12, None), (300, 384, 384, 8, True, 24, None),
+    (100, 256, 64, 8, False, 16, None),
     (300, 200, 320, 4, False, 32, None), (520, 384, 1024, 8, False, 28, None), (300, 384, 512, 8, False, 32, 8),
     (300, 200, 512, 4, True, 16, 4),
     # t starting at float 2 (8-byte aligned): refused with W4_ERR_ALIGN before any launch
