@@ -36,6 +36,12 @@
 //
 // The block -> tile map keeps each XCD (blocks are dealt to the 8 XCDs round-robin) on a
 // compact group of tiles so the A row panels and B column panels it streams stay in its L2.
+//
+// Low-rank branch (stable-diffusion.cpp PR #2010, "Summary"; ComfyUI-INT-Crush README,
+// "Forward Pass" step 6): T . L2 runs in the epilogue on the bf16 matrix cores, from t rows
+// and a transposed l2 tile staged in LDS (r <= 32) or from t read per token block (r <= 64).
+// Two linears that read the same codes can share one launch (GemmPair): the grid holds the
+// tiles of both, so neither leaves its last round of tiles partly idle.
 #include <algorithm>
 #include <type_traits>
 
