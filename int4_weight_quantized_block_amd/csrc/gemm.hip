@@ -556,7 +556,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
     // (8 - z) * 2^SHIFT), read from LDS where they are used: holding all 12 groups in
     // registers through the epilogue made the low-rank form spill, and each reload's vmcnt(0)
     // then also waited for the output stores of the previous token block
-    auto consts = [&](int j, int g, float (&sw)[4], float (&bs)[4], int (&zc)[4]) __attribute__((always_inline)) {
+    auto consts_lds = [&](int j, int g, float (&sw)[4], float (&bs)[4], int (&zc)[4]) __attribute__((always_inline)) {
         const int nl = wn * WTN + j * 32 + 8 * g + 4 * kb;  // feature within the tile
         const float4 sw4 = *reinterpret_cast<const float4 *>(c_sw + nl);
         sw[0] = sw4.x * kUnscale; sw[1] = sw4.y * kUnscale; sw[2] = sw4.z * kUnscale; sw[3] = sw4.w * kUnscale;
@@ -570,6 +570,32 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
             zc[2] = (8 - (int)z4.z) << SHIFT; zc[3] = (8 - (int)z4.w) << SHIFT;
         } else {
             zc[0] = zc[1] = zc[2] = zc[3] = 0;
+        }
+    };
+    // Forms with registers to spare (bf16 without the low-rank branch, raw int32, and the
+    // symmetric low-rank form with staged operands) read all 12 groups once, with one wait,
+    // before the first token block: per-use reads put an LDS round trip, and its wait behind
+    // the staging traffic, into every group of every block (4096 x 3072 -> 3072: 38 us per
+    // launch with the constants held, 47 us without).  The other low-rank forms would spill.
+    constexpr bool HOLD = !epi_lr(EPI) || (epi_lr_lds(EPI) && !ASYM);
+    float swv[HOLD ? FN : 1][4][4], bsv[HOLD ? FN : 1][4][4];
+    int zcv[HOLD ? FN : 1][4][4];
+    if constexpr (HOLD) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) consts_lds(j, g, swv[j][g], bsv[j][g], zcv[j][g]);
+    }
+    auto consts = [&](int j, int g, float (&sw)[4], float (&bs)[4], int (&zc)[4]) __attribute__((always_inline)) {
+        if constexpr (HOLD) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sw[r] = swv[j][g][r];
+                bs[r] = bsv[j][g][r];
+                zc[r] = zcv[j][g][r];
+            }
+        } else {
+            consts_lds(j, g, sw, bs, zc);
         }
     };
     if constexpr (EPI == kEpiI32) {
