@@ -625,10 +625,39 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
     // stores of a staged block: 32 rows x 12 chunks of 16 bytes; LDS operations of one wave
     // complete in order, so the reads see this block's writes and the next block's writes
     // follow these reads
-    auto store_block = [&](int64_t mrow0) __attribute__((always_inline)) {
-        constexpr int CPR = WTN * 2 / 16;
+    // In a single linear, tiles inside the output with 16-byte aligned rows take a path without
+    // per-store checks: each lane's 6 chunk offsets (row * N + column, 32-bit) are computed once
+    // per tile (the paired launch keeps the checked path: its low-rank form has no registers to
+    // spare for the offsets).
+    constexpr int CPR = WTN * 2 / 16;      // 16-byte chunks per staged row
+    constexpr int NCH = 32 * CPR / 64;     // stores per lane and block
+    const bool tile_in = !PAIR && full_n && m0 + BM <= p.M && n0 + BN <= p.N && p.N < (1 << 26);
+    uint32_t soff[PAIR ? 1 : NCH];
+    if constexpr (!PAIR) {
 #pragma unroll
-        for (int k = 0; k < 32 * CPR / 64; ++k) {
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            soff[k] = (uint32_t)(c / CPR) * (uint32_t)p.N + (uint32_t)(c % CPR) * 8;
+        }
+    }
+    auto store_block = [&](int64_t mrow0) __attribute__((always_inline)) {
+        if (tile_in) {
+            uint16_t *yb = Y + mrow0 * p.N + n0 + wn * WTN;
+            // all of the block's staged chunks are read before the first store, so the stores
+            // wait for one LDS round trip instead of one each
+            u32x4 v[NCH];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                const int c = lane + 64 * k;
+                v[k] = *reinterpret_cast<const u32x4 *>(stg + (c / CPR) * SROW + (c % CPR) * 16);
+            }
+#pragma unroll
+            for (int k = 0; k < NCH; ++k)  // streaming stores: the output is not read again here
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4 *>(yb + soff[PAIR ? 0 : k]));
+            return;
+        }
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
             const int c = lane + 64 * k;
             const int row = c / CPR, ch = c % CPR;
             const int64_t m = mrow0 + row, n = n0 + wn * WTN + ch * 8;
@@ -809,7 +838,8 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int a = acc[j][i][4 * g + r] + (ASYM ? zc[r] * rsv[i] : 0);
-                    y[r] = fmaf((float)a, sxv[i] * sw[r], bs[r]) + lacc[4 * g + r];
+                    y[r] = fmaf((float)a, sxv[i] * sw[r], bs[r]);
+                    if constexpr (epi_lr(EPI)) y[r] += lacc[4 * g + r];
                 }
                 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
                 typedef float fl2 __attribute__((ext_vector_type(2)));
