@@ -576,8 +576,10 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
     // symmetric low-rank form with staged operands) read all 12 groups once, with one wait,
     // before the first token block: per-use reads put an LDS round trip, and its wait behind
     // the staging traffic, into every group of every block (4096 x 3072 -> 3072: 38 us per
-    // launch with the constants held, 47 us without).  The other low-rank forms would spill.
-    constexpr bool HOLD = !epi_lr(EPI) || (epi_lr_lds(EPI) && !ASYM);
+    // launch with the constants held, 47 us without).  The other low-rank forms would spill, and
+    // the paired launch's low-rank form spends those registers on the check-free store path
+    // below instead (twenty double blocks: 15.2 -> 15.0 ms).
+    constexpr bool HOLD = !epi_lr(EPI) || (epi_lr_lds(EPI) && !ASYM && !PAIR);
     float swv[HOLD ? FN : 1][4][4], bsv[HOLD ? FN : 1][4][4];
     int zcv[HOLD ? FN : 1][4][4];
     if constexpr (HOLD) {
@@ -622,16 +624,12 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
     uint8_t *stg = smem + ((nk + 1) % STAGES) * L::STAGE + wave * 32 * SROW;
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
     const bool full_n = (p.N & 7) == 0;  // 16-byte aligned rows
-    // stores of a staged block: 32 rows x 12 chunks of 16 bytes; LDS operations of one wave
-    // complete in order, so the reads see this block's writes and the next block's writes
-    // follow these reads
-    // In a single linear, tiles inside the output with 16-byte aligned rows take a path without
-    // per-store checks: each lane's 6 chunk offsets (row * N + column, 32-bit) are computed once
-    // per tile (the paired launch keeps the checked path: its low-rank form has no registers to
-    // spare for the offsets).
+    // Tiles inside the output with 16-byte aligned rows take a path without per-store checks:
+    // each lane's 6 chunk offsets (row * N + column, 32-bit) are computed once per tile in a
+    // single linear, and at each store in the paired launch (fewer registers).
     constexpr int CPR = WTN * 2 / 16;      // 16-byte chunks per staged row
     constexpr int NCH = 32 * CPR / 64;     // stores per lane and block
-    const bool tile_in = !PAIR && full_n && m0 + BM <= p.M && n0 + BN <= p.N && p.N < (1 << 26);
+    const bool tile_in = full_n && m0 + BM <= p.M && n0 + BN <= p.N && p.N < (1 << 26);
     uint32_t soff[PAIR ? 1 : NCH];
     if constexpr (!PAIR) {
 #pragma unroll
@@ -640,6 +638,9 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
             soff[k] = (uint32_t)(c / CPR) * (uint32_t)p.N + (uint32_t)(c % CPR) * 8;
         }
     }
+    // stores of a staged block: 32 rows x 12 chunks of 16 bytes; LDS operations of one wave
+    // complete in order, so the reads see this block's writes and the next block's writes
+    // follow these reads
     auto store_block = [&](int64_t mrow0) __attribute__((always_inline)) {
         if (tile_in) {
             uint16_t *yb = Y + mrow0 * p.N + n0 + wn * WTN;
@@ -652,8 +653,11 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmPair gp, int l2_dma, Tile
                 v[k] = *reinterpret_cast<const u32x4 *>(stg + (c / CPR) * SROW + (c % CPR) * 16);
             }
 #pragma unroll
-            for (int k = 0; k < NCH; ++k)  // streaming stores: the output is not read again here
-                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4 *>(yb + soff[PAIR ? 0 : k]));
+            for (int k = 0; k < NCH; ++k) {  // streaming stores: the output is not read again here
+                const int c = lane + 64 * k;
+                const uint32_t off = PAIR ? (uint32_t)(c / CPR) * (uint32_t)p.N + (uint32_t)(c % CPR) * 8 : soff[PAIR ? 0 : k];
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4 *>(yb + off));
+            }
             return;
         }
 #pragma unroll
