@@ -425,3 +425,13 @@ def test_out_buffer_writes_bump_the_version(monkeypatch):
     w4.w4_linear_cached_rot(torch.zeros(M, K, dtype=torch.int8), torch.zeros(M), torch.zeros(M, dtype=torch.int32),
                             8, torch.zeros(N, K // 2, dtype=torch.uint8), torch.zeros(N), out=out)
     assert out._version == v0 + 2
+
+
+def test_phase_probe_anchors_occur_once():
+    # the GEMM phase probe instruments a copy of gemm.hip at fixed anchor strings; each must
+    # occur exactly once, or the probe would stamp the wrong place (checked on the host; the
+    # probe itself is built and run only for measurement)
+    from int4_weight_quantized_block_amd import phase_probe
+    src = open(os.path.join(ROOT, "int4_weight_quantized_block_amd", "csrc", "gemm.hip")).read()
+    for anchor, _ in phase_probe._EDITS:
+        assert src.count(anchor) == 1, anchor
