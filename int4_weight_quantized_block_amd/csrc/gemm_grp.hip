@@ -182,6 +182,9 @@ __device__ __forceinline__ bf8 bf16_codes(uint32_t d) {
     return r;
 }
 
+// Byte offset of the epilogue's bf16 staging rows: past the staged l2 rows (r x BN bf16).
+__host__ __device__ constexpr int grp_stg_off(int r, int bn) { return (2 * r * bn + 15) / 16 * 16; }
+
 // Two waves per SIMD (at most 256 registers per lane): one wave's group scaling and operand
 // unpacking then runs beside the other's MFMAs.
 template <int AT, int FM, int FN, int WM, int WN, int STAGES, int EPI>
@@ -380,8 +383,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
     // bf16 output: stage the tile's l2 rows in LDS (the ring is free once every wave is past it)
     const int r = p.lr_t ? p.lr_r : 0;
     uint16_t *l2s = reinterpret_cast<uint16_t *>(smem);
+    __syncthreads();  // every wave is past the ring
     if (r) {
-        __syncthreads();
         for (int e = tid; e < r * C::BN; e += 256) {
             const int q = e / C::BN, nl = e % C::BN;
             const int64_t n = min<int64_t>(n0 + nl, p.N - 1);
@@ -389,11 +392,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
         }
         __syncthreads();
     }
+    // Each wave converts 32 tokens at a time into its own bf16 staging rows (past the l2 rows)
+    // and stores them as 16-byte row chunks: stores of 8-byte pieces straight from the
+    // accumulator layout (one per token row and lane half) cost far more.
+    constexpr int WF = 32 * FN;                  // features per wave
+    constexpr int SROW = 2 * WF + 16;            // staged row bytes (padded)
+    constexpr int CPR = 2 * WF / 16;             // 16-byte chunks per row
+    uint8_t *stg = smem + grp_stg_off(r, C::BN) + wave * 32 * SROW;
+    const bool tile_in = m0 + C::BM <= p.M && n0 + C::BN <= p.N && (p.N & 7) == 0;
     uint16_t *Y = reinterpret_cast<uint16_t *>(p.Y);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * FM * 32 + i * 32 + l32;
-        if (m >= p.M) continue;
+        const int64_t m = min<int64_t>(m0 + wm * FM * 32 + i * 32 + l32, p.M - 1);  // rows past M: staged, not stored
         const float xs = INT ? p.sx[m] * UNSCALE : UNSCALE;
         const float *tr = r ? p.lr_t + m * p.lr_ldt : nullptr;
 #pragma unroll
@@ -420,16 +430,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k
                                             : reinterpret_cast<const float *>(p.bias)[nb];
                     }
                 }
-                uint16_t *yr = Y + m * p.N;
-                if (n + 3 < p.N && (p.N & 3) == 0) {
-                    *reinterpret_cast<uint2 *>(yr + n) =
-                        make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16), f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (n + u < p.N) yr[n + u] = (uint16_t)f32_to_bf16(y[u]);
-                }
+                *reinterpret_cast<uint2 *>(stg + l32 * SROW + (j * 32 + 8 * g + 4 * h) * 2) =
+                    make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16), f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
             }
+        // the block's rows: LDS operations of one wave complete in order, so these reads see
+        // the writes above and the next block's writes follow them
+        const int64_t mrow0 = m0 + wm * FM * 32 + i * 32;
+        const int64_t ncol0 = n0 + wn * WF;
+        constexpr int NCH = 32 * CPR / 64;
+        uint4 v[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            v[k] = *reinterpret_cast<const uint4 *>(stg + (c / CPR) * SROW + (c % CPR) * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+            const int c = lane + 64 * k;
+            const int64_t mm = mrow0 + c / CPR, nn = ncol0 + (c % CPR) * 8;
+            if (tile_in) {
+                *reinterpret_cast<uint4 *>(Y + mm * p.N + nn) = v[k];
+            } else if (mm < p.M) {
+                const uint16_t *hv = reinterpret_cast<const uint16_t *>(&v[k]);
+                for (int u = 0; u < 8; ++u)
+                    if (nn + u < p.N) Y[mm * p.N + nn + u] = hv[u];
+            }
+        }
     }
 }
 
@@ -464,7 +490,8 @@ __global__ void __launch_bounds__(256) k_grp_reduce(GrpArgs p) {
 template <int AT, int FM, int FN, int WM, int WN, int STAGES, int EPI>
 hipError_t launch_cfg(const GrpArgs &a, hipStream_t st) {
     using C = Cfg<AT, FM, FN, WM, WN, STAGES>;
-    const size_t lds = std::max<size_t>(C::LDS, (size_t)2 * a.lr_r * C::BN);
+    // the ring, or (bf16 output) the staged l2 rows and the four waves' staging rows
+    const size_t lds = std::max<size_t>(C::LDS, (size_t)grp_stg_off(a.lr_r, C::BN) + 4 * 32 * (64 * FN + 16));
     auto kern = k_gemm_grp<AT, FM, FN, WM, WN, STAGES, EPI>;
     if (lds > 65536) {
         static const hipError_t attr =
