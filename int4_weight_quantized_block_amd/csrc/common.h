@@ -50,6 +50,34 @@ __device__ __forceinline__ double dpp_f64(double x) {
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kRowMirror = 0x140;      // lane l of a 16-lane row takes lane 15 - l
+constexpr int kRowHalfMirror = 0x141;  // lane l of an 8-lane half row takes lane 7 - l
+
+// Wave-wide max of non-negative doubles and sum of ints, in registers: the two quad exchanges
+// and the half-row and row mirrors leave each 16-lane row's result in every lane of the row
+// (every step pairs lanes whose partial results cover disjoint lane sets), and four readlanes
+// combine the rows.  Every lane of the wave must be active.  A max is exact in any order and
+// an int sum is exact, so the result equals the butterfly over __shfl_xor, without its chain
+// of LDS round trips.
+__device__ __forceinline__ double wave_max_f64(double x) {
+    x = fmax(x, dpp_f64<kQuadXor1>(x));
+    x = fmax(x, dpp_f64<kQuadXor2>(x));
+    x = fmax(x, dpp_f64<kRowHalfMirror>(x));
+    x = fmax(x, dpp_f64<kRowMirror>(x));
+    const int lo = __double2loint(x), hi = __double2hiint(x);
+    double r = __hiloint2double(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(lo, 0));
+    r = fmax(r, __hiloint2double(__builtin_amdgcn_readlane(hi, 16), __builtin_amdgcn_readlane(lo, 16)));
+    r = fmax(r, __hiloint2double(__builtin_amdgcn_readlane(hi, 32), __builtin_amdgcn_readlane(lo, 32)));
+    return fmax(r, __hiloint2double(__builtin_amdgcn_readlane(hi, 48), __builtin_amdgcn_readlane(lo, 48)));
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+    x += __builtin_amdgcn_mov_dpp(x, kQuadXor1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_mov_dpp(x, kQuadXor2, 0xF, 0xF, false);
+    x += __builtin_amdgcn_mov_dpp(x, kRowHalfMirror, 0xF, 0xF, false);
+    x += __builtin_amdgcn_mov_dpp(x, kRowMirror, 0xF, 0xF, false);
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+           __builtin_amdgcn_readlane(x, 48);
+}
 
 // Lane exchange for a double through ds_swizzle (bit-mask mode), for lanes 4 and 8 apart.
 template <int PAT>

@@ -1461,8 +1461,7 @@ __global__ void __launch_bounds__(64 * NWV) k_gemv_fused(LinearArgs p, const uin
     int *ri = reinterpret_cast<int *>(smem + F::C_RI);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) am[t] = fmax(am[t], __shfl_xor(am[t], off));
+        am[t] = wave_max_f64(am[t]);
         if (lane == 0) rd[wave * TM + t] = am[t];
     }
     __syncthreads();  // also: every lane is past its reads of X
@@ -1523,8 +1522,7 @@ __global__ void __launch_bounds__(64 * NWV) k_gemv_fused(LinearArgs p, const uin
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) rsum[t] += __shfl_xor(rsum[t], off);
+        rsum[t] = wave_sum_i32(rsum[t]);
         if (lane == 0) ri[wave * TM + t] = rsum[t];
     }
     __syncthreads();  // codes and per-wave rowsums

@@ -541,8 +541,7 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
 
         // ---- per-token absmax: the wave, then (W > 1) the team through LDS
         double am = rt_absmax<C>(v);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) am = fmax(am, __shfl_xor(am, off));
+        am = wave_max_f64(am);
         if (W > 1) {
             if (lane == 0) red_d[par][w] = am;
             __syncthreads();
@@ -555,8 +554,7 @@ k_rotquant_row(const void *__restrict__ Xv, int64_t M, int K, int W, int64_t nte
 
         // ---- quantize, pack, store
         int rowsum = rt_quant_store<BITS, C>(v, rr, qv, row, K, blk0, cl);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) rowsum += __shfl_xor(rowsum, off);
+        rowsum = wave_sum_i32(rowsum);
         if (W > 1) {
             if (lane == 0) red_i[par][w] = rowsum;
             __syncthreads();
@@ -628,8 +626,7 @@ k_rotquant_lr(const uint16_t *__restrict__ X, int64_t M, int K, int R, void *__r
         if (row + NT < m1) load(row + NT, nxt);
         rt_fwht<G, C>(v, cl);
         double am = rt_absmax<C>(v);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) am = fmax(am, __shfl_xor(am, off));
+        am = wave_max_f64(am);
         if constexpr (W > 1) {
             if (lane == 0) red_d[par][w] = am;
             __syncthreads();
@@ -639,8 +636,7 @@ k_rotquant_lr(const uint16_t *__restrict__ X, int64_t M, int K, int R, void *__r
         const float scale = (float)((am * INV_SQRT_G) / (double)QMAX);
         const double rr = scale > 0.0f ? (1.0 / (double)scale) * INV_SQRT_G : 0.0;
         int rowsum = valid ? rt_quant_store<BITS, C>(v, rr, qv, row, K, blk0, cl) : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) rowsum += __shfl_xor(rowsum, off);
+        rowsum = wave_sum_i32(rowsum);
         if constexpr (W > 1) {
             if (lane == 0) red_i[par][w] = rowsum;
             __syncthreads();
